@@ -1,0 +1,373 @@
+"""Pins for the FP64 oracle: each check ties it to something other than itself.
+
+* exact decoding: library conversions (numpy float16, torch float8_e4m3fn) and
+  exact rational arithmetic (fractions.Fraction);
+* brute force: an independent pure-Python softmax attention (math.fsum, the
+  caches decoded with numpy / torch) on tiny inputs of every storage type,
+  quantisation, layout and row kind;
+* a special case that reduces to a library routine (torch softmax in float64);
+* invariants and closed forms (rows sum to one, a single token, equal keys,
+  split = monolithic, head-sink closed form = an extra zero-value logit,
+  block-table permutation leaves every bit unchanged, empty rows);
+* the worked numerical examples printed on the pages (tests/golden).
+"""
+import math
+import os
+from dataclasses import replace
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from workloads import Inputs, Problem
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ---------------------------------------------------------------------------
+# exact decoding
+# ---------------------------------------------------------------------------
+
+def test_f16_decode_exhaustive():
+    bits = np.arange(65536, dtype=np.uint16)
+    ref = bits.view(np.float16).astype(np.float64)
+    got = np.array([oracle.f16_to_f64(int(b)) for b in bits])
+    both_nan = np.isnan(ref) & np.isnan(got)
+    assert np.array_equal(ref[~both_nan], got[~both_nan])
+    assert np.array_equal(np.isnan(ref), np.isnan(got))
+
+
+def test_fp8_e4m3fn_decode_exhaustive_vs_torch():
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    ref = codes.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = np.array([oracle.fp8e4m3_to_f64(c) for c in range(256)])
+    assert np.array_equal(np.isnan(ref), np.isnan(got))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(ref[ok], got[ok])
+    # OCP e4m3fn anchor points: largest finite 448, smallest normal 2^-6,
+    # smallest subnormal 2^-9, one, minus one, NaN only at S.1111.111
+    assert got[0x7E] == 448.0 and got[0x08] == 2.0 ** -6 and got[0x01] == 2.0 ** -9
+    assert got[0x38] == 1.0 and got[0xB8] == -1.0
+    assert np.isnan(got[0x7F]) and np.isnan(got[0xFF]) and int(np.isnan(got).sum()) == 2
+
+
+@pytest.mark.parametrize("scale", [1.0, 0.0625, 0.0347, 3.0e-3, 2.0 ** -135, 2.0 ** 60, 1.7e38])
+def test_int8_dequant_exact(scale):
+    s32 = float(np.float32(scale))
+    for code in range(256):
+        signed = code - 256 if code >= 128 else code
+        exact = Fraction(signed) * Fraction(s32)
+        assert Fraction(oracle.dequant("i8", code, s32)) == exact
+
+
+def test_fp8_dequant_exact():
+    for s in (1.0, 0.0101, 2.0 ** -20):
+        s32 = float(np.float32(s))
+        for code in range(256):
+            v = oracle.fp8e4m3_to_f64(code)
+            if math.isnan(v):
+                continue
+            assert Fraction(oracle.dequant("fp8", code, s32)) == Fraction(v) * Fraction(s32)
+
+
+# ---------------------------------------------------------------------------
+# independent brute force (pure Python, fsum)
+# ---------------------------------------------------------------------------
+
+def _decode_cache(codes, cache_dtype):
+    if cache_dtype == "f16":
+        return codes.astype(np.float64)
+    if cache_dtype == "i8":
+        return codes.astype(np.int8).astype(np.float64)
+    t = torch.from_numpy(np.ascontiguousarray(codes).view(np.uint8)).view(torch.float8_e4m3fn)
+    return t.to(torch.float64).numpy()
+
+
+def _scale(scale, quant, g, dim):
+    if quant == "none":
+        return np.ones(dim)
+    if quant == "tensor":
+        return np.full(dim, float(scale[0]))
+    return np.asarray(scale, dtype=np.float64).reshape(-1, dim)[g]
+
+
+def brute_force(inp: Inputs):
+    p = inp.problem
+    K = _decode_cache(inp.key_cache, p.cache_dtype)
+    V = None if p.layout == "latent" else _decode_cache(inp.value_cache, p.cache_dtype)
+    q = inp.query.astype(np.float64)
+    group = p.heads // p.kv_heads
+    out = np.zeros((p.rows, p.heads, p.v_head_size))
+    lse = np.zeros((p.rows, p.heads))
+    for r in range(p.rows):
+        n = min(max(int(inp.seq_lens[r]), 0), p.max_blocks_per_row * p.block_size)
+        if p.max_candidates:
+            nc = min(max(int(inp.num_candidates[r]), 0), p.max_candidates)
+            toks = [int(c) for c in inp.candidates[r, :nc] if 0 <= c < n]
+        else:
+            toks = list(range(n))
+        for h in range(p.heads):
+            g = h // group
+            ks = _scale(inp.k_scale, p.k_quant, g, p.head_size)
+            if p.layout == "latent":
+                vs = ks[: p.v_head_size]
+            else:
+                vs = _scale(inp.v_scale, p.v_quant, g, p.v_head_size)
+            krows, vrows, xs = [], [], []
+            for t in toks:
+                blk = int(inp.block_table[r, t // p.block_size])
+                off = t % p.block_size
+                k = K[blk, off, g, :] * ks
+                if p.layout == "latent":
+                    v = K[blk, off, g, : p.v_head_size] * vs
+                else:
+                    v = V[blk, off, g, :] * vs
+                xs.append(inp.softmax_scale * math.fsum(q[r, h, d] * k[d] for d in range(p.head_size)))
+                vrows.append(v)
+            if not toks:
+                out[r, h] = 0.0
+                lse[r, h] = -math.inf
+                continue
+            m = max(xs)
+            w = [math.exp(x - m) for x in xs]
+            L = math.fsum(w)
+            for c in range(p.v_head_size):
+                out[r, h, c] = math.fsum(w[i] * vrows[i][c] for i in range(len(toks))) / L
+            lse[r, h] = m + math.log(L)
+            if inp.head_sink is not None:
+                out[r, h] *= 1.0 / (1.0 + math.exp(float(inp.head_sink[h]) - lse[r, h]))
+    return out, lse
+
+
+TINY_CASES = [
+    # cache, kq, vq, layout, gathered, sink, heads, kvh, D, VD, B
+    ("f16", "none", "none", "separate", False, False, 4, 1, 8, 8, 4),
+    ("f16", "none", "none", "separate", False, True, 6, 2, 8, 4, 2),
+    ("i8", "tensor", "tensor", "separate", False, False, 4, 2, 8, 8, 4),
+    ("i8", "channel", "channel", "separate", True, True, 6, 3, 4, 8, 2),
+    ("i8", "channel", "tensor", "separate", True, False, 2, 2, 8, 8, 1),
+    ("fp8", "tensor", "tensor", "separate", False, True, 4, 2, 8, 8, 4),
+    ("fp8", "channel", "channel", "separate", True, False, 4, 1, 8, 4, 2),
+    ("fp8", "tensor", "tensor", "latent", False, False, 4, 1, 8, 4, 4),
+    ("i8", "channel", "channel", "latent", True, True, 3, 1, 8, 6, 2),
+    ("f16", "none", "none", "latent", False, True, 2, 1, 8, 4, 8),
+]
+
+
+def _tiny(case, seed):
+    cache, kq, vq, layout, gathered, sink, H, KVH, D, VD, B = case
+    rng = np.random.default_rng(seed)
+    rows, mbpr = 3, 3
+    lens = rng.integers(0, mbpr * B + 3, size=rows)  # includes 0 and > capacity
+    lens[0] = max(lens[0], 1)
+    p = Problem(rows=rows, heads=H, kv_heads=KVH, head_size=D, v_head_size=VD, block_size=B,
+                max_blocks_per_row=mbpr, num_pool_blocks=0,
+                max_candidates=6 if gathered else 0, cache_dtype=cache, k_quant=kq,
+                v_quant=vq, layout=layout)
+    cand = None
+    if gathered:
+        # invalid entries (negative, beyond the length), duplicates, unsorted
+        cand = rng.integers(-2, mbpr * B + 2, size=(rows, 6)).astype(np.int32)
+        cand[0, :2] = [1, 1]
+    inp = workloads.make_inputs(p, seed, lens, candidates=cand, with_sink=sink,
+                                num_candidates=None if not gathered else np.array([6, 4, 0][:rows]),
+                                softmax_scale=0.37)
+    return inp
+
+
+@pytest.mark.parametrize("case", TINY_CASES)
+@pytest.mark.parametrize("seed", [11, 12])
+def test_brute_force_tiny(case, seed):
+    inp = _tiny(case, seed)
+    o, l = oracle.paged_decode(inp, threads=2)
+    bo, bl = brute_force(inp)
+    assert np.array_equal(np.isinf(l), np.isinf(bl))
+    fin = np.isfinite(bl)
+    np.testing.assert_allclose(l[fin], bl[fin], rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(o, bo, rtol=1e-12, atol=1e-14)
+
+
+def test_dense_case_equals_torch_softmax():
+    """Group 1, identity block table, one block per row: the definition
+    reduces to softmax(q k^T * scale) v, evaluated by torch in float64."""
+    T, D = 37, 16
+    p = Problem(rows=2, heads=3, kv_heads=3, head_size=D, v_head_size=D, block_size=T,
+                max_blocks_per_row=1, num_pool_blocks=2, cache_dtype="f16")
+    rng = np.random.default_rng(5)
+    q = rng.standard_normal((2, 3, D)).astype(np.float16)
+    k = rng.standard_normal((2, T, 3, D)).astype(np.float16)
+    v = rng.standard_normal((2, T, 3, D)).astype(np.float16)
+    inp = Inputs(problem=p, query=q, key_cache=k, value_cache=v,
+                 block_table=np.array([[0], [1]], dtype=np.int32),
+                 seq_lens=np.array([T, T], dtype=np.int32), softmax_scale=0.29)
+    o, l = oracle.paged_decode(inp)
+    for r in range(2):
+        for h in range(3):
+            qq = torch.from_numpy(q[r, h].astype(np.float64))
+            kk = torch.from_numpy(k[r, :, h].astype(np.float64))
+            vv = torch.from_numpy(v[r, :, h].astype(np.float64))
+            ref = torch.softmax(kk @ qq * 0.29, dim=0) @ vv
+            np.testing.assert_allclose(o[r, h], ref.numpy(), rtol=1e-13, atol=1e-15)
+            np.testing.assert_allclose(l[r, h], torch.logsumexp(kk @ qq * 0.29, 0).item(), rtol=1e-14)
+
+
+# ---------------------------------------------------------------------------
+# invariants and closed forms
+# ---------------------------------------------------------------------------
+
+def _small(cache="f16", seed=3, lens=(45, 1, 64, 17), sink=False, **kw):
+    kq = vq = "none" if cache == "f16" else "tensor"
+    p = Problem(rows=len(lens), heads=4, kv_heads=2, head_size=16, v_head_size=16, block_size=16,
+                max_blocks_per_row=4, num_pool_blocks=0, cache_dtype=cache, k_quant=kq,
+                v_quant=vq, **kw)
+    return workloads.make_inputs(p, seed, list(lens), with_sink=sink, softmax_scale=0.25)
+
+
+def test_rows_sum_to_one():
+    inp = _small()
+    inp.value_cache[...] = np.float16(1.0)
+    o, _ = oracle.paged_decode(inp)
+    np.testing.assert_allclose(o, 1.0, rtol=0, atol=1e-15)
+
+
+def test_single_token_returns_its_value_exactly():
+    inp = _small(lens=(1, 1, 1, 1))
+    o, l = oracle.paged_decode(inp)
+    B = inp.problem.block_size
+    for r in range(4):
+        blk = inp.block_table[r, 0]
+        for h in range(4):
+            v = inp.value_cache[blk, 0, h // 2].astype(np.float64)
+            assert np.array_equal(o[r, h], v)
+
+
+def test_equal_keys_give_the_mean_value():
+    inp = _small(lens=(45, 7, 64, 17))
+    inp.key_cache[...] = inp.key_cache[inp.block_table[0, 0], 0]
+    o, _ = oracle.paged_decode(inp)
+    for r in range(4):
+        n = int(inp.seq_lens[r])
+        for h in range(4):
+            vals = []
+            for t in range(n):
+                blk = inp.block_table[r, t // 16]
+                vals.append(inp.value_cache[blk, t % 16, h // 2].astype(np.float64))
+            np.testing.assert_allclose(o[r, h], np.mean(vals, axis=0), rtol=1e-13, atol=1e-15)
+
+
+@pytest.mark.parametrize("chunk", [1, 7, 16, 64, 4096])
+@pytest.mark.parametrize("cache", ["f16", "i8"])
+def test_split_equals_monolithic(chunk, cache):
+    inp = _small(cache=cache, sink=True, lens=(45, 1, 64, 0))
+    o0, l0 = oracle.paged_decode(inp)
+    o1, l1 = oracle.paged_decode(inp, chunk=chunk)
+    np.testing.assert_allclose(o1, o0, rtol=1e-13, atol=1e-15)
+    np.testing.assert_allclose(l1[np.isfinite(l0)], l0[np.isfinite(l0)], rtol=1e-13)
+    assert np.array_equal(np.isinf(l0), np.isinf(l1))
+
+
+def test_head_sink_equals_extra_zero_value_logit():
+    inp = _small(sink=True)
+    o, l = oracle.paged_decode(inp)
+    base = replace(inp.problem)
+    plain = Inputs(**{**inp.__dict__, "head_sink": None, "problem": base})
+    o0, l0 = oracle.paged_decode(plain)
+    for r in range(4):
+        for h in range(4):
+            s = float(inp.head_sink[h])
+            # softmax over the row's logits plus one extra logit s with value 0
+            denom = math.exp(l0[r, h]) + math.exp(s)
+            expect = o0[r, h] * math.exp(l0[r, h]) / denom
+            np.testing.assert_allclose(o[r, h], expect, rtol=1e-14, atol=1e-16)
+            assert l[r, h] == l0[r, h]  # lse is reported before the sink
+
+
+def test_block_table_permutation_is_bitwise_invariant():
+    inp = _small(cache="i8", sink=True)
+    o0, l0 = oracle.paged_decode(inp)
+    pool = inp.problem.num_pool_blocks
+    perm = np.random.default_rng(9).permutation(pool)  # new id of each old block
+    k2 = np.empty_like(inp.key_cache)
+    v2 = np.empty_like(inp.value_cache)
+    k2[perm] = inp.key_cache
+    v2[perm] = inp.value_cache
+    moved = Inputs(**{**inp.__dict__, "key_cache": k2, "value_cache": v2,
+                      "block_table": perm[inp.block_table].astype(np.int32)})
+    o1, l1 = oracle.paged_decode(moved)
+    assert np.array_equal(o0, o1) and np.array_equal(l0, l1)
+
+
+def test_empty_and_clamped_rows():
+    inp = _small(lens=(0, 64, 1000, -5))
+    o, l = oracle.paged_decode(inp)
+    assert np.all(o[0] == 0) and np.all(np.isneginf(l[0]))
+    assert np.all(o[3] == 0) and np.all(np.isneginf(l[3]))
+    # a length beyond the capacity is clamped to it (64 tokens here)
+    inp2 = Inputs(**{**inp.__dict__, "seq_lens": np.array([0, 64, 64, -5], dtype=np.int32)})
+    o2, l2 = oracle.paged_decode(inp2)
+    assert np.array_equal(o2[2], o[2]) and np.array_equal(l2[2], l[2])
+
+
+def test_all_candidates_invalid_gives_empty_row():
+    p = Problem(rows=1, heads=2, kv_heads=1, head_size=8, v_head_size=8, block_size=4,
+                max_blocks_per_row=2, num_pool_blocks=0, max_candidates=3, cache_dtype="f16")
+    inp = workloads.make_inputs(p, 1, 5, candidates=np.array([[-1, 5, 9]], dtype=np.int32))
+    o, l = oracle.paged_decode(inp)
+    assert np.all(o == 0) and np.all(np.isneginf(l))
+
+
+def test_bad_block_id_is_an_error():
+    inp = _small()
+    inp.block_table[1, 0] = inp.problem.num_pool_blocks
+    with pytest.raises(RuntimeError):
+        oracle.paged_decode(inp)
+
+
+# ---------------------------------------------------------------------------
+# the pages' worked examples
+# ---------------------------------------------------------------------------
+
+def _golden_rows():
+    rows = []
+    with open(os.path.join(GOLDEN, "worked_examples.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            rows.append(line.split())
+    return rows
+
+
+@pytest.mark.parametrize("row", _golden_rows(), ids=lambda r: r[0])
+def test_worked_examples(row):
+    (name, q0, q1, ka0, ka1, kb0, kb1, va, vb, vscale, sscale, expected, rtol,
+     printed, printed_tol) = row
+    D = 256
+    p = Problem(rows=1, heads=1, kv_heads=1, head_size=D, v_head_size=D, block_size=16,
+                max_blocks_per_row=1, num_pool_blocks=1, max_candidates=2, cache_dtype="i8",
+                k_quant="tensor", v_quant="tensor", out_dtype="f32")
+    q = np.zeros((1, 1, D), dtype=np.float16)
+    q[0, 0, 0], q[0, 0, 1] = np.float16(float(q0)), np.float16(float(q1))
+    assert float(q[0, 0, 0]) == float(q0) and float(q[0, 0, 1]) == float(q1)
+    k = np.zeros((1, 16, 1, D), dtype=np.int8)
+    v = np.zeros((1, 16, 1, D), dtype=np.int8)
+    # candidate a at token 3, candidate b at token 11 (same 16-token block)
+    k[0, 3, 0, :2] = [int(ka0), int(ka1)]
+    k[0, 11, 0, :2] = [int(kb0), int(kb1)]
+    v[0, 3, 0, 0], v[0, 11, 0, 0] = int(va), int(vb)
+    vs = np.float32(float(vscale))
+    assert float(vs) == float(vscale)
+    inp = Inputs(problem=p, query=q, key_cache=k, value_cache=v,
+                 block_table=np.zeros((1, 1), dtype=np.int32), seq_lens=np.array([16], np.int32),
+                 softmax_scale=float(sscale), k_scale=np.array([1.0], np.float32),
+                 v_scale=np.array([vs], np.float32), candidates=np.array([[3, 11]], np.int32),
+                 num_candidates=np.array([2], np.int32))
+    o, _ = oracle.paged_decode(inp)
+    got = o[0, 0, 0]
+    assert got == pytest.approx(float(expected), rel=float(rtol), abs=0)
+    if printed != "-":
+        assert abs(got - float(printed)) <= float(printed_tol)
+    assert np.all(o[0, 0, 1:] == 0)
