@@ -1,0 +1,229 @@
+/*
+ * pkv.h -- C ABI of libpkv: split-KV (flash-decoding) grouped-query decode
+ * attention over a paged KV cache stored as FP16, INT8 or FP8-e4m3fn, for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operation follows the pages' statement of the problem:
+ *   - ONNX Runtime PR #29912 (PagedAttention), "Summary of Changes": query,
+ *     key_cache / value_cache typed float16 | int8 | float8e4m3fn, the block
+ *     table and block size, head_sink, k_scale / v_scale with
+ *     k_quant_type / v_quant_type NONE | PER_TENSOR | PER_CHANNEL, the
+ *     SEPARATE | LATENT cache layout with v_head_size, and graph safety
+ *     (launch geometry and workspace from static shapes and the
+ *     block_table.shape[1] * block_size capacity; per-step lengths read on
+ *     the device);
+ *   - ONNX Runtime PR #33707 (INT8 DynamicSparseAttention), "Summary of
+ *     Changes" sections 1-2: per-row selected candidate lists with invalid
+ *     entries, a finite non-negative softmax scale, the split-K partial
+ *     (running maximum in natural-log units, running sum, value-scaled
+ *     accumulator) and its merge, a statically sized workspace;
+ *   - onnx-genai PR #1350 "Summary": the split count comes from the static
+ *     capacity and the row count so that about one occupancy wave of CTAs
+ *     runs, never from live lengths.
+ *
+ * Definition.  For row r (one decode query token) and query head h with KV
+ * head g = h / (num_heads / num_kv_heads):
+ *   len    = clamp(seq_lens[r], 0, max_blocks_per_row * block_size)
+ *   T      = [0, len) for dense rows (max_candidates == 0); for gathered rows
+ *            the list candidates[r][0 : clamp(num_candidates[r], 0,
+ *            max_candidates)] in list order, keeping entries in [0, len)
+ *            (duplicates count twice)
+ *   slot t = block_table[r][t / block_size] * block_size + t % block_size
+ *   x_t    = softmax_scale * sum_d Q[r,h,d] * K^[slot t, g, d]
+ *   O      = sum_t exp(x_t - m) V^[slot t, g, :] / sum_t exp(x_t - m),
+ *            m = max_t x_t;  lse = m + log sum_t exp(x_t - m)
+ *   sink   O <- O / (1 + exp(head_sink[h] - lse)) when head_sink != NULL
+ *   empty  T = {} gives O = 0 and lse = -inf.
+ * K^ / V^ are the stored codes times their scale (x = code * scale; per
+ * tensor: scale[0]; per channel: scale[g * dim + d]).  LATENT: one cache
+ * [.., 1 row per token and KV head, head_size]; V^ is the first v_head_size
+ * channels of the K row, with the K scales.
+ *
+ * Memory layouts (all row-major, device memory unless stated):
+ *   query        [num_rows, num_heads, head_size]              float16
+ *   key_cache    [num_pool_blocks, block_size, num_kv_heads, head_size]
+ *   value_cache  [num_pool_blocks, block_size, num_kv_heads, v_head_size]
+ *                (NULL for LATENT)                              cache_dtype
+ *   block_table  [num_rows, max_blocks_per_row]                int32
+ *   seq_lens     [num_rows]                                    int32
+ *   candidates   [num_rows, max_candidates]                    int32
+ *   num_candidates [num_rows]                                  int32
+ *   k_scale      [1] (PER_TENSOR) or [num_kv_heads, head_size] (PER_CHANNEL)
+ *   v_scale      [1] or [num_kv_heads, v_head_size]            float32
+ *   head_sink    [num_heads]                                   float32
+ *   out          [num_rows, num_heads, v_head_size]            out_dtype
+ *   lse_out      [num_rows, num_heads]                         float32
+ *   workspace    partial accumulators [num_rows, num_heads, S, v_head_size]
+ *                float32 followed by (m, l) pairs [num_rows, num_heads, S, 2]
+ *
+ * Ownership and threading.  The caller allocates and frees every buffer; the
+ * library never allocates, frees or synchronises.  Calls enqueue work on the
+ * caller's HIP stream and return; buffers must stay valid until that work
+ * completes.  Two calls that share a workspace must not overlap in time.
+ * The only library state is a per-device cache of the CU count and kernel
+ * occupancy (thread-safe).
+ *
+ * Errors.  Static arguments are checked before anything is enqueued; on any
+ * error nothing was enqueued.  pkv_last_error() returns a message naming the
+ * offending argument (thread-local).  Device-resident data cannot be checked
+ * without a synchronisation, so it has defined semantics instead: seq_lens
+ * are clamped to [0, capacity]; num_candidates to [0, max_candidates];
+ * candidate indices outside [0, len) are skipped; a block-table entry
+ * outside [0, num_pool_blocks) makes its tokens contribute nothing (they are
+ * never read); block-table entries past the live length are never read.
+ *
+ * Graph safety.  The launch configuration depends only on pkv_problem and
+ * pkv_geometry, never on device data, and no call records a memset or a
+ * host synchronisation, so a call may be captured in a hipGraph and replayed
+ * with different seq_lens / candidates / block tables.
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PKV_OK = 0,
+  PKV_EINVAL = 1,          /* an argument is invalid (null, out of range, ...) */
+  PKV_EUNSUPPORTED = 2,    /* valid, but no compiled kernel covers it */
+  PKV_EALIGN = 3,          /* a pointer is not aligned as required */
+  PKV_EWORKSPACE = 4,      /* workspace_bytes smaller than required */
+  PKV_EHIP = 5             /* the HIP runtime reported an error */
+} pkv_status;
+
+typedef enum { PKV_F16 = 0, PKV_I8 = 1, PKV_FP8_E4M3FN = 2, PKV_F32 = 3 } pkv_dtype;
+typedef enum { PKV_QUANT_NONE = 0, PKV_QUANT_PER_TENSOR = 1, PKV_QUANT_PER_CHANNEL = 2 } pkv_quant;
+typedef enum { PKV_SEPARATE = 0, PKV_LATENT = 1 } pkv_layout;
+
+/* Static description of one decode step; nothing here depends on live data.
+ * Supported: (head_size, v_head_size) in {(64,64), (128,128), (256,256)} for
+ * SEPARATE and (576,512) for LATENT; block_size a positive multiple of 16;
+ * cache_dtype F16 (any quant), I8 or FP8_E4M3FN (quant PER_TENSOR or
+ * PER_CHANNEL); out_dtype F16 or F32; num_heads a multiple of num_kv_heads. */
+typedef struct {
+  int32_t num_rows;
+  int32_t num_heads;
+  int32_t num_kv_heads;
+  int32_t head_size;
+  int32_t v_head_size;
+  int32_t block_size;
+  int32_t max_blocks_per_row;
+  int32_t num_pool_blocks;
+  int32_t max_candidates;  /* 0: dense rows [0, seq_len); > 0: gathered rows */
+  int32_t cache_dtype;     /* pkv_dtype */
+  int32_t out_dtype;       /* pkv_dtype: PKV_F16 or PKV_F32 */
+  int32_t k_quant;         /* pkv_quant */
+  int32_t v_quant;         /* pkv_quant; LATENT: ignored (V uses the K scales) */
+  int32_t layout;          /* pkv_layout */
+} pkv_problem;
+
+/* Optional knobs of split_geometry (pass NULL for all defaults; 0 = default). */
+typedef struct {
+  int32_t num_cus;          /* compute units; 0 = query the current device */
+  int32_t ctas_per_cu;      /* resident CTAs per CU; 0 = occupancy query */
+  int32_t splits_override;  /* > 0: use this split count (clipped to the caps) */
+  int32_t min_chunk;        /* smallest positions per split (multiple of 16) */
+  int32_t max_splits;       /* cap on the split count */
+  int32_t waves;            /* target = waves * num_cus * ctas_per_cu CTAs */
+} pkv_geometry_opts;
+
+/* Launch geometry; produced by split_geometry, consumed unchanged. */
+typedef struct {
+  int32_t num_splits;       /* S: CTAs per (row, KV head, head block) */
+  int32_t min_chunk;        /* positions per active split are >= this */
+  int32_t threads;          /* threads per CTA of the split kernel */
+  int32_t head_blocks;      /* ceil(group / 16): query heads go 16 per CTA */
+  int32_t grid_x, grid_y, grid_z;  /* split-kernel grid: S, kv_heads*head_blocks, rows */
+  int32_t reserved;
+  uint64_t workspace_bytes; /* bytes of workspace the calls below need */
+} pkv_geometry;
+
+/*
+ * split_geometry -- choose the split count S from static shapes only.
+ *
+ * units = num_rows * num_kv_heads * ceil(group / 16);
+ * cap   = max_blocks_per_row * block_size (dense) or max_candidates
+ *         (gathered);  resident = num_cus * ctas_per_cu.
+ * Dense rows (onnx-genai PR #1350 "Summary"):
+ *   S = min(ceil(waves * resident / units), ceil(cap / min_chunk), max_splits)
+ * Gathered rows (ONNX Runtime PR #33707 section 2, split count rule): the
+ *   unit of work is a 64-candidate tile; tiles-per-split is the smallest
+ *   power of two for which ceil(tiles / tps) * units <= waves * resident;
+ *   S = min(ceil(tiles / tps), max_splits).
+ * A positive splits_override replaces the automatic count (then clipped to
+ * [1, max_splits] and to ceil(cap / 16)).  On the device each row spreads its
+ * live positions evenly over n = min(S, ceil(len / min_chunk)) splits in
+ * 16-position steps; splits beyond that publish an empty partial.
+ * Defaults: min_chunk 64 (gathered: 64), max_splits 64, waves 1.
+ * Returns PKV_EINVAL / PKV_EUNSUPPORTED as paged_decode_attention would, or
+ * PKV_EHIP if the device query fails.  Does not touch device memory.
+ */
+pkv_status split_geometry(const pkv_problem* problem, const pkv_geometry_opts* opts,
+                          pkv_geometry* out);
+
+/*
+ * paged_decode_attention -- one decode step: the split kernel writes per-split
+ * partials into `workspace`, then the combine kernel merges them (fixed split
+ * order, so results are bitwise repeatable), applies the head sink and writes
+ * `out` (and `lse_out` if not NULL).  Two kernel launches on `stream`
+ * (a hipStream_t; NULL = the default stream); no allocation, no memset, no
+ * synchronisation.
+ *
+ * Alignment: query, key_cache, value_cache, out, workspace and per-channel
+ * scale arrays 16-byte aligned; integer arrays, per-tensor scales,
+ * head_sink and lse_out 4-byte aligned.  softmax_scale must be finite and
+ * >= 0.  workspace_bytes >= geometry->workspace_bytes.  The geometry must be
+ * the one split_geometry returned for this problem.
+ */
+pkv_status paged_decode_attention(const pkv_problem* problem, const pkv_geometry* geometry,
+                                  const void* query, const void* key_cache,
+                                  const void* value_cache, const int32_t* block_table,
+                                  const int32_t* seq_lens, const int32_t* candidates,
+                                  const int32_t* num_candidates, const float* k_scale,
+                                  const float* v_scale, float softmax_scale,
+                                  const float* head_sink, void* out, float* lse_out,
+                                  void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * paged_decode_partials -- the split kernel alone: writes the per-split
+ * partials (value-scaled accumulator, running maximum in natural-log units,
+ * running sum) into `workspace` and nothing else.  split_combine then turns
+ * them into the output.  Partials of disjoint position ranges (for example
+ * computed on different devices for one long row) merge exactly the same
+ * way.  Same arguments and rules as paged_decode_attention.
+ */
+pkv_status paged_decode_partials(const pkv_problem* problem, const pkv_geometry* geometry,
+                                 const void* query, const void* key_cache,
+                                 const void* value_cache, const int32_t* block_table,
+                                 const int32_t* seq_lens, const int32_t* candidates,
+                                 const int32_t* num_candidates, const float* k_scale,
+                                 const float* v_scale, float softmax_scale,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * split_combine -- merge the S partials of every (row, query head) in split
+ * order: M = max_k m_k, w_k = exp(m_k - M), L = sum_k w_k l_k,
+ * O = sum_k w_k acc_k / L, lse = M + log L (empty: O = 0, lse = -inf), then
+ * the exact head-sink rescale O <- O / (1 + exp(head_sink[h] - lse))
+ * (ONNX Runtime PR #29912, ApplyHeadSink).  One launch on `stream`.
+ */
+pkv_status split_combine(const pkv_problem* problem, const pkv_geometry* geometry,
+                         const void* workspace, size_t workspace_bytes, const float* head_sink,
+                         void* out, float* lse_out, void* stream);
+
+/* Static string for a status code. */
+const char* pkv_status_string(pkv_status status);
+
+/* Message describing the most recent failure on the calling thread ("" if none). */
+const char* pkv_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H */

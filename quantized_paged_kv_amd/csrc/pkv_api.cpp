@@ -1,0 +1,417 @@
+// pkv_api.cpp -- the C ABI of libpkv: argument validation, split geometry
+// and kernel dispatch.  See include/pkv.h for the contract.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <unordered_map>
+
+#include "pkv_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+pkv_status fail(pkv_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
+
+bool aligned(const void* p, size_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
+
+pkv::Variant variant_of(const pkv_problem& p) {
+  pkv::Variant v;
+  v.cache_dtype = p.cache_dtype;
+  v.head_size = p.head_size;
+  v.v_head_size = p.v_head_size;
+  v.latent = p.layout == PKV_LATENT;
+  v.gathered = p.max_candidates > 0;
+  return v;
+}
+
+// Static checks of the problem description.
+pkv_status check_problem(const pkv_problem* p) {
+  if (!p) return fail(PKV_EINVAL, "problem is NULL");
+  if (p->num_rows < 0) return fail(PKV_EINVAL, "num_rows < 0");
+  if (p->num_heads <= 0 || p->num_kv_heads <= 0)
+    return fail(PKV_EINVAL, "num_heads and num_kv_heads must be positive");
+  if (p->num_heads % p->num_kv_heads)
+    return fail(PKV_EINVAL, "num_heads (%d) is not a multiple of num_kv_heads (%d)", p->num_heads,
+                p->num_kv_heads);
+  if (p->head_size <= 0 || p->v_head_size <= 0) return fail(PKV_EINVAL, "head sizes must be positive");
+  if (p->block_size <= 0 || p->block_size % 16)
+    return fail(PKV_EUNSUPPORTED, "block_size (%d) must be a positive multiple of 16", p->block_size);
+  if (p->max_blocks_per_row <= 0) return fail(PKV_EINVAL, "max_blocks_per_row must be positive");
+  if (p->num_pool_blocks <= 0) return fail(PKV_EINVAL, "num_pool_blocks must be positive");
+  if ((int64_t)p->max_blocks_per_row * p->block_size > INT32_MAX)
+    return fail(PKV_EINVAL, "capacity max_blocks_per_row * block_size overflows int32");
+  if (p->max_candidates < 0) return fail(PKV_EINVAL, "max_candidates < 0");
+  if (p->cache_dtype != PKV_F16 && p->cache_dtype != PKV_I8 && p->cache_dtype != PKV_FP8_E4M3FN)
+    return fail(PKV_EINVAL, "cache_dtype must be PKV_F16, PKV_I8 or PKV_FP8_E4M3FN");
+  if (p->out_dtype != PKV_F16 && p->out_dtype != PKV_F32)
+    return fail(PKV_EINVAL, "out_dtype must be PKV_F16 or PKV_F32");
+  if (p->layout != PKV_SEPARATE && p->layout != PKV_LATENT)
+    return fail(PKV_EINVAL, "layout must be PKV_SEPARATE or PKV_LATENT");
+  for (int q : {p->k_quant, p->v_quant})
+    if (q < PKV_QUANT_NONE || q > PKV_QUANT_PER_CHANNEL)
+      return fail(PKV_EINVAL, "quant must be NONE, PER_TENSOR or PER_CHANNEL");
+  if (p->cache_dtype != PKV_F16) {
+    if (p->k_quant == PKV_QUANT_NONE)
+      return fail(PKV_EINVAL, "a quantised cache needs k_quant PER_TENSOR or PER_CHANNEL");
+    if (p->layout == PKV_SEPARATE && p->v_quant == PKV_QUANT_NONE)
+      return fail(PKV_EINVAL, "a quantised cache needs v_quant PER_TENSOR or PER_CHANNEL");
+  }
+  if (p->num_rows > 65535 || (int64_t)p->num_kv_heads * ceil_div(p->num_heads / p->num_kv_heads, 16) > 65535)
+    return fail(PKV_EUNSUPPORTED, "num_rows and num_kv_heads * ceil(group / 16) must be <= 65535");
+  if (p->layout == PKV_LATENT && p->v_head_size > p->head_size)
+    return fail(PKV_EINVAL, "LATENT needs v_head_size <= head_size");
+  if (!pkv::variant_supported(variant_of(*p)))
+    return fail(PKV_EUNSUPPORTED,
+                "no kernel for head_size %d / v_head_size %d with layout %d (compiled: "
+                "64/64, 128/128, 256/256 SEPARATE; 576/512 LATENT)",
+                p->head_size, p->v_head_size, p->layout);
+  return PKV_OK;
+}
+
+uint64_t workspace_bytes_for(const pkv_problem& p, int S) {
+  const uint64_t pairs = (uint64_t)p.num_rows * p.num_heads;
+  return pairs * S * p.v_head_size * sizeof(float) + pairs * S * 2 * sizeof(float);
+}
+
+// Per-device cache of (CU count, occupancy per variant).
+struct DeviceInfo {
+  int cus = 0;
+  std::unordered_map<uint64_t, int> occupancy;
+};
+std::mutex g_dev_mu;
+std::unordered_map<int, DeviceInfo> g_dev;
+
+uint64_t variant_key(const pkv::Variant& v) {
+  return ((uint64_t)v.cache_dtype << 40) | ((uint64_t)v.head_size << 24) |
+         ((uint64_t)v.v_head_size << 8) | (v.latent << 1) | v.gathered;
+}
+
+pkv_status device_numbers(const pkv::Variant& v, int* cus, int* occ) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(PKV_EHIP, "hipGetDevice failed");
+  std::lock_guard<std::mutex> lock(g_dev_mu);
+  DeviceInfo& info = g_dev[dev];
+  if (info.cus == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      return fail(PKV_EHIP, "cannot query the CU count of device %d", dev);
+    info.cus = n;
+  }
+  *cus = info.cus;
+  if (occ) {
+    const uint64_t key = variant_key(v);
+    auto it = info.occupancy.find(key);
+    if (it == info.occupancy.end()) {
+      int n = 0;
+      if (pkv::split_occupancy(v, &n) != hipSuccess || n <= 0)
+        return fail(PKV_EHIP, "occupancy query failed");
+      it = info.occupancy.emplace(key, n).first;
+    }
+    *occ = it->second;
+  }
+  return PKV_OK;
+}
+
+pkv_status check_geometry(const pkv_problem& p, const pkv_geometry* g) {
+  if (!g) return fail(PKV_EINVAL, "geometry is NULL");
+  const int group = p.num_heads / p.num_kv_heads;
+  if (g->num_splits < 1 || g->num_splits > pkv::kMaxSplits)
+    return fail(PKV_EINVAL, "geometry num_splits %d outside [1, %d]", g->num_splits, pkv::kMaxSplits);
+  if (g->min_chunk < 16 || g->min_chunk % 16)
+    return fail(PKV_EINVAL, "geometry min_chunk %d is not a positive multiple of 16", g->min_chunk);
+  if (g->head_blocks != ceil_div(group, 16) || g->threads != pkv::kThreads ||
+      g->grid_x != g->num_splits || g->grid_y != p.num_kv_heads * g->head_blocks ||
+      g->grid_z != p.num_rows || g->workspace_bytes != workspace_bytes_for(p, g->num_splits))
+    return fail(PKV_EINVAL, "geometry does not belong to this problem (call split_geometry)");
+  return PKV_OK;
+}
+
+struct Ptrs {
+  const void* query;
+  const void* key_cache;
+  const void* value_cache;
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  const int32_t* candidates;
+  const int32_t* num_candidates;
+  const float* k_scale;
+  const float* v_scale;
+};
+
+pkv_status check_inputs(const pkv_problem& p, const Ptrs& x, float softmax_scale) {
+  if (!x.query) return fail(PKV_EINVAL, "query is NULL");
+  if (!x.key_cache) return fail(PKV_EINVAL, "key_cache is NULL");
+  if (p.layout == PKV_SEPARATE && !x.value_cache) return fail(PKV_EINVAL, "value_cache is NULL");
+  if (p.layout == PKV_LATENT && x.value_cache)
+    return fail(PKV_EINVAL, "value_cache must be NULL for the LATENT layout");
+  if (!x.block_table) return fail(PKV_EINVAL, "block_table is NULL");
+  if (!x.seq_lens) return fail(PKV_EINVAL, "seq_lens is NULL");
+  if (p.max_candidates > 0 && (!x.candidates || !x.num_candidates))
+    return fail(PKV_EINVAL, "gathered rows need candidates and num_candidates");
+  if (p.k_quant != PKV_QUANT_NONE && !x.k_scale) return fail(PKV_EINVAL, "k_scale is NULL");
+  if (p.layout == PKV_SEPARATE && p.v_quant != PKV_QUANT_NONE && !x.v_scale)
+    return fail(PKV_EINVAL, "v_scale is NULL");
+  if (p.layout == PKV_LATENT && x.v_scale && x.v_scale != x.k_scale)
+    return fail(PKV_EINVAL, "LATENT: v_scale must be NULL or equal to k_scale");
+  if (!std::isfinite(softmax_scale) || softmax_scale < 0.0f)
+    return fail(PKV_EINVAL, "softmax_scale must be finite and >= 0");
+  if (!aligned(x.query, 16)) return fail(PKV_EALIGN, "query is not 16-byte aligned");
+  if (!aligned(x.key_cache, 16)) return fail(PKV_EALIGN, "key_cache is not 16-byte aligned");
+  if (x.value_cache && !aligned(x.value_cache, 16))
+    return fail(PKV_EALIGN, "value_cache is not 16-byte aligned");
+  for (const void* q : {(const void*)x.block_table, (const void*)x.seq_lens,
+                        (const void*)x.candidates, (const void*)x.num_candidates})
+    if (q && !aligned(q, 4)) return fail(PKV_EALIGN, "an int32 array is not 4-byte aligned");
+  if (x.k_scale && !aligned(x.k_scale, p.k_quant == PKV_QUANT_PER_CHANNEL ? 16 : 4))
+    return fail(PKV_EALIGN, "k_scale is not aligned");
+  if (x.v_scale && !aligned(x.v_scale, p.v_quant == PKV_QUANT_PER_CHANNEL ? 16 : 4))
+    return fail(PKV_EALIGN, "v_scale is not aligned");
+  return PKV_OK;
+}
+
+pkv_status check_workspace(const pkv_geometry& g, const void* ws, size_t bytes) {
+  if (!ws) return fail(PKV_EINVAL, "workspace is NULL");
+  if (!aligned(ws, 16)) return fail(PKV_EALIGN, "workspace is not 16-byte aligned");
+  if (bytes < g.workspace_bytes)
+    return fail(PKV_EWORKSPACE, "workspace_bytes %zu < required %llu", bytes,
+                (unsigned long long)g.workspace_bytes);
+  return PKV_OK;
+}
+
+pkv_status check_outputs(const void* out, const float* lse, const float* sink) {
+  if (!out) return fail(PKV_EINVAL, "out is NULL");
+  if (!aligned(out, 16)) return fail(PKV_EALIGN, "out is not 16-byte aligned");
+  if (lse && !aligned(lse, 4)) return fail(PKV_EALIGN, "lse_out is not 4-byte aligned");
+  if (sink && !aligned(sink, 4)) return fail(PKV_EALIGN, "head_sink is not 4-byte aligned");
+  return PKV_OK;
+}
+
+pkv::SplitArgs split_args(const pkv_problem& p, const pkv_geometry& g, const Ptrs& x,
+                          float softmax_scale, void* workspace) {
+  pkv::SplitArgs a;
+  std::memset(&a, 0, sizeof(a));
+  const uint64_t pairs = (uint64_t)p.num_rows * p.num_heads;
+  a.query = static_cast<const uint16_t*>(x.query);
+  a.key_cache = static_cast<const uint8_t*>(x.key_cache);
+  a.value_cache = static_cast<const uint8_t*>(x.value_cache);
+  a.block_table = x.block_table;
+  a.seq_lens = x.seq_lens;
+  a.candidates = x.candidates;
+  a.num_candidates = x.num_candidates;
+  a.k_scale = x.k_scale;
+  const bool latent = p.layout == PKV_LATENT;
+  a.v_scale = latent ? x.k_scale : x.v_scale;
+  a.ws_acc = static_cast<float*>(workspace);
+  a.ws_ml = a.ws_acc + pairs * g.num_splits * p.v_head_size;
+  a.rows = p.num_rows;
+  a.heads = p.num_heads;
+  a.kv_heads = p.num_kv_heads;
+  a.group = p.num_heads / p.num_kv_heads;
+  a.head_blocks = g.head_blocks;
+  a.block_size = p.block_size;
+  a.max_blocks_per_row = p.max_blocks_per_row;
+  a.num_pool_blocks = p.num_pool_blocks;
+  a.max_candidates = p.max_candidates;
+  a.num_splits = g.num_splits;
+  a.min_chunk = g.min_chunk;
+  a.k_quant = p.k_quant;
+  a.v_quant = latent ? p.k_quant : p.v_quant;
+  a.v_scale_stride = latent ? p.head_size : p.v_head_size;
+  const float code_factor = p.cache_dtype == PKV_FP8_E4M3FN ? 256.0f : 1.0f;
+  a.score_scale = softmax_scale * code_factor;
+  a.v_mult = code_factor;
+  return a;
+}
+
+pkv::CombineArgs combine_args(const pkv_problem& p, const pkv_geometry& g, const void* ws,
+                              const float* sink, void* out, float* lse) {
+  pkv::CombineArgs c;
+  const uint64_t pairs = (uint64_t)p.num_rows * p.num_heads;
+  c.ws_acc = static_cast<const float*>(ws);
+  c.ws_ml = c.ws_acc + pairs * g.num_splits * p.v_head_size;
+  c.head_sink = sink;
+  c.out = out;
+  c.lse_out = lse;
+  c.rows = p.num_rows;
+  c.heads = p.num_heads;
+  c.num_splits = g.num_splits;
+  return c;
+}
+
+pkv_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return PKV_OK;
+  return fail(PKV_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pkv_status_string(pkv_status s) {
+  switch (s) {
+    case PKV_OK: return "PKV_OK";
+    case PKV_EINVAL: return "PKV_EINVAL: invalid argument";
+    case PKV_EUNSUPPORTED: return "PKV_EUNSUPPORTED: no kernel for this problem";
+    case PKV_EALIGN: return "PKV_EALIGN: misaligned pointer";
+    case PKV_EWORKSPACE: return "PKV_EWORKSPACE: workspace too small";
+    case PKV_EHIP: return "PKV_EHIP: HIP runtime error";
+    default: return "unknown pkv_status";
+  }
+}
+
+const char* pkv_last_error(void) { return g_err; }
+
+pkv_status split_geometry(const pkv_problem* problem, const pkv_geometry_opts* opts,
+                          pkv_geometry* out) {
+  g_err[0] = 0;
+  if (!out) return fail(PKV_EINVAL, "out is NULL");
+  pkv_status st = check_problem(problem);
+  if (st != PKV_OK) return st;
+  const pkv_problem& p = *problem;
+  pkv_geometry_opts o;
+  std::memset(&o, 0, sizeof(o));
+  if (opts) o = *opts;
+  if (o.num_cus < 0 || o.ctas_per_cu < 0 || o.splits_override < 0 || o.min_chunk < 0 ||
+      o.max_splits < 0 || o.waves < 0)
+    return fail(PKV_EINVAL, "geometry options must be >= 0");
+  const bool gathered = p.max_candidates > 0;
+  const int min_chunk = o.min_chunk ? o.min_chunk : 64;
+  if (min_chunk % 16) return fail(PKV_EINVAL, "min_chunk must be a multiple of 16");
+  const int max_splits = o.max_splits ? o.max_splits : pkv::kMaxSplits;
+  if (max_splits > pkv::kMaxSplits)
+    return fail(PKV_EINVAL, "max_splits %d exceeds %d", max_splits, pkv::kMaxSplits);
+  const int waves = o.waves ? o.waves : 1;
+
+  const int group = p.num_heads / p.num_kv_heads;
+  const int head_blocks = ceil_div(group, 16);
+  const int64_t units = std::max<int64_t>(1, (int64_t)p.num_rows * p.num_kv_heads * head_blocks);
+  const int64_t cap = gathered ? p.max_candidates : (int64_t)p.max_blocks_per_row * p.block_size;
+
+  int S;
+  if (o.splits_override > 0) {
+    S = o.splits_override;
+  } else {
+    int cus = o.num_cus, occ = o.ctas_per_cu;
+    if (cus == 0 || occ == 0) {
+      int qc = 0, qo = 0;
+      st = device_numbers(variant_of(p), &qc, occ == 0 ? &qo : nullptr);
+      if (st != PKV_OK) return st;
+      if (cus == 0) cus = qc;
+      if (occ == 0) occ = qo;
+    }
+    const int64_t target = (int64_t)waves * cus * occ;
+    if (gathered) {
+      // 64-candidate tiles; smallest power-of-two tiles per split for which
+      // all tiles of all units fit the target number of CTAs.
+      const int64_t tiles = (cap + 63) / 64;
+      int64_t tps = 1;
+      while (ceil_div(tiles, tps) * units > target && tps < tiles) tps *= 2;
+      S = ceil_div(tiles, tps);
+    } else {
+      S = (int)std::min<int64_t>(ceil_div(target, units), ceil_div(cap, min_chunk));
+    }
+  }
+  S = std::max(1, std::min(S, max_splits));
+  S = std::max(1, std::min<int>(S, ceil_div(cap, 16)));
+
+  out->num_splits = S;
+  out->min_chunk = min_chunk;
+  out->threads = pkv::kThreads;
+  out->head_blocks = head_blocks;
+  out->grid_x = S;
+  out->grid_y = p.num_kv_heads * head_blocks;
+  out->grid_z = p.num_rows;
+  out->reserved = 0;
+  out->workspace_bytes = workspace_bytes_for(p, S);
+  return PKV_OK;
+}
+
+pkv_status paged_decode_partials(const pkv_problem* problem, const pkv_geometry* geometry,
+                                 const void* query, const void* key_cache,
+                                 const void* value_cache, const int32_t* block_table,
+                                 const int32_t* seq_lens, const int32_t* candidates,
+                                 const int32_t* num_candidates, const float* k_scale,
+                                 const float* v_scale, float softmax_scale, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  g_err[0] = 0;
+  pkv_status st = check_problem(problem);
+  if (st != PKV_OK) return st;
+  st = check_geometry(*problem, geometry);
+  if (st != PKV_OK) return st;
+  const Ptrs x{query, key_cache, value_cache, block_table, seq_lens,
+               candidates, num_candidates, k_scale, v_scale};
+  st = check_inputs(*problem, x, softmax_scale);
+  if (st != PKV_OK) return st;
+  st = check_workspace(*geometry, workspace, workspace_bytes);
+  if (st != PKV_OK) return st;
+  if (problem->num_rows == 0) return PKV_OK;
+  const pkv::SplitArgs a = split_args(*problem, *geometry, x, softmax_scale, workspace);
+  return hip_status(pkv::launch_split(variant_of(*problem), a, static_cast<hipStream_t>(stream)),
+                    "split kernel launch");
+}
+
+pkv_status split_combine(const pkv_problem* problem, const pkv_geometry* geometry,
+                         const void* workspace, size_t workspace_bytes, const float* head_sink,
+                         void* out, float* lse_out, void* stream) {
+  g_err[0] = 0;
+  pkv_status st = check_problem(problem);
+  if (st != PKV_OK) return st;
+  st = check_geometry(*problem, geometry);
+  if (st != PKV_OK) return st;
+  st = check_workspace(*geometry, workspace, workspace_bytes);
+  if (st != PKV_OK) return st;
+  st = check_outputs(out, lse_out, head_sink);
+  if (st != PKV_OK) return st;
+  if (problem->num_rows == 0) return PKV_OK;
+  const pkv::CombineArgs c = combine_args(*problem, *geometry, workspace, head_sink, out, lse_out);
+  return hip_status(pkv::launch_combine(problem->v_head_size, problem->out_dtype, c,
+                                        static_cast<hipStream_t>(stream)),
+                    "combine kernel launch");
+}
+
+pkv_status paged_decode_attention(const pkv_problem* problem, const pkv_geometry* geometry,
+                                  const void* query, const void* key_cache,
+                                  const void* value_cache, const int32_t* block_table,
+                                  const int32_t* seq_lens, const int32_t* candidates,
+                                  const int32_t* num_candidates, const float* k_scale,
+                                  const float* v_scale, float softmax_scale,
+                                  const float* head_sink, void* out, float* lse_out,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+  g_err[0] = 0;
+  pkv_status st = check_problem(problem);
+  if (st != PKV_OK) return st;
+  st = check_geometry(*problem, geometry);
+  if (st != PKV_OK) return st;
+  const Ptrs x{query, key_cache, value_cache, block_table, seq_lens,
+               candidates, num_candidates, k_scale, v_scale};
+  st = check_inputs(*problem, x, softmax_scale);
+  if (st != PKV_OK) return st;
+  st = check_workspace(*geometry, workspace, workspace_bytes);
+  if (st != PKV_OK) return st;
+  st = check_outputs(out, lse_out, head_sink);
+  if (st != PKV_OK) return st;
+  if (problem->num_rows == 0) return PKV_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const pkv::SplitArgs a = split_args(*problem, *geometry, x, softmax_scale, workspace);
+  st = hip_status(pkv::launch_split(variant_of(*problem), a, s), "split kernel launch");
+  if (st != PKV_OK) return st;
+  const pkv::CombineArgs c = combine_args(*problem, *geometry, workspace, head_sink, out, lse_out);
+  return hip_status(pkv::launch_combine(problem->v_head_size, problem->out_dtype, c, s),
+                    "combine kernel launch");
+}
+
+}  // extern "C"

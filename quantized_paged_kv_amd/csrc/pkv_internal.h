@@ -1,0 +1,62 @@
+// pkv_internal.h -- declarations shared by the C-ABI layer (pkv_api.cpp) and
+// the kernels (pkv_kernels.hip).  Not part of the public interface.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/pkv.h"
+
+namespace pkv {
+
+// Everything the split kernel reads, resolved on the host.
+struct SplitArgs {
+  const uint16_t* query;        // [rows, heads, D] fp16 bits
+  const uint8_t* key_cache;     // [pool, B, KVH, D] codes
+  const uint8_t* value_cache;   // [pool, B, KVH, VD] codes (SEPARATE)
+  const int32_t* block_table;   // [rows, max_blocks_per_row]
+  const int32_t* seq_lens;      // [rows]
+  const int32_t* candidates;    // [rows, max_candidates] or null
+  const int32_t* num_candidates;
+  const float* k_scale;         // null for quant NONE
+  const float* v_scale;         // LATENT: the K scales
+  float* ws_acc;                // [rows, heads, S, VD]
+  float* ws_ml;                 // [rows, heads, S, 2]
+  int rows, heads, kv_heads, group, head_blocks;
+  int block_size, max_blocks_per_row, num_pool_blocks, max_candidates;
+  int num_splits, min_chunk;
+  int k_quant, v_quant;         // pkv_quant
+  int v_scale_stride;           // per-channel V scale row stride (VD, or D for LATENT)
+  float score_scale;            // softmax_scale times the code-to-operand factor
+  float v_mult;                 // code-to-operand factor of V (256 for FP8, else 1)
+};
+
+struct CombineArgs {
+  const float* ws_acc;
+  const float* ws_ml;
+  const float* head_sink;       // [heads] or null
+  void* out;                    // [rows, heads, VD]
+  float* lse_out;               // [rows, heads] or null
+  int rows, heads, num_splits;
+};
+
+// Kernel variant key.
+struct Variant {
+  int cache_dtype;  // pkv_dtype
+  int head_size, v_head_size;
+  int latent;
+  int gathered;
+};
+
+constexpr int kWaves = 4;          // waves per split-kernel CTA
+constexpr int kThreads = 64 * kWaves;
+constexpr int kMaxSplits = 64;     // the combine holds one split per lane
+
+// Launchers; return hipSuccess or the launch error.  `supported` reports
+// whether a variant was compiled.
+bool variant_supported(const Variant& v);
+hipError_t launch_split(const Variant& v, const SplitArgs& a, hipStream_t stream);
+hipError_t launch_combine(int v_head_size, int out_dtype, const CombineArgs& a, hipStream_t stream);
+hipError_t split_occupancy(const Variant& v, int* ctas_per_cu);
+
+}  // namespace pkv

@@ -1,0 +1,189 @@
+"""The C-ABI library on the CPU: it loads, exports every declared entry
+point, computes geometry from static shapes (the pages' worked examples) and
+rejects invalid arguments before anything is enqueued.  No kernel runs here:
+every call below fails validation or is a pure host computation."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import quantized_paged_kv_amd as pkv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pkv.h")
+GOLDEN = os.path.join(ROOT, "tests", "golden", "geometry_examples.txt")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return re.findall(r"^\s*(?:pkv_status|const char\*)\s+(\w+)\s*\(", text, flags=re.M)
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_functions()
+    assert set(names) == set(pkv.SYMBOLS)
+    lib = ctypes.CDLL(pkv.LIB_PATH)
+    for n in names:
+        assert getattr(lib, n) is not None
+
+
+def _golden():
+    rows = []
+    for line in open(GOLDEN):
+        line = line.strip()
+        if line and not line.startswith("#"):
+            rows.append(line.split())
+    return rows
+
+
+@pytest.mark.parametrize("row", _golden(), ids=lambda r: r[0])
+def test_geometry_matches_the_pages(row):
+    name, rows, kvh, mbpr, bs, maxc, cus, occ, ovr, minc, maxs, exp_s, exp_ctas = row
+    cand = int(maxc)
+    p = pkv.make_problem(int(rows), int(kvh) * 12, int(kvh), 256, 256, int(bs), int(mbpr), 100000,
+                         max_candidates=cand, cache_dtype="i8", k_quant="channel",
+                         v_quant="channel")
+    g = pkv.split_geometry(p, num_cus=int(cus), ctas_per_cu=int(occ), splits_override=int(ovr),
+                           min_chunk=int(minc), max_splits=int(maxs))
+    assert g.num_splits == int(exp_s)
+    assert g.grid_x * g.grid_y * g.grid_z == int(exp_ctas)
+
+
+def test_geometry_never_depends_on_live_data_and_sizes_workspace():
+    p = pkv.make_problem(16, 32, 8, 128, 128, 16, 512, 5000)
+    g1 = pkv.split_geometry(p, num_cus=256, ctas_per_cu=2)
+    g2 = pkv.split_geometry(p, num_cus=256, ctas_per_cu=2)
+    assert g1.as_dict() == g2.as_dict()
+    S = g1.num_splits
+    assert g1.workspace_bytes == 16 * 32 * S * (128 + 2) * 4
+    assert (g1.grid_x, g1.grid_y, g1.grid_z) == (S, 8, 16)
+    # more heads per KV head than one 16-wide tile: head blocks
+    p2 = pkv.make_problem(2, 40, 2, 128, 128, 16, 64, 500)
+    g = pkv.split_geometry(p2, num_cus=256, ctas_per_cu=2)
+    assert g.head_blocks == 2 and g.grid_y == 4
+
+
+def test_geometry_caps():
+    p = pkv.make_problem(1, 4, 1, 64, 64, 16, 1, 8)  # capacity 16 tokens
+    g = pkv.split_geometry(p, num_cus=256, ctas_per_cu=8, splits_override=50)
+    assert g.num_splits == 1
+    p = pkv.make_problem(1, 4, 1, 64, 64, 16, 4096, 5000)
+    g = pkv.split_geometry(p, num_cus=256, ctas_per_cu=8)
+    assert g.num_splits == 64
+    with pytest.raises(pkv.PkvError):
+        pkv.split_geometry(p, num_cus=256, ctas_per_cu=8, max_splits=65)
+    with pytest.raises(pkv.PkvError):
+        pkv.split_geometry(p, num_cus=256, ctas_per_cu=8, min_chunk=24)
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("num_heads", 7, 1), ("num_kv_heads", 0, 1), ("head_size", 96, 2), ("v_head_size", 32, 2),
+    ("block_size", 24, 2), ("block_size", 0, 2), ("max_blocks_per_row", 0, 1),
+    ("num_pool_blocks", 0, 1), ("cache_dtype", 3, 1), ("out_dtype", 1, 1),
+    ("k_quant", 3, 1), ("layout", 2, 1), ("num_rows", -1, 1), ("max_candidates", -1, 1),
+])
+def test_problem_validation(field, value, status):
+    p = pkv.make_problem(2, 8, 2, 128, 128, 16, 8, 32)
+    setattr(p, field, value)
+    with pytest.raises(pkv.PkvError) as e:
+        pkv.split_geometry(p, num_cus=4, ctas_per_cu=1)
+    assert e.value.status == status
+
+
+def test_quantised_cache_needs_scales_kind():
+    p = pkv.make_problem(2, 8, 2, 128, 128, 16, 8, 32, cache_dtype="i8", k_quant="none",
+                         v_quant="tensor")
+    with pytest.raises(pkv.PkvError) as e:
+        pkv.split_geometry(p, num_cus=4, ctas_per_cu=1)
+    assert e.value.status == 1
+
+
+# Fake device addresses: never dereferenced, because every call below fails
+# validation before anything is enqueued.
+A = 1 << 20  # 16-byte aligned
+
+
+def _args(**over):
+    a = dict(query=A, key_cache=A, value_cache=A, block_table=A, seq_lens=A, candidates=None,
+             num_candidates=None, k_scale=None, v_scale=None, softmax_scale=0.125,
+             head_sink=None, out=A, lse_out=None, workspace=A)
+    a.update(over)
+    return a
+
+
+def _call(p, g, a, workspace_bytes):
+    pkv.paged_decode_attention(p, g, a["query"], a["key_cache"], a["value_cache"],
+                               a["block_table"], a["seq_lens"], a["candidates"],
+                               a["num_candidates"], a["k_scale"], a["v_scale"],
+                               a["softmax_scale"], a["head_sink"], a["out"], a["lse_out"],
+                               a["workspace"], workspace_bytes=workspace_bytes, stream=0)
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(query=None), 1), (dict(key_cache=None), 1), (dict(value_cache=None), 1),
+    (dict(block_table=None), 1), (dict(seq_lens=None), 1), (dict(out=None), 1),
+    (dict(workspace=None), 1), (dict(softmax_scale=float("nan")), 1),
+    (dict(softmax_scale=-1.0), 1), (dict(softmax_scale=float("inf")), 1),
+    (dict(query=A + 8), 3), (dict(key_cache=A + 4), 3), (dict(value_cache=A + 2), 3),
+    (dict(out=A + 8), 3), (dict(workspace=A + 4), 3), (dict(block_table=A + 2), 3),
+    (dict(lse_out=A + 2), 3),
+])
+def test_call_validation(over, status):
+    p = pkv.make_problem(2, 8, 2, 128, 128, 16, 8, 32)
+    g = pkv.split_geometry(p, num_cus=4, ctas_per_cu=1)
+    with pytest.raises(pkv.PkvError) as e:
+        _call(p, g, _args(**over), g.workspace_bytes)
+    assert e.value.status == status
+
+
+def test_workspace_too_small_and_foreign_geometry():
+    p = pkv.make_problem(2, 8, 2, 128, 128, 16, 8, 32)
+    g = pkv.split_geometry(p, num_cus=4, ctas_per_cu=1)
+    with pytest.raises(pkv.PkvError) as e:
+        _call(p, g, _args(query=None), g.workspace_bytes)  # sanity: fails on the NULL first
+    assert e.value.status == 1
+    with pytest.raises(pkv.PkvError) as e:
+        _call(p, g, _args(key_cache=None), g.workspace_bytes - 1)
+    assert e.value.status == 1
+    p2 = pkv.make_problem(3, 8, 2, 128, 128, 16, 8, 32)
+    with pytest.raises(pkv.PkvError) as e:
+        _call(p2, g, _args(out=None), g.workspace_bytes)
+    assert e.value.status == 1 and "geometry" in str(e.value)
+
+
+def test_workspace_size_error_code():
+    # every pointer valid-looking but the workspace too small: rejected before launch
+    p = pkv.make_problem(2, 8, 2, 128, 128, 16, 8, 32)
+    g = pkv.split_geometry(p, num_cus=4, ctas_per_cu=1)
+    with pytest.raises(pkv.PkvError) as e:
+        _call(p, g, _args(), g.workspace_bytes - 4)
+    assert e.value.status == 4
+
+
+def test_gathered_and_scale_requirements():
+    p = pkv.make_problem(2, 8, 2, 128, 128, 16, 8, 32, max_candidates=4)
+    g = pkv.split_geometry(p, num_cus=4, ctas_per_cu=1)
+    with pytest.raises(pkv.PkvError) as e:
+        _call(p, g, _args(), g.workspace_bytes)
+    assert e.value.status == 1 and "candidates" in str(e.value)
+    p = pkv.make_problem(2, 8, 2, 128, 128, 16, 8, 32, cache_dtype="i8", k_quant="tensor",
+                         v_quant="channel")
+    g = pkv.split_geometry(p, num_cus=4, ctas_per_cu=1)
+    with pytest.raises(pkv.PkvError) as e:
+        _call(p, g, _args(k_scale=A), g.workspace_bytes)
+    assert e.value.status == 1 and "v_scale" in str(e.value)
+    with pytest.raises(pkv.PkvError) as e:
+        _call(p, g, _args(k_scale=A, v_scale=A + 4), g.workspace_bytes)
+    assert e.value.status == 3
+    # latent: no value cache, v_scale NULL or the K scales
+    p = pkv.make_problem(2, 16, 1, 576, 512, 64, 8, 32, cache_dtype="fp8", k_quant="tensor",
+                         layout="latent")
+    g = pkv.split_geometry(p, num_cus=4, ctas_per_cu=1)
+    with pytest.raises(pkv.PkvError) as e:
+        _call(p, g, _args(k_scale=A), g.workspace_bytes)
+    assert e.value.status == 1 and "value_cache" in str(e.value)
+    with pytest.raises(pkv.PkvError) as e:
+        _call(p, g, _args(k_scale=A, value_cache=None, v_scale=A + 64), g.workspace_bytes)
+    assert e.value.status == 1
