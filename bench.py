@@ -117,6 +117,8 @@ def main():
                     help="cold-cache protocol: replicate the cache until this many bytes")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--splits", type=int, default=0, help="split-count override (0 = automatic)")
+    ap.add_argument("--min-chunk", type=int, default=0, help="geometry min_chunk (0 = default)")
+    ap.add_argument("--waves", type=int, default=0, help="geometry target waves (0 = default)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -142,7 +144,8 @@ def main():
     kv_bytes = inp.effective_kv_bytes()
     d = to_device(inp, dev)
     prob = pkv.make_problem(**d.problem_kwargs)
-    geo = pkv.split_geometry(prob, splits_override=args.splits)
+    geo = pkv.split_geometry(prob, splits_override=args.splits, min_chunk=args.min_chunk,
+                             waves=args.waves)
     ws = pkv.workspace_for(geo, dev)
 
     # cold-cache replicas of the caches (the block table, lengths, Q, scales are shared)

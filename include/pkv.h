@@ -102,7 +102,7 @@ typedef enum { PKV_SEPARATE = 0, PKV_LATENT = 1 } pkv_layout;
 
 /* Static description of one decode step; nothing here depends on live data.
  * Supported: (head_size, v_head_size) in {(64,64), (128,128), (256,256)} for
- * SEPARATE and (576,512) for LATENT; block_size a positive multiple of 16;
+ * SEPARATE and (576,512) for LATENT; block_size a power of two >= 16;
  * cache_dtype F16 (any quant), I8 or FP8_E4M3FN (quant PER_TENSOR or
  * PER_CHANNEL); out_dtype F16 or F32; num_heads a multiple of num_kv_heads. */
 typedef struct {
@@ -138,8 +138,8 @@ typedef struct {
   int32_t min_chunk;        /* positions per active split are >= this */
   int32_t threads;          /* threads per CTA of the split kernel */
   int32_t head_blocks;      /* ceil(group / 16): query heads go 16 per CTA */
-  int32_t grid_x, grid_y, grid_z;  /* split-kernel grid: S, kv_heads*head_blocks, rows */
-  int32_t reserved;
+  int32_t grid_x, grid_y, grid_z;  /* split-kernel grid (1-D: grid_y = grid_z = 1) */
+  int32_t target_ctas;      /* active CTAs the live chunk size aims at (0: per-row rule) */
   uint64_t workspace_bytes; /* bytes of workspace the calls below need */
 } pkv_geometry;
 
@@ -149,17 +149,30 @@ typedef struct {
  * units = num_rows * num_kv_heads * ceil(group / 16);
  * cap   = max_blocks_per_row * block_size (dense) or max_candidates
  *         (gathered);  resident = num_cus * ctas_per_cu.
- * Dense rows (onnx-genai PR #1350 "Summary"):
- *   S = min(ceil(waves * resident / units), ceil(cap / min_chunk), max_splits)
+ * Dense rows (onnx-genai PR #1350 "Summary"; target = waves * resident):
+ *   S = min(ceil(target / units), ceil(cap / min_chunk), max_splits)
+ *   (see below for the factor 4 of the live-balanced mode)
  * Gathered rows (ONNX Runtime PR #33707 section 2, split count rule): the
  *   unit of work is a 64-candidate tile; tiles-per-split is the smallest
  *   power of two for which ceil(tiles / tps) * units <= waves * resident;
  *   S = min(ceil(tiles / tps), max_splits).
  * A positive splits_override replaces the automatic count (then clipped to
- * [1, max_splits] and to ceil(cap / 16)).  On the device each row spreads its
- * live positions evenly over n = min(S, ceil(len / min_chunk)) splits in
- * 16-position steps; splits beyond that publish an empty partial.
- * Defaults: min_chunk 64 (gathered: 64), max_splits 64, waves 1.
+ * [1, max_splits] and to ceil(cap / 16)).
+ * On the device (graph safe, from live data): with target_ctas > 0 every CTA
+ * sums the live positions of all rows (npos_r = clamped seq_len, or clamped
+ * num_candidates for gathered rows) and takes one chunk
+ *   c = max(min_chunk, round_up_16(ceil(sum_r npos_r * units_per_row / target_ctas)))
+ * so that about target_ctas CTAs of similar work run; row r then uses
+ * n_r = clamp(ceil(npos_r / c), 1, S) splits, and the 1-D grid's CTAs take
+ * the work items (row, KV head x head block, split) in that order (the
+ * grid holds min(units * S, target_ctas + units) CTAs; spare ones exit).
+ * With target_ctas = 0 (more than 1024 rows) CTA i is item i of the static
+ * (row, unit, split < S) list and n_r = min(S, ceil(npos_r / min_chunk)).
+ * A row's n_r splits share its positions evenly in 16-position steps;
+ * splits beyond n_r publish an empty partial.  In the live-balanced
+ * mode the automatic S allows rows up to four times the mean work:
+ *   S = min(ceil(4 * target / units), ceil(cap / min_chunk), max_splits).
+ * Defaults: min_chunk 64, max_splits 64, waves 1.
  * Returns PKV_EINVAL / PKV_EUNSUPPORTED as paged_decode_attention would, or
  * PKV_EHIP if the device query fails.  Does not touch device memory.
  */

@@ -41,10 +41,10 @@ class GeometryOpts(ctypes.Structure):
 class Geometry(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "num_splits", "min_chunk", "threads", "head_blocks", "grid_x", "grid_y", "grid_z",
-        "reserved")] + [("workspace_bytes", ctypes.c_uint64)]
+        "target_ctas")] + [("workspace_bytes", ctypes.c_uint64)]
 
     def as_dict(self):
-        return {n: getattr(self, n) for n, _ in self._fields_ if n != "reserved"}
+        return {n: getattr(self, n) for n, _ in self._fields_}
 
 
 class PkvError(RuntimeError):

@@ -26,6 +26,8 @@ pkv_status fail(pkv_status st, const char* fmt, ...) {
 
 int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
 
+using pkv::kMaxBalancedRows;
+
 bool aligned(const void* p, size_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
 
 pkv::Variant variant_of(const pkv_problem& p) {
@@ -48,8 +50,8 @@ pkv_status check_problem(const pkv_problem* p) {
     return fail(PKV_EINVAL, "num_heads (%d) is not a multiple of num_kv_heads (%d)", p->num_heads,
                 p->num_kv_heads);
   if (p->head_size <= 0 || p->v_head_size <= 0) return fail(PKV_EINVAL, "head sizes must be positive");
-  if (p->block_size <= 0 || p->block_size % 16)
-    return fail(PKV_EUNSUPPORTED, "block_size (%d) must be a positive multiple of 16", p->block_size);
+  if (p->block_size < 16 || (p->block_size & (p->block_size - 1)))
+    return fail(PKV_EUNSUPPORTED, "block_size (%d) must be a power of two >= 16", p->block_size);
   if (p->max_blocks_per_row <= 0) return fail(PKV_EINVAL, "max_blocks_per_row must be positive");
   if (p->num_pool_blocks <= 0) return fail(PKV_EINVAL, "num_pool_blocks must be positive");
   if ((int64_t)p->max_blocks_per_row * p->block_size > INT32_MAX)
@@ -70,8 +72,9 @@ pkv_status check_problem(const pkv_problem* p) {
     if (p->layout == PKV_SEPARATE && p->v_quant == PKV_QUANT_NONE)
       return fail(PKV_EINVAL, "a quantised cache needs v_quant PER_TENSOR or PER_CHANNEL");
   }
-  if (p->num_rows > 65535 || (int64_t)p->num_kv_heads * ceil_div(p->num_heads / p->num_kv_heads, 16) > 65535)
-    return fail(PKV_EUNSUPPORTED, "num_rows and num_kv_heads * ceil(group / 16) must be <= 65535");
+  if ((int64_t)p->num_rows * p->num_kv_heads * ceil_div(p->num_heads / p->num_kv_heads, 16) * 64 >
+      INT32_MAX)
+    return fail(PKV_EUNSUPPORTED, "num_rows * num_kv_heads * ceil(group / 16) is too large");
   if (p->layout == PKV_LATENT && p->v_head_size > p->head_size)
     return fail(PKV_EINVAL, "LATENT needs v_head_size <= head_size");
   if (!pkv::variant_supported(variant_of(*p)))
@@ -85,6 +88,17 @@ pkv_status check_problem(const pkv_problem* p) {
 uint64_t workspace_bytes_for(const pkv_problem& p, int S) {
   const uint64_t pairs = (uint64_t)p.num_rows * p.num_heads;
   return pairs * S * p.v_head_size * sizeof(float) + pairs * S * 2 * sizeof(float);
+}
+
+// CTAs of the split kernel's 1-D grid.  Static mode: one per (row, unit,
+// split).  Live-balanced mode: the work items are at most
+// target + rows * units (each row rounds its split count up by less than one
+// chunk), and never more than the static count.
+int64_t grid_ctas_for(const pkv_problem& p, int S, int target) {
+  const int64_t units = (int64_t)p.num_rows * p.num_kv_heads *
+                        ceil_div(p.num_heads / p.num_kv_heads, 16);
+  const int64_t all = units * S;
+  return target > 0 ? std::min<int64_t>(all, (int64_t)target + units) : all;
 }
 
 // Per-device cache of (CU count, occupancy per variant).
@@ -134,8 +148,9 @@ pkv_status check_geometry(const pkv_problem& p, const pkv_geometry* g) {
   if (g->min_chunk < 16 || g->min_chunk % 16)
     return fail(PKV_EINVAL, "geometry min_chunk %d is not a positive multiple of 16", g->min_chunk);
   if (g->head_blocks != ceil_div(group, 16) || g->threads != pkv::kThreads ||
-      g->grid_x != g->num_splits || g->grid_y != p.num_kv_heads * g->head_blocks ||
-      g->grid_z != p.num_rows || g->workspace_bytes != workspace_bytes_for(p, g->num_splits))
+      g->grid_x != grid_ctas_for(p, g->num_splits, g->target_ctas) || g->grid_y != 1 ||
+      g->grid_z != 1 || g->workspace_bytes != workspace_bytes_for(p, g->num_splits) ||
+      g->target_ctas < 0 || (g->target_ctas > 0 && p.num_rows > kMaxBalancedRows))
     return fail(PKV_EINVAL, "geometry does not belong to this problem (call split_geometry)");
   return PKV_OK;
 }
@@ -223,17 +238,19 @@ pkv::SplitArgs split_args(const pkv_problem& p, const pkv_geometry& g, const Ptr
   a.group = p.num_heads / p.num_kv_heads;
   a.head_blocks = g.head_blocks;
   a.block_size = p.block_size;
+  a.log2_block = __builtin_ctz((unsigned)p.block_size);
   a.max_blocks_per_row = p.max_blocks_per_row;
   a.num_pool_blocks = p.num_pool_blocks;
   a.max_candidates = p.max_candidates;
   a.num_splits = g.num_splits;
   a.min_chunk = g.min_chunk;
+  a.target_ctas = g.target_ctas;
+  a.grid_ctas = g.grid_x;
   a.k_quant = p.k_quant;
   a.v_quant = latent ? p.k_quant : p.v_quant;
   a.v_scale_stride = latent ? p.head_size : p.v_head_size;
-  const float code_factor = p.cache_dtype == PKV_FP8_E4M3FN ? 256.0f : 1.0f;
-  a.score_scale = softmax_scale * code_factor;
-  a.v_mult = code_factor;
+  a.score_scale = softmax_scale;
+  a.v_mult = 1.0f;
   return a;
 }
 
@@ -301,19 +318,22 @@ pkv_status split_geometry(const pkv_problem* problem, const pkv_geometry_opts* o
   const int64_t units = std::max<int64_t>(1, (int64_t)p.num_rows * p.num_kv_heads * head_blocks);
   const int64_t cap = gathered ? p.max_candidates : (int64_t)p.max_blocks_per_row * p.block_size;
 
+  // The device balances chunk sizes across rows from the live lengths when
+  // the row count is modest (each CTA reads every row's length).
+  const bool balanced = p.num_rows <= kMaxBalancedRows;
+  int cus = o.num_cus, occ = o.ctas_per_cu;
+  if (cus == 0 || occ == 0) {
+    int qc = 0, qo = 0;
+    st = device_numbers(variant_of(p), &qc, occ == 0 ? &qo : nullptr);
+    if (st != PKV_OK) return st;
+    if (cus == 0) cus = qc;
+    if (occ == 0) occ = qo;
+  }
+  const int64_t target = (int64_t)waves * cus * occ;
   int S;
   if (o.splits_override > 0) {
     S = o.splits_override;
   } else {
-    int cus = o.num_cus, occ = o.ctas_per_cu;
-    if (cus == 0 || occ == 0) {
-      int qc = 0, qo = 0;
-      st = device_numbers(variant_of(p), &qc, occ == 0 ? &qo : nullptr);
-      if (st != PKV_OK) return st;
-      if (cus == 0) cus = qc;
-      if (occ == 0) occ = qo;
-    }
-    const int64_t target = (int64_t)waves * cus * occ;
     if (gathered) {
       // 64-candidate tiles; smallest power-of-two tiles per split for which
       // all tiles of all units fit the target number of CTAs.
@@ -322,7 +342,9 @@ pkv_status split_geometry(const pkv_problem* problem, const pkv_geometry_opts* o
       while (ceil_div(tiles, tps) * units > target && tps < tiles) tps *= 2;
       S = ceil_div(tiles, tps);
     } else {
-      S = (int)std::min<int64_t>(ceil_div(target, units), ceil_div(cap, min_chunk));
+      // live-balanced chunks: leave room for rows up to 4x the mean work
+      const int64_t want = balanced ? 4 * target : target;
+      S = (int)std::min<int64_t>(ceil_div(want, units), ceil_div(cap, min_chunk));
     }
   }
   S = std::max(1, std::min(S, max_splits));
@@ -332,10 +354,12 @@ pkv_status split_geometry(const pkv_problem* problem, const pkv_geometry_opts* o
   out->min_chunk = min_chunk;
   out->threads = pkv::kThreads;
   out->head_blocks = head_blocks;
-  out->grid_x = S;
-  out->grid_y = p.num_kv_heads * head_blocks;
-  out->grid_z = p.num_rows;
-  out->reserved = 0;
+  out->target_ctas = balanced ? (int32_t)std::min<int64_t>(target, INT32_MAX) : 0;
+  const int64_t grid = grid_ctas_for(p, S, out->target_ctas);
+  if (grid > INT32_MAX) return fail(PKV_EUNSUPPORTED, "too many CTAs (%lld)", (long long)grid);
+  out->grid_x = (int32_t)grid;
+  out->grid_y = 1;
+  out->grid_z = 1;
   out->workspace_bytes = workspace_bytes_for(p, S);
   return PKV_OK;
 }

