@@ -46,10 +46,10 @@ def kernel_source_hash() -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def read_traffic(workload: str):
-    """HBM bytes per split-kernel launch from the committed counter summary,
+def read_traffic(kernel: str, workload: str):
+    """HBM bytes per launch of `kernel` from the committed counter summary,
     if it was taken on this kernel source; else None."""
-    path = os.path.join(ROOT, "profiles", f"split_kernel_{workload}_counters.txt")
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_counters.txt")
     if not os.path.exists(path):
         return None
     fields = {}
@@ -119,6 +119,12 @@ def main():
     ap.add_argument("--splits", type=int, default=0, help="split-count override (0 = automatic)")
     ap.add_argument("--min-chunk", type=int, default=0, help="geometry min_chunk (0 = default)")
     ap.add_argument("--waves", type=int, default=0, help="geometry target waves (0 = default)")
+    ap.add_argument("--eager", action="store_true",
+                    help="launch every step eagerly instead of from a HIP graph (for "
+                         "per-dispatch hardware counters)")
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="only run 4 plain device-to-device copies of this many bytes and exit "
+                         "(calibrates the HBM byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -133,10 +139,19 @@ def main():
     import workloads
     from workloads.device import to_device
 
-    pkv.load()
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.copy_bytes > 0:
+        a = torch.ones(args.copy_bytes, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        for _ in range(4):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        log(f"copied {args.copy_bytes} bytes 4 times")
+        return 0
+    pkv.load()
 
     log(f"generating {args.workload}")
     inp = workloads.workload(args.workload)
@@ -177,7 +192,17 @@ def main():
         step(i)
     torch.cuda.synchronize()
 
+    class Eager:
+        def __init__(self, fn, n):
+            self.fn, self.n = fn, n
+
+        def replay(self):
+            for i in range(self.n):
+                self.fn(i)
+
     def capture(fn, n):
+        if args.eager:
+            return Eager(fn, n)
         g = torch.cuda.CUDAGraph()
         s = torch.cuda.Stream()
         s.wait_stream(torch.cuda.current_stream())
@@ -217,7 +242,8 @@ def main():
 
     value = kv_bytes / (ms_step * 1e-3) / 1e9
     achieved = kv_bytes / (ms_split * 1e-3) / 1e9
-    traffic = read_traffic(args.workload)
+    kernel = "latent_kernel" if p.layout == "latent" else "split_kernel"
+    traffic = read_traffic(kernel, args.workload)
     log(f"step {ms_step * 1e3:.2f} us ({value:.0f} GB/s), split kernel {ms_split * 1e3:.2f} us "
         f"({achieved:.0f} GB/s)")
 
@@ -244,7 +270,8 @@ def main():
                        "accumulation; fp32 softmax",
             "num_splits": geo.num_splits,
             "cold_cache_replicas": R,
-            "timing": "one HIP-graph replay of K steps, HIP events on the launch stream",
+            "timing": ("K eager launches" if args.eager else "one HIP-graph replay of K steps")
+                      + ", HIP events on the launch stream",
         },
         "roofline": {
             "bound": "hbm",
@@ -253,7 +280,7 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic,
-            "kernel": "split_kernel (paged_decode_partials)",
+            "kernel": f"{kernel} (paged_decode_partials)",
             "kernel_us": round(ms_split * 1e3, 3),
             "algorithmic_bytes_per_launch": kv_bytes,
         },

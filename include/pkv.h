@@ -130,6 +130,8 @@ typedef struct {
   int32_t min_chunk;        /* smallest positions per split (multiple of 16) */
   int32_t max_splits;       /* cap on the split count */
   int32_t waves;            /* target = waves * num_cus * ctas_per_cu CTAs */
+  int32_t balance;          /* 0: auto (live-balanced for 16..1024 rows), 1: live-
+                               balanced (up to 1024 rows), 2: static */
 } pkv_geometry_opts;
 
 /* Launch geometry; produced by split_geometry, consumed unchanged. */
@@ -166,13 +168,18 @@ typedef struct {
  * n_r = clamp(ceil(npos_r / c), 1, S) splits, and the 1-D grid's CTAs take
  * the work items (row, KV head x head block, split) in that order (the
  * grid holds min(units * S, target_ctas + units) CTAs; spare ones exit).
- * With target_ctas = 0 (more than 1024 rows) CTA i is item i of the static
- * (row, unit, split < S) list and n_r = min(S, ceil(npos_r / min_chunk)).
  * A row's n_r splits share its positions evenly in 16-position steps;
- * splits beyond n_r publish an empty partial.  In the live-balanced
+ * splits beyond n_r publish an empty partial.
+ * Static mode (target_ctas = 0: opts.balance = 2, fewer than 16 rows under
+ * auto, or more than 1024 rows): CTA i is item i of the (row, unit,
+ * split < S) list and split k covers positions [k c, (k + 1) c) with
+ * c = max(min_chunk, round_up_16(ceil(cap / S))); splits past the live length publish an
+ * empty partial.  In the live-balanced
  * mode the automatic S allows rows up to four times the mean work:
  *   S = min(ceil(4 * target / units), ceil(cap / min_chunk), max_splits).
- * Defaults: min_chunk 64, max_splits 64, waves 1.
+ * Defaults: min_chunk 64, max_splits 64; waves 2 in the live-balanced mode
+ * when a split's partial (group * (v_head_size + 2) * 4 bytes) is less than
+ * half the KV bytes of min_chunk positions, else 1.
  * Returns PKV_EINVAL / PKV_EUNSUPPORTED as paged_decode_attention would, or
  * PKV_EHIP if the device query fails.  Does not touch device memory.
  */

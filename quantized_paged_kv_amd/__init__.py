@@ -35,7 +35,8 @@ class Problem(ctypes.Structure):
 
 class GeometryOpts(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
-        "num_cus", "ctas_per_cu", "splits_override", "min_chunk", "max_splits", "waves")]
+        "num_cus", "ctas_per_cu", "splits_override", "min_chunk", "max_splits", "waves",
+        "balance")]
 
 
 class Geometry(ctypes.Structure):
@@ -109,9 +110,9 @@ def make_problem(num_rows, num_heads, num_kv_heads, head_size, v_head_size, bloc
 
 
 def split_geometry(problem: Problem, num_cus=0, ctas_per_cu=0, splits_override=0, min_chunk=0,
-                   max_splits=0, waves=0) -> Geometry:
+                   max_splits=0, waves=0, balance=0) -> Geometry:
     opts = GeometryOpts(int(num_cus), int(ctas_per_cu), int(splits_override), int(min_chunk),
-                        int(max_splits), int(waves))
+                        int(max_splits), int(waves), int(balance))
     g = Geometry()
     _check(load().split_geometry(ctypes.byref(problem), ctypes.byref(opts), ctypes.byref(g)))
     return g

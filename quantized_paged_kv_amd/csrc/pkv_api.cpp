@@ -27,6 +27,9 @@ pkv_status fail(pkv_status st, const char* fmt, ...) {
 int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
 
 using pkv::kMaxBalancedRows;
+// Fewer rows than this: the static decomposition (its first block reads do
+// not wait for the live lengths, which matters more than balance there).
+constexpr int kMinBalancedRows = 16;
 
 bool aligned(const void* p, size_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
 
@@ -246,6 +249,12 @@ pkv::SplitArgs split_args(const pkv_problem& p, const pkv_geometry& g, const Ptr
   a.min_chunk = g.min_chunk;
   a.target_ctas = g.target_ctas;
   a.grid_ctas = g.grid_x;
+  {
+    const int64_t cap_pos = p.max_candidates > 0 ? p.max_candidates
+                                                 : (int64_t)p.max_blocks_per_row * p.block_size;
+    a.static_chunk = std::max<int>(g.min_chunk,
+                                   (int)((((cap_pos + g.num_splits - 1) / g.num_splits) + 15) / 16 * 16));
+  }
   a.k_quant = p.k_quant;
   a.v_quant = latent ? p.k_quant : p.v_quant;
   a.v_scale_stride = latent ? p.head_size : p.v_head_size;
@@ -266,6 +275,7 @@ pkv::CombineArgs combine_args(const pkv_problem& p, const pkv_geometry& g, const
   c.rows = p.num_rows;
   c.heads = p.num_heads;
   c.num_splits = g.num_splits;
+  c.skip_empty = g.target_ctas > 0;
   return c;
 }
 
@@ -311,7 +321,7 @@ pkv_status split_geometry(const pkv_problem* problem, const pkv_geometry_opts* o
   const int max_splits = o.max_splits ? o.max_splits : pkv::kMaxSplits;
   if (max_splits > pkv::kMaxSplits)
     return fail(PKV_EINVAL, "max_splits %d exceeds %d", max_splits, pkv::kMaxSplits);
-  const int waves = o.waves ? o.waves : 1;
+  const int waves_req = o.waves;
 
   const int group = p.num_heads / p.num_kv_heads;
   const int head_blocks = ceil_div(group, 16);
@@ -320,7 +330,9 @@ pkv_status split_geometry(const pkv_problem* problem, const pkv_geometry_opts* o
 
   // The device balances chunk sizes across rows from the live lengths when
   // the row count is modest (each CTA reads every row's length).
-  const bool balanced = p.num_rows <= kMaxBalancedRows;
+  if (o.balance < 0 || o.balance > 2) return fail(PKV_EINVAL, "balance must be 0, 1 or 2");
+  const bool balanced = p.num_rows <= kMaxBalancedRows &&
+                        (o.balance == 1 || (o.balance == 0 && p.num_rows >= kMinBalancedRows));
   int cus = o.num_cus, occ = o.ctas_per_cu;
   if (cus == 0 || occ == 0) {
     int qc = 0, qo = 0;
@@ -329,6 +341,17 @@ pkv_status split_geometry(const pkv_problem* problem, const pkv_geometry_opts* o
     if (cus == 0) cus = qc;
     if (occ == 0) occ = qo;
   }
+  // Live-balanced mode: about two rounds of CTAs per resident slot let the
+  // dispatcher even out what per-row rounding leaves (measured on MI355X),
+  // unless a split's partial (written once, read once by the combine) is at
+  // least half the KV bytes of a min_chunk -- then halving the chunk costs
+  // more traffic than it saves (latent rows: 16 heads x 512 FP32 per split).
+  const int64_t partial_bytes = (int64_t)(p.num_heads / p.num_kv_heads) * (p.v_head_size + 2) * 4;
+  const int64_t row_bytes = (int64_t)(p.layout == PKV_LATENT ? p.head_size
+                                                             : p.head_size + p.v_head_size) *
+                            (p.cache_dtype == PKV_F16 ? 2 : 1);
+  const bool cheap_partials = 2 * partial_bytes < row_bytes * min_chunk;
+  const int waves = waves_req ? waves_req : (balanced && cheap_partials ? 2 : 1);
   const int64_t target = (int64_t)waves * cus * occ;
   int S;
   if (o.splits_override > 0) {

@@ -27,6 +27,7 @@ struct SplitArgs {
   int num_splits, min_chunk;
   int target_ctas;              // > 0: live chunk from the total work of all rows
   int grid_ctas;                // 1-D grid of the split kernel
+  int static_chunk;             // static mode: positions per split
   int k_quant, v_quant;         // pkv_quant
   int v_scale_stride;           // per-channel V scale row stride (VD, or D for LATENT)
   float score_scale;            // softmax_scale (codes enter the MFMAs at their value)
@@ -40,6 +41,7 @@ struct CombineArgs {
   void* out;                    // [rows, heads, VD]
   float* lse_out;               // [rows, heads] or null
   int rows, heads, num_splits;
+  int skip_empty;               // read only splits with a nonzero weight
 };
 
 // Kernel variant key.

@@ -266,7 +266,7 @@ __device__ __forceinline__ bool locate_work(const SplitArgs& a, int lane, Work& 
     u = rem / S;
     split = rem - u * S;
     npos = __builtin_amdgcn_readfirstlane(row_positions<GATHER>(a, r, cap));
-    n_row = npos > 0 ? min(S, (npos + a.min_chunk - 1) / a.min_chunk) : 0;
+    n_row = S;
   }
   w.r = r;
   w.u = u;
@@ -283,11 +283,24 @@ __device__ __forceinline__ bool locate_work(const SplitArgs& a, int lane, Work& 
 
 // Position range [p0, p1) of the work item; publishes the empty partials
 // (m = -inf, l = 0; accumulators are never read) this CTA is responsible
-// for and returns false when its own range is empty.
+// for and returns false when its own range is empty.  Live-balanced mode:
+// the row's n_row splits share its positions evenly in 16-position steps.
+// Static mode: split k covers [k c, (k + 1) c) with the host's chunk c, so
+// p0 is known before any length is read.
+__device__ __forceinline__ int static_p0(const SplitArgs& a, int split) {
+  return split * a.static_chunk;
+}
+
 __device__ __forceinline__ bool split_range(const SplitArgs& a, const Work& w, int& p0, int& p1) {
   const int S = a.num_splits;
-  const int chunk = w.n_row > 0 ? (((w.npos + w.n_row - 1) / w.n_row + 15) & ~15) : 0;
-  p0 = w.split * chunk;
+  int chunk;
+  if (a.target_ctas > 0) {
+    chunk = w.n_row > 0 ? (((w.npos + w.n_row - 1) / w.n_row + 15) & ~15) : 0;
+    p0 = w.split * chunk;
+  } else {
+    chunk = a.static_chunk;
+    p0 = static_p0(a, w.split);
+  }
   p1 = min(w.npos, p0 + chunk);
   const size_t pair0 = (size_t)w.r * a.heads + w.h0;
   float2* const ml = reinterpret_cast<float2*>(a.ws_ml);
@@ -297,7 +310,7 @@ __device__ __forceinline__ bool split_range(const SplitArgs& a, const Work& w, i
     for (int e = threadIdx.x; e < w.nh * (S - w.n_row); e += kThreads)
       ml[(pair0 + e % w.nh) * S + w.n_row + e / w.nh] = make_float2(kNegInf, 0.0f);
   }
-  if (w.split >= w.n_row || p0 >= w.npos) {
+  if (p0 >= w.npos || (a.target_ctas > 0 && w.split >= w.n_row)) {
     if (threadIdx.x < w.nh) ml[(pair0 + threadIdx.x) * S + w.split] = make_float2(kNegInf, 0.0f);
     return false;
   }
@@ -315,48 +328,71 @@ __device__ __forceinline__ int q_channel(int ks, int lj) {
 }
 
 template <int NKS, int EB, int D, int QPT>
-__device__ __forceinline__ void q_issue(const SplitArgs& a, const Work& w, uint4 (&qraw)[QPT]) {
+__device__ __forceinline__ void q_issue(const SplitArgs& a, const Work& w, uint4 (&qraw)[QPT],
+                                        float4 (&ksc)[QPT][2]) {
 #pragma unroll
   for (int i = 0; i < QPT; ++i) {
     const int e = threadIdx.x + i * kThreads;
     qraw[i] = uint4{0u, 0u, 0u, 0u};
+    ksc[i][0] = ksc[i][1] = make_float4(1.f, 1.f, 1.f, 1.f);
     if (e < NKS * 64) {
       const int ks = e >> 6, el = e & 63, eli = el & 15, elj = el >> 4;
+      const int d0 = q_channel<EB>(ks, elj);
       if (eli < w.nh)
-        qraw[i] = *reinterpret_cast<const uint4*>(a.query + ((size_t)w.r * a.heads + w.h0 + eli) * D +
-                                                  q_channel<EB>(ks, elj));
+        qraw[i] = *reinterpret_cast<const uint4*>(a.query + ((size_t)w.r * a.heads + w.h0 + eli) * D + d0);
+      if (a.k_quant == PKV_QUANT_PER_CHANNEL) {
+        const float4* kp = reinterpret_cast<const float4*>(a.k_scale + (size_t)w.g * D + d0);
+        ksc[i][0] = kp[0];
+        ksc[i][1] = kp[1];
+      }
     }
   }
 }
 
+// ks_tensor: the per-tensor key scale (1 when not per tensor).
 template <int NKS, int EB, int D, int QPT>
-__device__ __forceinline__ void q_stage(const SplitArgs& a, const Work& w, const uint4 (&qraw)[QPT],
-                                        uint4* s_q) {
+__device__ __forceinline__ void q_stage(const uint4 (&qraw)[QPT], const float4 (&ksc)[QPT][2],
+                                        float ks_tensor, uint4* s_q) {
 #pragma unroll
   for (int i = 0; i < QPT; ++i) {
     const int e = threadIdx.x + i * kThreads;
     if (e < NKS * 64) {
-      const int ks = e >> 6, elj = (e & 63) >> 4;
-      const int d0 = q_channel<EB>(ks, elj);
       const half8 q = __builtin_bit_cast(half8, qraw[i]);
+      const float kc[8] = {ksc[i][0].x, ksc[i][0].y, ksc[i][0].z, ksc[i][0].w,
+                           ksc[i][1].x, ksc[i][1].y, ksc[i][1].z, ksc[i][1].w};
       half8 o;
 #pragma unroll
-      for (int x = 0; x < 8; ++x) {
-        float ks_e = 1.0f;
-        if (a.k_quant == PKV_QUANT_PER_TENSOR) ks_e = a.k_scale[0];
-        else if (a.k_quant == PKV_QUANT_PER_CHANNEL) ks_e = a.k_scale[(size_t)w.g * D + d0 + x];
-        o[x] = (half_t)((float)q[x] * ks_e);
-      }
+      for (int x = 0; x < 8; ++x) o[x] = (half_t)((float)q[x] * (kc[x] * ks_tensor));
       s_q[e] = __builtin_bit_cast(uint4, o);
     }
   }
 }
 
-// Value scale of channel c of KV head g (applied once, after accumulation).
-__device__ __forceinline__ float v_scale_of(const SplitArgs& a, int g, int c) {
-  if (a.v_quant == PKV_QUANT_PER_TENSOR) return a.v_scale[0];
-  if (a.v_quant == PKV_QUANT_PER_CHANNEL) return a.v_scale[(size_t)g * a.v_scale_stride + c];
-  return 1.0f;
+// Scales read in the prologue, so the epilogue issues no dependent load:
+// per-tensor values in SGPRs, per-channel value scales of the KV head in LDS.
+struct Scales {
+  float k_tensor;  // per-tensor key scale, else 1
+  float v_tensor;  // per-tensor value scale, else 1
+};
+
+template <int VD>
+__device__ __forceinline__ Scales load_scales(const SplitArgs& a, int g, float* s_vs) {
+  Scales sc;
+  sc.k_tensor = a.k_quant == PKV_QUANT_PER_TENSOR ? a.k_scale[0] : 1.0f;
+  sc.v_tensor = a.v_quant == PKV_QUANT_PER_TENSOR ? a.v_scale[0] : 1.0f;
+  if (a.v_quant == PKV_QUANT_PER_CHANNEL) {
+    for (int c = threadIdx.x; c < VD / 4; c += kThreads)
+      reinterpret_cast<float4*>(s_vs)[c] =
+          *reinterpret_cast<const float4*>(a.v_scale + (size_t)g * a.v_scale_stride + 4 * c);
+  }
+  return sc;
+}
+
+// Value scale of channel c (applied once, after accumulation); s_vs holds
+// the per-channel scales of the CTA's KV head.
+__device__ __forceinline__ float v_scale_of(const SplitArgs& a, const Scales& sc, const float* s_vs,
+                                            int c) {
+  return a.v_quant == PKV_QUANT_PER_CHANNEL ? s_vs[c] : sc.v_tensor;
 }
 
 template <int CT, int D, int VD, bool LATENT, bool GATHER>
@@ -380,15 +416,31 @@ split_kernel(const SplitArgs a) {
   const int r = wk.r, g = wk.g, h0 = wk.h0, nh = wk.nh, len = wk.len;
 
   __shared__ uint4 s_q[C::NKS * 64];
+  __shared__ float s_vs[VD];
   constexpr int QPT = (C::NKS * 64 + kThreads - 1) / kThreads;  // entries per thread
   uint4 qraw[QPT];
-  q_issue<C::NKS, C::EB, D>(a, wk, qraw);
+  float4 ksc[QPT][2];
+  q_issue<C::NKS, C::EB, D>(a, wk, qraw, ksc);
+  const Scales sc = load_scales<VD>(a, g, s_vs);
+  const int32_t* bt_row = a.block_table + (size_t)r * a.max_blocks_per_row;
+  const int cap_pos = a.max_blocks_per_row * a.block_size;
+  // static mode: the first tiles' block ids do not depend on the live length,
+  // so read them now, alongside it
+  int pre_blk[NST - 1];
+  if constexpr (!GATHER) {
+    const int p0s = static_p0(a, wk.split);
+#pragma unroll
+    for (int i = 0; i < NST - 1; ++i) {
+      const int tp = p0s + 16 * (wave + i * W);
+      pre_blk[i] = (a.target_ctas == 0 && tp < cap_pos)
+                       ? __builtin_amdgcn_readfirstlane(bt_row[tp >> a.log2_block]) : 0;
+    }
+  }
 
   int p0, p1;
   if (!split_range(a, wk, p0, p1)) return;
   const int split = wk.split;
   const int ntiles = (p1 - p0 + 15) >> 4;
-  const int32_t* bt_row = a.block_table + (size_t)r * a.max_blocks_per_row;
 
   // Per-lane byte offsets inside a 16-token tile of one block (dense rows):
   // K: row of token li, 16-byte chunk lj (+64 s);  V: rows of tokens 4 lj + q
@@ -402,7 +454,8 @@ split_kernel(const SplitArgs a) {
   // Issue the loads of tile t into T.  Tiles at or past ntiles issue loads
   // that read nothing (dense rows: an empty buffer descriptor) so every
   // iteration issues the same instruction stream.
-  auto issue = [&](Tile<C>& T, int t) {
+  // pre >= 0: the block id was read in the prologue (pre_blk[pre]).
+  auto issue = [&](Tile<C>& T, int t, int pre) {
     const int tp = p0 + 16 * t;  // first position of the tile
     uint32_t vm = 0;
     if constexpr (!GATHER) {
@@ -410,7 +463,8 @@ split_kernel(const SplitArgs a) {
       bool bv = false;
       if (t < ntiles) {
         // the address is wave-uniform; keep the block id in an SGPR
-        blk = __builtin_amdgcn_readfirstlane(bt_row[tp >> a.log2_block]);
+        blk = (pre >= 0 && a.target_ctas == 0)
+                  ? pre_blk[pre] : __builtin_amdgcn_readfirstlane(bt_row[tp >> a.log2_block]);
         bv = blk >= 0 && blk < a.num_pool_blocks;
       }
       const int64_t s0 = bv ? ((int64_t)blk << a.log2_block) + (tp & (a.block_size - 1)) : 0;
@@ -545,10 +599,10 @@ split_kernel(const SplitArgs a) {
   // tiles in flight while one is consumed -----------------------------------
   Tile<C> buf[NST];
 #pragma unroll
-  for (int i = 0; i < NST - 1; ++i) issue(buf[i], wave + i * W);
+  for (int i = 0; i < NST - 1; ++i) issue(buf[i], wave + i * W, i);
 
   // Q' into LDS (its loads were issued before the tile loads above)
-  q_stage<C::NKS, C::EB, D>(a, wk, qraw, s_q);
+  q_stage<C::NKS, C::EB, D>(qraw, ksc, sc.k_tensor, s_q);
   __syncthreads();
 
   for (int t = wave; t < ntiles; t += NST * W) {
@@ -556,7 +610,7 @@ split_kernel(const SplitArgs a) {
     for (int st = 0; st < NST; ++st) {
       const int tt = t + st * W;
       if (tt >= ntiles) break;
-      issue(buf[(st + NST - 1) % NST], tt + (NST - 1) * W);
+      issue(buf[(st + NST - 1) % NST], tt + (NST - 1) * W, -1);
       consume(buf[st]);
     }
   }
@@ -626,7 +680,7 @@ split_kernel(const SplitArgs a) {
         float4 o;
         float* op = reinterpret_cast<float*>(&o);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) op[e] = (acc[ct + e][q] * a.v_mult) * v_scale_of(a, g, cbase + ct + e);
+        for (int e = 0; e < 4; ++e) op[e] = (acc[ct + e][q] * a.v_mult) * v_scale_of(a, sc, s_vs, cbase + ct + e);
         *reinterpret_cast<float4*>(dst + cbase + ct) = o;
       }
     }
@@ -693,16 +747,19 @@ latent_kernel(const SplitArgs a) {
 
   __shared__ uint4 s_q[C::NKS * 64];
   __shared__ f32x4 s_sc[2][W][64];  // published scores, double buffered by round
+  __shared__ float s_vs[C::VD];
   constexpr int QPT = (C::NKS * 64 + kThreads - 1) / kThreads;
   uint4 qraw[QPT];
-  q_issue<C::NKS, C::EB, D>(a, wk, qraw);
+  float4 ksc[QPT][2];
+  q_issue<C::NKS, C::EB, D>(a, wk, qraw, ksc);
+  const Scales sc = load_scales<C::VD>(a, g, s_vs);
+  const int32_t* bt_row = a.block_table + (size_t)r * a.max_blocks_per_row;
 
   int p0, p1;
   if (!split_range(a, wk, p0, p1)) return;
   const int split = wk.split;
   const int ntiles = (p1 - p0 + 15) >> 4;
   const int nrounds = (ntiles + W - 1) / W;
-  const int32_t* bt_row = a.block_table + (size_t)r * a.max_blocks_per_row;
 
   const uint32_t tok = (uint32_t)KVH * C::KROW;  // bytes per token slot
   const uint32_t koff = (uint32_t)li * tok + (uint32_t)g * C::KROW + 16u * lj;
@@ -876,7 +933,7 @@ latent_kernel(const SplitArgs a) {
   LatK<C> ka, kb;
   LatV<C> vbuf;
   issue_k(ka, wave);
-  q_stage<C::NKS, C::EB, D>(a, wk, qraw, s_q);
+  q_stage<C::NKS, C::EB, D>(qraw, ksc, sc.k_tensor, s_q);
   __syncthreads();
   for (int rd = 0; rd < nrounds; rd += 2) {
     issue_v(vbuf, rd);
@@ -905,7 +962,7 @@ latent_kernel(const SplitArgs a) {
         float* op = reinterpret_cast<float*>(&o);
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          op[e] = (acc[ct + e][q] * a.v_mult) * v_scale_of(a, g, cbase + ct + e);
+          op[e] = (acc[ct + e][q] * a.v_mult) * v_scale_of(a, sc, s_vs, cbase + ct + e);
         *reinterpret_cast<float4*>(dst + cbase + ct) = o;
       }
     }
@@ -960,15 +1017,27 @@ combine_kernel(const CombineArgs a) {
     }
   }
 
-  // issue every partial load of this thread before using any of them
+  // Static decomposition: issue every partial load before the weights are
+  // known (a short row's empty splits are read and ignored).  Live-balanced
+  // decomposition: most of the S slots of a row can be empty, so read only
+  // the splits with a nonzero weight.
   const float* base = a.ws_acc + (size_t)pair * S * VD + cg * 4;
   float4 v[MAXI];
+  if (!a.skip_empty) {
 #pragma unroll
-  for (int i = 0; i < MAXI; ++i) {
-    const int k = ks + i * KS;
-    if (k < S) v[i] = *reinterpret_cast<const float4*>(base + (size_t)k * VD);
+    for (int i = 0; i < MAXI; ++i) {
+      const int k = ks + i * KS;
+      if (k < S) v[i] = *reinterpret_cast<const float4*>(base + (size_t)k * VD);
+    }
   }
   __syncthreads();
+  if (a.skip_empty) {
+#pragma unroll
+    for (int i = 0; i < MAXI; ++i) {
+      const int k = ks + i * KS;
+      if (k < S && s_w[k] != 0.0f) v[i] = *reinterpret_cast<const float4*>(base + (size_t)k * VD);
+    }
+  }
   float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
   for (int i = 0; i < MAXI; ++i) {

@@ -64,7 +64,13 @@ def test_geometry_never_depends_on_live_data_and_sizes_workspace():
     # more heads per KV head than one 16-wide tile: head blocks
     p2 = pkv.make_problem(2, 40, 2, 128, 128, 16, 64, 500)
     g = pkv.split_geometry(p2, num_cus=256, ctas_per_cu=2)
-    assert g.head_blocks == 2 and g.grid_x == min(2 * 4 * g.num_splits, g.target_ctas + 8)
+    # two rows: the static decomposition, one CTA per (row, unit, split)
+    assert g.head_blocks == 2 and g.target_ctas == 0 and g.grid_x == 2 * 4 * g.num_splits
+    gb = pkv.split_geometry(p2, num_cus=256, ctas_per_cu=2, balance=1)
+    # live-balanced default: two rounds of the 512 resident CTAs
+    assert gb.target_ctas == 1024 and gb.grid_x == min(2 * 4 * gb.num_splits, 1024 + 8)
+    gw = pkv.split_geometry(p2, num_cus=256, ctas_per_cu=2, balance=1, waves=1)
+    assert gw.target_ctas == 512 and gw.grid_x == min(2 * 4 * gw.num_splits, 512 + 8)
 
 
 def test_geometry_caps():
