@@ -88,6 +88,21 @@ __device__ __forceinline__ half4 codes4_to_half4(uint32_t x) {
   else return fp8x4_to_half4(x);
 }
 
+// ---- wave-uniform reads ----------------------------------------------------
+//
+// A value every lane of a wave needs at the same index (a block id of a
+// 16-token tile, a row length) is read with a scalar load through the
+// constant address space: it lands in an SGPR and is waited for with the
+// scalar/LDS counter.  Read as a vector load, waiting for it would also wait
+// for every K/V load issued before it (vector loads complete in order),
+// draining the prefetch pipeline.  The arrays read this way (block table,
+// lengths) are never written while a kernel runs.
+typedef const __attribute__((address_space(4))) int32_t cint32_t;
+
+__device__ __forceinline__ int uniform_load(const int32_t* p, size_t idx) {
+  return ((cint32_t*)p)[idx];  // address-space cast (C-style; not expressible as a C++ cast)
+}
+
 // ---- global loads of NB bytes into dwords ---------------------------------
 
 template <int NB>
@@ -265,7 +280,8 @@ __device__ __forceinline__ bool locate_work(const SplitArgs& a, int lane, Work& 
     const int rem = c - r * units_row * S;
     u = rem / S;
     split = rem - u * S;
-    npos = __builtin_amdgcn_readfirstlane(row_positions<GATHER>(a, r, cap));
+    npos = GATHER ? min(max(uniform_load(a.num_candidates, r), 0), a.max_candidates)
+                  : min(max(uniform_load(a.seq_lens, r), 0), cap);
     n_row = S;
   }
   w.r = r;
@@ -273,7 +289,7 @@ __device__ __forceinline__ bool locate_work(const SplitArgs& a, int lane, Work& 
   w.split = split;
   w.n_row = n_row;
   w.npos = npos;
-  w.len = GATHER ? min(max(__builtin_amdgcn_readfirstlane(a.seq_lens[r]), 0), cap) : npos;
+  w.len = GATHER ? min(max(uniform_load(a.seq_lens, r), 0), cap) : npos;
   w.g = u / a.head_blocks;
   w.hb = u - w.g * a.head_blocks;
   w.h0 = w.g * a.group + w.hb * 16;
@@ -432,8 +448,7 @@ split_kernel(const SplitArgs a) {
 #pragma unroll
     for (int i = 0; i < NST - 1; ++i) {
       const int tp = p0s + 16 * (wave + i * W);
-      pre_blk[i] = (a.target_ctas == 0 && tp < cap_pos)
-                       ? __builtin_amdgcn_readfirstlane(bt_row[tp >> a.log2_block]) : 0;
+      pre_blk[i] = (a.target_ctas == 0 && tp < cap_pos) ? uniform_load(bt_row, tp >> a.log2_block) : 0;
     }
   }
 
@@ -463,8 +478,7 @@ split_kernel(const SplitArgs a) {
       bool bv = false;
       if (t < ntiles) {
         // the address is wave-uniform; keep the block id in an SGPR
-        blk = (pre >= 0 && a.target_ctas == 0)
-                  ? pre_blk[pre] : __builtin_amdgcn_readfirstlane(bt_row[tp >> a.log2_block]);
+        blk = (pre >= 0 && a.target_ctas == 0) ? pre_blk[pre] : uniform_load(bt_row, tp >> a.log2_block);
         bv = blk >= 0 && blk < a.num_pool_blocks;
       }
       const int64_t s0 = bv ? ((int64_t)blk << a.log2_block) + (tp & (a.block_size - 1)) : 0;
@@ -611,6 +625,8 @@ split_kernel(const SplitArgs a) {
       const int tt = t + st * W;
       if (tt >= ntiles) break;
       issue(buf[(st + NST - 1) % NST], tt + (NST - 1) * W, -1);
+      // keep the loads ahead of the wait for this tile's data
+      __builtin_amdgcn_sched_barrier(0);
       consume(buf[st]);
     }
   }
@@ -770,7 +786,7 @@ latent_kernel(const SplitArgs a) {
   auto tile_block = [&](int t, int64_t& s0) -> bool {
     if (t >= ntiles) return false;
     const int tp = p0 + 16 * t;
-    const int blk = __builtin_amdgcn_readfirstlane(bt_row[tp >> a.log2_block]);
+    const int blk = uniform_load(bt_row, tp >> a.log2_block);
     if (blk < 0 || blk >= a.num_pool_blocks) return false;
     s0 = ((int64_t)blk << a.log2_block) + (tp & (a.block_size - 1));
     return true;
@@ -938,10 +954,12 @@ latent_kernel(const SplitArgs a) {
   for (int rd = 0; rd < nrounds; rd += 2) {
     issue_v(vbuf, rd);
     issue_k(kb, (rd + 1) * W + wave);
+    __builtin_amdgcn_sched_barrier(0);
     round(ka, vbuf, rd);
     if (rd + 1 >= nrounds) break;
     issue_v(vbuf, rd + 1);
     issue_k(ka, (rd + 2) * W + wave);
+    __builtin_amdgcn_sched_barrier(0);
     round(kb, vbuf, rd + 1);
   }
 
