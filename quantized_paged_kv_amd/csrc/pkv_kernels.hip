@@ -103,6 +103,10 @@ __device__ __forceinline__ int uniform_load(const int32_t* p, size_t idx) {
   return ((cint32_t*)p)[idx];  // address-space cast (C-style; not expressible as a C++ cast)
 }
 
+__device__ __forceinline__ float uniform_load(const float* p, size_t idx) {
+  return ((const __attribute__((address_space(4))) float*)p)[idx];
+}
+
 // ---- global loads of NB bytes into dwords ---------------------------------
 
 template <int NB>
@@ -215,86 +219,104 @@ struct Work {
 // (row, unit, split) are numbered row by row, so consecutive CTAs -- which
 // the hardware spreads round-robin over the XCDs -- carry equal work and no
 // CTA launches only to find nothing to do (except trailing padding).  All
-// row lengths are read in one round trip (lane i holds rows i + 64 k).
-// Static mode: CTA c is (row, unit, split) = c decomposed with S splits,
-// n_r = min(S, ceil(npos_r / min_chunk)).
+// row lengths are read in one round trip (lane i holds rows i + 64 k; the
+// loads are issued unconditionally, from clamped indices).
 template <bool GATHER>
-__device__ __forceinline__ bool locate_work(const SplitArgs& a, int lane, Work& w) {
+__device__ __forceinline__ bool locate_balanced(const SplitArgs& a, int lane, Work& w) {
   const int S = a.num_splits;
   const int units_row = a.kv_heads * a.head_blocks;
   const int cap = a.max_blocks_per_row * a.block_size;
   const int c = blockIdx.x;
-  int r, u, split, n_row, npos;
-  if (a.target_ctas > 0) {
-    int np[kMaxBalancedRows / 64];
-    int tot = 0;
+  constexpr int NR = kMaxBalancedRows / 64;
+  int raw[NR];
 #pragma unroll
-    for (int i = 0; i < kMaxBalancedRows / 64; ++i) {
-      const int rr = lane + 64 * i;
-      np[i] = rr < a.rows ? row_positions<GATHER>(a, rr, cap) : 0;
-      tot += np[i];
-    }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) tot += __shfl_xor(tot, off);
-    const int64_t work = (int64_t)__builtin_amdgcn_readfirstlane(tot) * units_row;
-    const int64_t cl = (work + a.target_ctas - 1) / a.target_ctas;
-    const int cgl = max(a.min_chunk, (int)min<int64_t>(((cl + 15) >> 4) << 4, 1 << 30));
-    int base = 0;
-    r = -1;
-    u = split = n_row = npos = 0;
-#pragma unroll
-    for (int i = 0; i < kMaxBalancedRows / 64; ++i) {
-      if (64 * i >= a.rows) break;
-      const int rr = lane + 64 * i;
-      const int n = rr < a.rows ? min(S, max(1, (np[i] + cgl - 1) / cgl)) : 0;
-      const int items = n * units_row;
-      int incl = items;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const int t = __shfl_up(incl, off);
-        if (lane >= off) incl += t;
-      }
-      const int excl = incl - items;
-      const bool hit = c >= base + excl && c < base + incl;
-      const uint64_t m = __ballot(hit);
-      if (m) {
-        const int src = __builtin_ctzll(m);
-        r = 64 * i + src;
-        const int off = c - base - __shfl(excl, src);
-        n_row = __shfl(n, src);
-        npos = __shfl(np[i], src);
-        u = off / n_row;
-        split = off - u * n_row;
-        break;
-      }
-      base += __shfl(incl, 63);
-    }
-    r = __builtin_amdgcn_readfirstlane(r);
-    if (r < 0) return false;
-    u = __builtin_amdgcn_readfirstlane(u);
-    split = __builtin_amdgcn_readfirstlane(split);
-    n_row = __builtin_amdgcn_readfirstlane(n_row);
-    npos = __builtin_amdgcn_readfirstlane(npos);
-  } else {
-    r = c / (units_row * S);
-    const int rem = c - r * units_row * S;
-    u = rem / S;
-    split = rem - u * S;
-    npos = GATHER ? min(max(uniform_load(a.num_candidates, r), 0), a.max_candidates)
-                  : min(max(uniform_load(a.seq_lens, r), 0), cap);
-    n_row = S;
+  for (int i = 0; i < NR; ++i) {
+    const int rr = min(lane + 64 * i, a.rows - 1);
+    raw[i] = GATHER ? a.num_candidates[rr] : a.seq_lens[rr];
   }
+  int np[NR];
+  int tot = 0;
+#pragma unroll
+  for (int i = 0; i < NR; ++i) {
+    const int rr = lane + 64 * i;
+    np[i] = rr < a.rows ? min(max(raw[i], 0), GATHER ? a.max_candidates : cap) : 0;
+    tot += np[i];
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) tot += __shfl_xor(tot, off);
+  const int64_t work = (int64_t)__builtin_amdgcn_readfirstlane(tot) * units_row;
+  const int64_t cl = (work + a.target_ctas - 1) / a.target_ctas;
+  const int cgl = max(a.min_chunk, (int)min<int64_t>(((cl + 15) >> 4) << 4, 1 << 30));
+  int base = 0;
+  int r = -1, u = 0, split = 0, n_row = 0, npos = 0;
+#pragma unroll
+  for (int i = 0; i < NR; ++i) {
+    if (64 * i >= a.rows) break;
+    const int rr = lane + 64 * i;
+    const int n = rr < a.rows ? min(S, max(1, (np[i] + cgl - 1) / cgl)) : 0;
+    const int items = n * units_row;
+    int incl = items;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int t = __shfl_up(incl, off);
+      if (lane >= off) incl += t;
+    }
+    const int excl = incl - items;
+    const bool hit = c >= base + excl && c < base + incl;
+    const uint64_t m = __ballot(hit);
+    if (m) {
+      const int src = __builtin_ctzll(m);
+      r = 64 * i + src;
+      const int off = c - base - __shfl(excl, src);
+      n_row = __shfl(n, src);
+      npos = __shfl(np[i], src);
+      u = off / n_row;
+      split = off - u * n_row;
+      break;
+    }
+    base += __shfl(incl, 63);
+  }
+  r = __builtin_amdgcn_readfirstlane(r);
+  if (r < 0) return false;
   w.r = r;
-  w.u = u;
-  w.split = split;
-  w.n_row = n_row;
-  w.npos = npos;
-  w.len = GATHER ? min(max(uniform_load(a.seq_lens, r), 0), cap) : npos;
-  w.g = u / a.head_blocks;
-  w.hb = u - w.g * a.head_blocks;
+  w.u = __builtin_amdgcn_readfirstlane(u);
+  w.split = __builtin_amdgcn_readfirstlane(split);
+  w.n_row = __builtin_amdgcn_readfirstlane(n_row);
+  w.npos = __builtin_amdgcn_readfirstlane(npos);
+  w.len = w.npos;
+  return true;
+}
+
+// Static mode (target_ctas == 0): CTA c is item c of the (row, unit,
+// split < S) list; nothing is read.
+__device__ __forceinline__ void static_item(const SplitArgs& a, Work& w) {
+  const int S = a.num_splits;
+  const int units_row = a.kv_heads * a.head_blocks;
+  const int c = blockIdx.x;
+  w.r = c / (units_row * S);
+  const int rem = c - w.r * units_row * S;
+  w.u = rem / S;
+  w.split = rem - w.u * S;
+  w.n_row = S;
+  w.npos = w.len = 0;
+}
+
+__device__ __forceinline__ void unit_heads(const SplitArgs& a, Work& w) {
+  w.g = w.u / a.head_blocks;
+  w.hb = w.u - w.g * a.head_blocks;
   w.h0 = w.g * a.group + w.hb * 16;
   w.nh = min(16, a.group - w.hb * 16);
-  return true;
+}
+
+// Clamped lengths from the raw values read in the prologue: raw_npos (static
+// mode: seq_len, or num_candidates of gathered rows) and raw_len (gathered
+// rows: seq_len, which bounds the valid candidate indices).
+template <bool GATHER>
+__device__ __forceinline__ void finish_item(const SplitArgs& a, Work& w, bool balanced,
+                                            int raw_npos, int raw_len) {
+  const int cap = a.max_blocks_per_row * a.block_size;
+  if (!balanced) w.npos = min(max(raw_npos, 0), GATHER ? a.max_candidates : cap);
+  w.len = GATHER ? min(max(raw_len, 0), cap) : w.npos;
 }
 
 // Position range [p0, p1) of the work item; publishes the empty partials
@@ -385,23 +407,30 @@ __device__ __forceinline__ void q_stage(const uint4 (&qraw)[QPT], const float4 (
 }
 
 // Scales read in the prologue, so the epilogue issues no dependent load:
-// per-tensor values in SGPRs, per-channel value scales of the KV head in LDS.
+// per-tensor values in SGPRs, per-channel value scales of the KV head
+// loaded into registers (vs) and copied to LDS with the query (stage_scales).
 struct Scales {
   float k_tensor;  // per-tensor key scale, else 1
   float v_tensor;  // per-tensor value scale, else 1
+  float4 vs;       // this thread's float4 of the per-channel value scales
 };
 
 template <int VD>
-__device__ __forceinline__ Scales load_scales(const SplitArgs& a, int g, float* s_vs) {
+__device__ __forceinline__ Scales load_scales(const SplitArgs& a, int g) {
+  static_assert(VD / 4 <= kThreads, "one float4 of value scales per thread");
   Scales sc;
-  sc.k_tensor = a.k_quant == PKV_QUANT_PER_TENSOR ? a.k_scale[0] : 1.0f;
-  sc.v_tensor = a.v_quant == PKV_QUANT_PER_TENSOR ? a.v_scale[0] : 1.0f;
-  if (a.v_quant == PKV_QUANT_PER_CHANNEL) {
-    for (int c = threadIdx.x; c < VD / 4; c += kThreads)
-      reinterpret_cast<float4*>(s_vs)[c] =
-          *reinterpret_cast<const float4*>(a.v_scale + (size_t)g * a.v_scale_stride + 4 * c);
-  }
+  sc.k_tensor = a.k_quant == PKV_QUANT_PER_TENSOR ? uniform_load(a.k_scale, 0) : 1.0f;
+  sc.v_tensor = a.v_quant == PKV_QUANT_PER_TENSOR ? uniform_load(a.v_scale, 0) : 1.0f;
+  sc.vs = make_float4(1.f, 1.f, 1.f, 1.f);
+  if (a.v_quant == PKV_QUANT_PER_CHANNEL && threadIdx.x < VD / 4)
+    sc.vs = *reinterpret_cast<const float4*>(a.v_scale + (size_t)g * a.v_scale_stride + 4 * threadIdx.x);
   return sc;
+}
+
+template <int VD>
+__device__ __forceinline__ void stage_scales(const SplitArgs& a, const Scales& sc, float* s_vs) {
+  if (a.v_quant == PKV_QUANT_PER_CHANNEL && threadIdx.x < VD / 4)
+    reinterpret_cast<float4*>(s_vs)[threadIdx.x] = sc.vs;
 }
 
 // Value scale of channel c (applied once, after accumulation); s_vs holds
@@ -427,9 +456,20 @@ split_kernel(const SplitArgs a) {
 
   const int S = a.num_splits;
   const int KVH = a.kv_heads;
+  // ---- prologue: every independent read is issued before the first wait
+  // (static mode: row length, first block ids, scales and query together)
+  const bool balanced = a.target_ctas > 0;
   Work wk;
-  if (!locate_work<GATHER>(a, lane, wk)) return;  // padding CTA
-  const int r = wk.r, g = wk.g, h0 = wk.h0, nh = wk.nh, len = wk.len;
+  int raw_npos = 0, raw_len = 0;
+  if (balanced) {
+    if (!locate_balanced<GATHER>(a, lane, wk)) return;  // padding CTA
+  } else {
+    static_item(a, wk);
+    raw_npos = GATHER ? uniform_load(a.num_candidates, wk.r) : uniform_load(a.seq_lens, wk.r);
+  }
+  if constexpr (GATHER) raw_len = uniform_load(a.seq_lens, wk.r);
+  unit_heads(a, wk);
+  const int r = wk.r, g = wk.g, h0 = wk.h0, nh = wk.nh;
 
   __shared__ uint4 s_q[C::NKS * 64];
   __shared__ float s_vs[VD];
@@ -437,20 +477,20 @@ split_kernel(const SplitArgs a) {
   uint4 qraw[QPT];
   float4 ksc[QPT][2];
   q_issue<C::NKS, C::EB, D>(a, wk, qraw, ksc);
-  const Scales sc = load_scales<VD>(a, g, s_vs);
+  const Scales sc = load_scales<VD>(a, g);
   const int32_t* bt_row = a.block_table + (size_t)r * a.max_blocks_per_row;
-  const int cap_pos = a.max_blocks_per_row * a.block_size;
-  // static mode: the first tiles' block ids do not depend on the live length,
-  // so read them now, alongside it
+  // static mode: the first tiles' block ids do not depend on the live length
   int pre_blk[NST - 1];
   if constexpr (!GATHER) {
     const int p0s = static_p0(a, wk.split);
 #pragma unroll
     for (int i = 0; i < NST - 1; ++i) {
-      const int tp = p0s + 16 * (wave + i * W);
-      pre_blk[i] = (a.target_ctas == 0 && tp < cap_pos) ? uniform_load(bt_row, tp >> a.log2_block) : 0;
+      const int bi = min((p0s + 16 * (wave + i * W)) >> a.log2_block, a.max_blocks_per_row - 1);
+      pre_blk[i] = balanced ? 0 : uniform_load(bt_row, bi);
     }
   }
+  finish_item<GATHER>(a, wk, balanced, raw_npos, raw_len);
+  const int len = wk.len;
 
   int p0, p1;
   if (!split_range(a, wk, p0, p1)) return;
@@ -482,15 +522,19 @@ split_kernel(const SplitArgs a) {
         bv = blk >= 0 && blk < a.num_pool_blocks;
       }
       const int64_t s0 = bv ? ((int64_t)blk << a.log2_block) + (tp & (a.block_size - 1)) : 0;
-      const auto krs = make_rsrc(a.key_cache + s0 * tok_k, bv ? 16u * tok_k : 0u);
+      // the descriptors cover the tile's valid rows only: rows past the end
+      // (and a whole tile with an invalid block) read as zeros, so the V
+      // operands need no mask
+      const uint32_t nv = bv ? (uint32_t)min(16, p1 - tp) : 0u;
+      const auto krs = make_rsrc(a.key_cache + s0 * tok_k, nv * tok_k);
 #pragma unroll
       for (int s = 0; s < C::NKL; ++s) buffer_bytes<16>(krs, koff + 64 * s, 0, &T.k[4 * s]);
       const uint8_t* vbase = LATENT ? a.key_cache : a.value_cache;
-      const auto vrs = make_rsrc(vbase + s0 * tok_v, bv ? 16u * tok_v : 0u);
+      const auto vrs = make_rsrc(vbase + s0 * tok_v, nv * tok_v);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        buffer_bytes<C::VSEG>(vrs, voff, (uint32_t)q * tok_v, T.v[q]);
-        vm |= (bv && (tp + 4 * lj + q < p1)) ? (1u << q) : 0u;
+        buffer_bytes<C::VSEG>(vrs, voff + (uint32_t)q * tok_v, 0, T.v[q]);
+        vm |= (4 * lj + q < (int)nv) ? (1u << q) : 0u;
       }
     } else {
       // gathered rows: per-token slots; invalid entries (and tiles past the
@@ -578,7 +622,7 @@ split_kernel(const SplitArgs a) {
     // 4 lj .. 4 lj + 3 (rows q = 0..3 of its segments), transposed in registers
     uint32_t vz[4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) vz[q] = ((T.vmask >> q) & 1u) ? 0xffffffffu : 0u;
+    for (int q = 0; q < 4; ++q) vz[q] = (GATHER && !((T.vmask >> q) & 1u)) ? 0u : 0xffffffffu;
     if constexpr (C::EB == 2) {
 #pragma unroll
       for (int w = 0; w < C::NVW; ++w) {
@@ -617,6 +661,7 @@ split_kernel(const SplitArgs a) {
 
   // Q' into LDS (its loads were issued before the tile loads above)
   q_stage<C::NKS, C::EB, D>(qraw, ksc, sc.k_tensor, s_q);
+  stage_scales<VD>(a, sc, s_vs);
   __syncthreads();
 
   for (int t = wave; t < ntiles; t += NST * W) {
@@ -705,16 +750,20 @@ split_kernel(const SplitArgs a) {
 
 // ---- the latent (absorbed-MLA) kernel -------------------------------------
 //
-// One cache row per token supplies K (all 576 channels) and V (the first 512
+// One cache row per token supplies K (all 576 channels) and V (its first 512
 // channels).  A CTA walks its position range in rounds of four 16-token
-// tiles.  In each round wave w computes the scores S^T = K Q'^T of tile w
-// and publishes them in LDS; after one barrier every wave runs the same
-// online softmax over all 64 tokens (so all waves hold the same running
-// maximum and sum), and the PV product is split by channels: wave w
-// accumulates V channels [128 w, 128 w + 128) of all four tiles.  Each wave
-// therefore keeps a 16 x 128 accumulator instead of 16 x 512, no
-// accumulator merge is needed, K bytes come from HBM once (the V re-read of
-// the same rows, issued one QK phase later, is served by L2).
+// tiles.  In round rd wave w
+//   * computes the scores S^T = K Q'^T of tile w from its K registers
+//     (fetched two rounds ahead) and publishes them in LDS,
+//   * copies the tile's raw codes into the round's LDS stage (64 rows),
+//   * runs, like every wave, the online softmax over all 64 tokens (so all
+//     waves hold the same running maximum and sum), and
+//   * accumulates V channels [128 w, 128 w + 128) of all 64 tokens, reading
+//     the V^T operands from the stage with the LDS transpose reads.
+// Each row therefore crosses HBM and L2 once, V needs no registers while in
+// flight, and each wave keeps a 16 x 128 accumulator instead of 16 x 512.
+// Stage rows are padded so that the four token groups of a transposed V
+// read fall on disjoint LDS banks.
 
 template <int CT, bool GATHER>
 struct LatCfg {
@@ -725,23 +774,36 @@ struct LatCfg {
   static constexpr int NKL = KROW / 64;          // 16-byte K loads per lane per tile
   static constexpr int NKW = NKL * 4;
   static constexpr int VQ = VD / kWaves;         // V channels per wave
-  static constexpr int VSEG = VQ * EB / 16;      // V bytes per lane per row
-  static constexpr int NVW = VSEG / 4;
-  static constexpr int CPL = VQ / 16;            // channels per lane per row = col tiles
+  static constexpr int CPL = VQ / 16;            // 16-channel column tiles per wave
+  static constexpr int RS = KROW + 32 * EB;      // LDS stage row stride (bytes)
+  static constexpr int ROUND = 16 * kWaves;      // tokens per round
   static constexpr int MIN_WAVES = EB == 1 ? 2 : 1;
+  static_assert(RS % 16 == 0, "stage rows hold 16-byte chunks");
 };
 
 template <class C>
 struct LatK {
   uint32_t k[C::NKW];
   uint32_t mask;  // bit q: token 4 lj + q of the tile valid
+  bool row_ok;    // token li of the tile valid
 };
 
-template <class C>
-struct LatV {
-  uint32_t v[4][4][C::NVW];  // [tile][row q][dword]
-  uint32_t mask[4];
-};
+// LDS transpose reads (gfx950): within each group of 16 lanes, the 8-byte
+// pieces the lanes point at form a byte (tr8) or half (tr16) matrix whose
+// rows are the pieces of lanes {2k, 2k+1} (tr8: 8 rows of 16 bytes) or
+// {4k .. 4k+3} (tr16: 4 rows of 16 halves); lane i of the group receives
+// column i -- one element of each row, in row order.
+typedef int v2i32 __attribute__((ext_vector_type(2)));
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ v2i32 lds_read_tr8(const uint8_t* p) {
+  return __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) v2i32*)p);
+}
+
+__device__ __forceinline__ half4 lds_read_tr16(const uint8_t* p) {
+  return __builtin_bit_cast(
+      half4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)p));
+}
 
 template <int CT, bool GATHER>
 __global__ void __launch_bounds__(kThreads)
@@ -757,19 +819,41 @@ latent_kernel(const SplitArgs a) {
   const int S = a.num_splits;
   const int KVH = a.kv_heads;
 
+  // ---- prologue: every independent read is issued before the first wait
+  const bool balanced = a.target_ctas > 0;
   Work wk;
-  if (!locate_work<GATHER>(a, lane, wk)) return;  // padding CTA
-  const int r = wk.r, g = wk.g, h0 = wk.h0, nh = wk.nh, len = wk.len;
+  int raw_npos = 0, raw_len = 0;
+  if (balanced) {
+    if (!locate_balanced<GATHER>(a, lane, wk)) return;  // padding CTA
+  } else {
+    static_item(a, wk);
+    raw_npos = GATHER ? uniform_load(a.num_candidates, wk.r) : uniform_load(a.seq_lens, wk.r);
+  }
+  if constexpr (GATHER) raw_len = uniform_load(a.seq_lens, wk.r);
+  unit_heads(a, wk);
+  const int r = wk.r, g = wk.g, h0 = wk.h0, nh = wk.nh;
 
   __shared__ uint4 s_q[C::NKS * 64];
-  __shared__ f32x4 s_sc[2][W][64];  // published scores, double buffered by round
+  __shared__ f32x4 s_sc[W][64];                   // published scores of the round
+  __shared__ __attribute__((aligned(16))) uint8_t s_stage[C::ROUND * C::RS];
   __shared__ float s_vs[C::VD];
   constexpr int QPT = (C::NKS * 64 + kThreads - 1) / kThreads;
   uint4 qraw[QPT];
   float4 ksc[QPT][2];
   q_issue<C::NKS, C::EB, D>(a, wk, qraw, ksc);
-  const Scales sc = load_scales<C::VD>(a, g, s_vs);
+  const Scales sc = load_scales<C::VD>(a, g);
   const int32_t* bt_row = a.block_table + (size_t)r * a.max_blocks_per_row;
+  // static mode: block ids of the first two rounds' tiles of this wave
+  int pre_blk[2] = {0, 0};
+  if (!GATHER && !balanced) {
+    const int p0s = static_p0(a, wk.split);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      pre_blk[i] = uniform_load(bt_row, min((p0s + 16 * (wave + i * W)) >> a.log2_block,
+                                            a.max_blocks_per_row - 1));
+  }
+  finish_item<GATHER>(a, wk, balanced, raw_npos, raw_len);
+  const int len = wk.len;
 
   int p0, p1;
   if (!split_range(a, wk, p0, p1)) return;
@@ -779,85 +863,47 @@ latent_kernel(const SplitArgs a) {
 
   const uint32_t tok = (uint32_t)KVH * C::KROW;  // bytes per token slot
   const uint32_t koff = (uint32_t)li * tok + (uint32_t)g * C::KROW + 16u * lj;
-  const uint32_t voff = (uint32_t)(4 * lj) * tok + (uint32_t)g * C::KROW +
-                        (uint32_t)wave * C::VQ * C::EB + (uint32_t)li * C::VSEG;
 
-  // dense rows: block of tile t as an SGPR value (false: invalid or past the end)
-  auto tile_block = [&](int t, int64_t& s0) -> bool {
-    if (t >= ntiles) return false;
-    const int tp = p0 + 16 * t;
-    const int blk = uniform_load(bt_row, tp >> a.log2_block);
-    if (blk < 0 || blk >= a.num_pool_blocks) return false;
-    s0 = ((int64_t)blk << a.log2_block) + (tp & (a.block_size - 1));
-    return true;
-  };
-  // gathered rows: slot of position p0 + 16 t + li (0 if invalid)
-  auto gather_slot = [&](int t, bool& v) -> int64_t {
-    const int pos = p0 + 16 * t + li;
-    const int c = (t < ntiles && pos < p1) ? a.candidates[(size_t)r * a.max_candidates + pos] : -1;
-    v = c >= 0 && c < len;
-    const int blk = v ? bt_row[c >> a.log2_block] : 0;
-    v = v && blk >= 0 && blk < a.num_pool_blocks;
-    return v ? ((int64_t)blk << a.log2_block) + (c & (a.block_size - 1)) : 0;
-  };
-
-  auto issue_k = [&](LatK<C>& T, int t) {
+  // pre >= 0: the tile's block id was read in the prologue (static mode)
+  auto issue_k = [&](LatK<C>& T, int t, int pre) {
     uint32_t m = 0;
     if constexpr (!GATHER) {
       int64_t s0 = 0;
-      const bool bv = tile_block(t, s0);
-      const auto rs = make_rsrc(a.key_cache + s0 * tok, bv ? 16u * tok : 0u);
+      bool bv = false;
+      if (t < ntiles) {
+        const int tp = p0 + 16 * t;
+        const int blk = (pre >= 0 && !balanced) ? pre_blk[pre] : uniform_load(bt_row, tp >> a.log2_block);
+        bv = blk >= 0 && blk < a.num_pool_blocks;
+        s0 = bv ? ((int64_t)blk << a.log2_block) + (tp & (a.block_size - 1)) : 0;
+      }
+      // the descriptor covers the tile's valid rows only: rows past the end
+      // (and a whole tile with an invalid block) read as zeros
+      const int tp = p0 + 16 * t;
+      const uint32_t nv = bv ? (uint32_t)min(16, p1 - tp) : 0u;
+      const auto rs = make_rsrc(a.key_cache + s0 * tok, nv * tok);
 #pragma unroll
       for (int s = 0; s < C::NKL; ++s) buffer_bytes<16>(rs, koff + 64 * s, 0, &T.k[4 * s]);
-      const int tp = p0 + 16 * t;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) m |= (bv && tp + 4 * lj + q < p1) ? (1u << q) : 0u;
+      for (int q = 0; q < 4; ++q) m |= (4 * lj + q < (int)nv) ? (1u << q) : 0u;
+      T.row_ok = true;
     } else {
-      bool v;
-      const int64_t sl = gather_slot(t, v);
+      // per-token slots; invalid entries (and tiles past the end) read token
+      // slot 0 of the pool and are masked
+      const int pos = p0 + 16 * t + li;
+      const int c = (t < ntiles && pos < p1) ? a.candidates[(size_t)r * a.max_candidates + pos] : -1;
+      bool v = c >= 0 && c < len;
+      const int blk = v ? bt_row[c >> a.log2_block] : 0;
+      v = v && blk >= 0 && blk < a.num_pool_blocks;
+      const int64_t sl = v ? ((int64_t)blk << a.log2_block) + (c & (a.block_size - 1)) : 0;
       const uint8_t* krow = a.key_cache + ((size_t)sl * KVH + g) * C::KROW;
 #pragma unroll
       for (int s = 0; s < C::NKL; ++s) load_bytes<16>(krow + 64 * s + 16 * lj, &T.k[4 * s]);
       const int vi = v ? 1 : 0;
 #pragma unroll
       for (int q = 0; q < 4; ++q) m |= __shfl(vi, 4 * lj + q) ? (1u << q) : 0u;
+      T.row_ok = v;
     }
     T.mask = m;
-  };
-
-  auto issue_v = [&](LatV<C>& V, int rd) {
-#pragma unroll
-    for (int j = 0; j < W; ++j) {
-      const int t = rd * W + j;
-      uint32_t m = 0;
-      if constexpr (!GATHER) {
-        int64_t s0 = 0;
-        const bool bv = tile_block(t, s0);
-        const auto rs = make_rsrc(a.key_cache + s0 * tok, bv ? 16u * tok : 0u);
-        const int tp = p0 + 16 * t;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          buffer_bytes<C::VSEG>(rs, voff, (uint32_t)q * tok, V.v[j][q]);
-          m |= (bv && tp + 4 * lj + q < p1) ? (1u << q) : 0u;
-        }
-      } else {
-        bool v;
-        const int64_t sl = gather_slot(t, v);
-        const int vi = v ? 1 : 0;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int src = 4 * lj + q;
-          const int lo = __shfl((int)(sl & 0xffffffff), src);
-          const int hi = __shfl((int)(sl >> 32), src);
-          const int64_t sq = ((int64_t)hi << 32) | (uint32_t)lo;
-          const uint8_t* vrow = a.key_cache + ((size_t)sq * KVH + g) * C::KROW +
-                                (size_t)wave * C::VQ * C::EB + li * C::VSEG;
-          load_bytes<C::VSEG>(vrow, V.v[j][q]);
-          m |= __shfl(vi, src) ? (1u << q) : 0u;
-        }
-      }
-      V.mask[j] = m;
-    }
   };
 
   f32x4 acc[C::CPL];
@@ -866,35 +912,64 @@ latent_kernel(const SplitArgs a) {
   float m_ref = kNegInf;
   float l_part = 0.0f;
 
-  // one round: scores of this wave's tile -> LDS; barrier; softmax over the
-  // round's four tiles; PV on this wave's channels
-  auto round = [&](const LatK<C>& K, const LatV<C>& V, int rd) {
+  // this lane's 16-byte K chunks of its tile row
+  uint8_t* const stage_k = s_stage + (size_t)(16 * wave + li) * C::RS + 16 * lj;
+  // the piece this lane contributes to a transposed V read (see lds_read_tr8
+  // / lds_read_tr16): one-byte codes -- row k = li / 2 of k-group lj is token
+  // 4 lj + (k & 3) of the first (k < 4) or second tile of a tile pair, bytes
+  // [8 (li & 1), +8) of a 16-channel column tile; two-byte codes -- row
+  // k = li / 4 is token 4 lj + k of a tile, halves [4 (li & 3), +4).
+  const uint8_t* stage_v;
+  if constexpr (C::EB == 1)
+    stage_v = s_stage + (size_t)(16 * ((li >> 1) >> 2) + 4 * lj + ((li >> 1) & 3)) * C::RS +
+              (size_t)wave * C::VQ + 8 * (li & 1);
+  else
+    stage_v = s_stage + (size_t)(4 * lj + (li >> 2)) * C::RS + (size_t)(wave * C::VQ + 4 * (li & 3)) * 2;
+
+  // Round rd on the K tile in T; afterwards T is free and the loads of
+  // round rd + 2 are issued into it.
+  auto round = [&](LatK<C>& T, int rd) {
+    // scores of this wave's tile
     f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < C::NKL; ++s) {
       if constexpr (C::EB == 2) {
         const half8 kop = __builtin_bit_cast(
-            half8, uint4{K.k[4 * s], K.k[4 * s + 1], K.k[4 * s + 2], K.k[4 * s + 3]});
+            half8, uint4{T.k[4 * s], T.k[4 * s + 1], T.k[4 * s + 2], T.k[4 * s + 3]});
         sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop, __builtin_bit_cast(half8, s_q[s * 64 + lane]), sacc, 0, 0, 0);
       } else {
-        const half4 c0 = codes4_to_half4<CT>(K.k[4 * s + 0]);
-        const half4 c1 = codes4_to_half4<CT>(K.k[4 * s + 1]);
-        const half4 c2 = codes4_to_half4<CT>(K.k[4 * s + 2]);
-        const half4 c3 = codes4_to_half4<CT>(K.k[4 * s + 3]);
+        const half4 c0 = codes4_to_half4<CT>(T.k[4 * s + 0]);
+        const half4 c1 = codes4_to_half4<CT>(T.k[4 * s + 1]);
+        const half4 c2 = codes4_to_half4<CT>(T.k[4 * s + 2]);
+        const half4 c3 = codes4_to_half4<CT>(T.k[4 * s + 3]);
         const half8 k0 = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
         const half8 k1 = {c2[0], c2[1], c2[2], c2[3], c3[0], c3[1], c3[2], c3[3]};
         sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(k0, __builtin_bit_cast(half8, s_q[(2 * s) * 64 + lane]), sacc, 0, 0, 0);
         sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(k1, __builtin_bit_cast(half8, s_q[(2 * s + 1) * 64 + lane]), sacc, 0, 0, 0);
       }
     }
-    f32x4 sc;
+    f32x4 scw;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) sc[q] = ((K.mask >> q) & 1u) ? sacc[q] * a.score_scale : kNegInf;
-    s_sc[rd & 1][wave][lane] = sc;
+    for (int q = 0; q < 4; ++q) scw[q] = ((T.mask >> q) & 1u) ? sacc[q] * a.score_scale : kNegInf;
+    s_sc[wave][lane] = scw;
+    // every wave is past the previous round's V reads and has published its
+    // scores (one score buffer suffices: a wave reads the scores of round rd
+    // before the second barrier of round rd, and they are next written after
+    // it)
     __syncthreads();
+    // invalid rows are stored as zeros, so the V operands need no mask
+    // (dense rows: already zero from the buffer descriptor)
+    const uint32_t keep = (GATHER && !T.row_ok) ? 0u : 0xffffffffu;
+#pragma unroll
+    for (int s = 0; s < C::NKL; ++s)
+      *reinterpret_cast<uint4*>(stage_k + 64 * s) =
+          uint4{T.k[4 * s] & keep, T.k[4 * s + 1] & keep, T.k[4 * s + 2] & keep, T.k[4 * s + 3] & keep};
+    issue_k(T, (rd + 2) * W + wave, -1);
+    __builtin_amdgcn_sched_barrier(0);
+
     f32x4 st[W];
 #pragma unroll
-    for (int j = 0; j < W; ++j) st[j] = s_sc[rd & 1][j][lane];
+    for (int j = 0; j < W; ++j) st[j] = s_sc[j][lane];
     float mt = kNegInf;
 #pragma unroll
     for (int j = 0; j < W; ++j)
@@ -910,57 +985,55 @@ latent_kernel(const SplitArgs a) {
       m_ref = mn;
     }
     const float mu = (m_ref == kNegInf) ? 0.0f : m_ref;
+    half4 pop[W];
 #pragma unroll
     for (int j = 0; j < W; ++j) {
       float p[4];
 #pragma unroll
       for (int q = 0; q < 4; ++q) p[q] = __builtin_amdgcn_exp2f((st[j][q] - mu) * kLog2e);
       l_part += (p[0] + p[1]) + (p[2] + p[3]);
-      const half4 pop = {(half_t)p[0], (half_t)p[1], (half_t)p[2], (half_t)p[3]};
-      uint32_t vz[4];
+      pop[j] = half4{(half_t)p[0], (half_t)p[1], (half_t)p[2], (half_t)p[3]};
+    }
+    // the stage holds all 64 rows of the round
+    __syncthreads();
+    if constexpr (C::EB == 1) {
+      // O^T += V^T P^T over tile pairs with 16x16x32 MFMAs: k index 8 lj + e
+      // is token 4 lj + (e & 3) of tile 2 m + (e >> 2), in both operands
 #pragma unroll
-      for (int q = 0; q < 4; ++q) vz[q] = ((V.mask[j] >> q) & 1u) ? 0xffffffffu : 0u;
-      if constexpr (C::EB == 2) {
+      for (int m = 0; m < W / 2; ++m) {
+        const half8 pb = {pop[2 * m][0], pop[2 * m][1], pop[2 * m][2], pop[2 * m][3],
+                          pop[2 * m + 1][0], pop[2 * m + 1][1], pop[2 * m + 1][2], pop[2 * m + 1][3]};
 #pragma unroll
-        for (int x = 0; x < C::NVW; ++x) {
-          const uint32_t r0 = V.v[j][0][x] & vz[0], r1 = V.v[j][1][x] & vz[1];
-          const uint32_t r2 = V.v[j][2][x] & vz[2], r3 = V.v[j][3][x] & vz[3];
-          const half4 va = __builtin_bit_cast(half4, uint2{perm(r1, r0, 0x05040100u), perm(r3, r2, 0x05040100u)});
-          const half4 vb = __builtin_bit_cast(half4, uint2{perm(r1, r0, 0x07060302u), perm(r3, r2, 0x07060302u)});
-          acc[2 * x] = __builtin_amdgcn_mfma_f32_16x16x16f16(va, pop, acc[2 * x], 0, 0, 0);
-          acc[2 * x + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(vb, pop, acc[2 * x + 1], 0, 0, 0);
+        for (int ct = 0; ct < C::CPL; ++ct) {
+          const v2i32 raw = lds_read_tr8(stage_v + (size_t)(32 * m) * C::RS + 16 * ct);
+          const half4 lo = codes4_to_half4<CT>((uint32_t)raw.x);
+          const half4 hi = codes4_to_half4<CT>((uint32_t)raw.y);
+          const half8 va = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pb, acc[ct], 0, 0, 0);
         }
-      } else {
+      }
+    } else {
 #pragma unroll
-        for (int x = 0; x < C::NVW; ++x) {
-          const uint32_t r0 = V.v[j][0][x] & vz[0], r1 = V.v[j][1][x] & vz[1];
-          const uint32_t r2 = V.v[j][2][x] & vz[2], r3 = V.v[j][3][x] & vz[3];
-          const uint32_t t0 = perm(r1, r0, 0x05010400u), t1 = perm(r1, r0, 0x07030602u);
-          const uint32_t t2 = perm(r3, r2, 0x05010400u), t3 = perm(r3, r2, 0x07030602u);
-          acc[4 * x + 0] = __builtin_amdgcn_mfma_f32_16x16x16f16(codes4_to_half4<CT>(perm(t2, t0, 0x05040100u)), pop, acc[4 * x + 0], 0, 0, 0);
-          acc[4 * x + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(codes4_to_half4<CT>(perm(t2, t0, 0x07060302u)), pop, acc[4 * x + 1], 0, 0, 0);
-          acc[4 * x + 2] = __builtin_amdgcn_mfma_f32_16x16x16f16(codes4_to_half4<CT>(perm(t3, t1, 0x05040100u)), pop, acc[4 * x + 2], 0, 0, 0);
-          acc[4 * x + 3] = __builtin_amdgcn_mfma_f32_16x16x16f16(codes4_to_half4<CT>(perm(t3, t1, 0x07060302u)), pop, acc[4 * x + 3], 0, 0, 0);
+      for (int j = 0; j < W; ++j) {
+#pragma unroll
+        for (int ct = 0; ct < C::CPL; ++ct) {
+          const half4 va = lds_read_tr16(stage_v + (size_t)(16 * j) * C::RS + 32 * ct);
+          acc[ct] = __builtin_amdgcn_mfma_f32_16x16x16f16(va, pop[j], acc[ct], 0, 0, 0);
         }
       }
     }
   };
 
   LatK<C> ka, kb;
-  LatV<C> vbuf;
-  issue_k(ka, wave);
+  issue_k(ka, wave, 0);
+  issue_k(kb, W + wave, 1);
   q_stage<C::NKS, C::EB, D>(qraw, ksc, sc.k_tensor, s_q);
+  stage_scales<C::VD>(a, sc, s_vs);
   __syncthreads();
   for (int rd = 0; rd < nrounds; rd += 2) {
-    issue_v(vbuf, rd);
-    issue_k(kb, (rd + 1) * W + wave);
-    __builtin_amdgcn_sched_barrier(0);
-    round(ka, vbuf, rd);
+    round(ka, rd);
     if (rd + 1 >= nrounds) break;
-    issue_v(vbuf, rd + 1);
-    issue_k(ka, (rd + 2) * W + wave);
-    __builtin_amdgcn_sched_barrier(0);
-    round(kb, vbuf, rd + 1);
+    round(kb, rd + 1);
   }
 
   // every wave holds the same running maximum and sum; sum the lane groups
@@ -971,18 +1044,15 @@ latent_kernel(const SplitArgs a) {
     const size_t pidx = ((size_t)r * a.heads + h) * S + split;
     if (wave == 0 && lj == 0) reinterpret_cast<float2*>(a.ws_ml)[pidx] = make_float2(m_ref, l_part);
     float* dst = a.ws_acc + pidx * C::VD;
+    // column tile ct holds channels 16 ct + 4 lj + q of this wave's range
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int cbase = wave * C::VQ + (4 * lj + q) * C::CPL;
+    for (int ct = 0; ct < C::CPL; ++ct) {
+      const int cbase = wave * C::VQ + 16 * ct + 4 * lj;
+      float4 o;
+      float* op = reinterpret_cast<float*>(&o);
 #pragma unroll
-      for (int ct = 0; ct < C::CPL; ct += 4) {
-        float4 o;
-        float* op = reinterpret_cast<float*>(&o);
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          op[e] = (acc[ct + e][q] * a.v_mult) * v_scale_of(a, sc, s_vs, cbase + ct + e);
-        *reinterpret_cast<float4*>(dst + cbase + ct) = o;
-      }
+      for (int q = 0; q < 4; ++q) op[q] = (acc[ct][q] * a.v_mult) * v_scale_of(a, sc, s_vs, cbase + q);
+      *reinterpret_cast<float4*>(dst + cbase) = o;
     }
   }
 }
