@@ -177,9 +177,13 @@ typedef struct {
  * empty partial.  In the live-balanced
  * mode the automatic S allows rows up to four times the mean work:
  *   S = min(ceil(4 * target / units), ceil(cap / min_chunk), max_splits).
- * Defaults: min_chunk 64, max_splits 64; waves 2 in the live-balanced mode
- * when a split's partial (group * (v_head_size + 2) * 4 bytes) is less than
- * half the KV bytes of min_chunk positions, else 1.
+ * Defaults: max_splits 64.  min_chunk: 64, raised to the smallest power of
+ * two c for which a split's partial P = group * (v_head_size + 2) * 4 bytes
+ * is at most a quarter of the KV bytes of c positions -- unless the grid
+ * would then hold fewer than a quarter of the resident CTAs
+ * (units * ceil(cap / c) * 4 < resident), a latency-bound step that gains
+ * from more, shorter splits.  waves: 2 in the live-balanced mode when 2 P is
+ * less than the KV bytes of min_chunk positions, else 1.
  * Returns PKV_EINVAL / PKV_EUNSUPPORTED as paged_decode_attention would, or
  * PKV_EHIP if the device query fails.  Does not touch device memory.
  */

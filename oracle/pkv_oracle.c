@@ -29,8 +29,9 @@
  *   - ONNX Runtime PR #33707 (DynamicSparseAttention INT8 KV cache),
  *     "Summary of Changes" section 1 (key scale folded into the query, value
  *     scale applied after accumulation, natural-log softmax) and its test
- *     description: an FP64 reference "from the inputs as the kernel receives
- *     them" with max-subtracted weights; section 2 (split-K partials of
+ *     description: an FP64 reference evaluated on exactly the inputs the
+ *     kernel gets, with weights taken relative to the maximum score;
+ *     section 2 (split-K partials of
  *     running maximum, running sum and accumulator, merged afterwards;
  *     selected candidate lists with invalid entries).
  *   - ONNX Runtime PR #29912 (PagedAttention), "Summary of Changes": the

@@ -316,8 +316,7 @@ pkv_status split_geometry(const pkv_problem* problem, const pkv_geometry_opts* o
       o.max_splits < 0 || o.waves < 0)
     return fail(PKV_EINVAL, "geometry options must be >= 0");
   const bool gathered = p.max_candidates > 0;
-  const int min_chunk = o.min_chunk ? o.min_chunk : 64;
-  if (min_chunk % 16) return fail(PKV_EINVAL, "min_chunk must be a multiple of 16");
+  if (o.min_chunk % 16) return fail(PKV_EINVAL, "min_chunk must be a multiple of 16");
   const int max_splits = o.max_splits ? o.max_splits : pkv::kMaxSplits;
   if (max_splits > pkv::kMaxSplits)
     return fail(PKV_EINVAL, "max_splits %d exceeds %d", max_splits, pkv::kMaxSplits);
@@ -350,6 +349,19 @@ pkv_status split_geometry(const pkv_problem* problem, const pkv_geometry_opts* o
   const int64_t row_bytes = (int64_t)(p.layout == PKV_LATENT ? p.head_size
                                                              : p.head_size + p.v_head_size) *
                             (p.cache_dtype == PKV_F16 ? 2 : 1);
+  // Automatic chunk floor: 64 positions, raised to the power of two that
+  // keeps a split's partial at most a quarter of the KV bytes it covers --
+  // unless the grid would then hold fewer than a quarter of the resident
+  // CTAs (a small step is bound by latency, and more, shorter splits finish
+  // sooner).
+  int min_chunk = o.min_chunk;
+  if (min_chunk == 0) {
+    min_chunk = 64;
+    int64_t by_partial = 16;
+    while (by_partial < ceil_div(4 * partial_bytes, row_bytes)) by_partial *= 2;
+    if (by_partial > min_chunk && units * ceil_div(cap, by_partial) * 4 >= (int64_t)cus * occ)
+      min_chunk = (int)std::min<int64_t>(by_partial, 1 << 20);
+  }
   const bool cheap_partials = 2 * partial_bytes < row_bytes * min_chunk;
   const int waves = waves_req ? waves_req : (balanced && cheap_partials ? 2 : 1);
   const int64_t target = (int64_t)waves * cus * occ;
@@ -362,7 +374,7 @@ pkv_status split_geometry(const pkv_problem* problem, const pkv_geometry_opts* o
       // all tiles of all units fit the target number of CTAs.
       const int64_t tiles = (cap + 63) / 64;
       int64_t tps = 1;
-      while (ceil_div(tiles, tps) * units > target && tps < tiles) tps *= 2;
+      while ((ceil_div(tiles, tps) * units > target || 64 * tps < min_chunk) && tps < tiles) tps *= 2;
       S = ceil_div(tiles, tps);
     } else {
       // live-balanced chunks: leave room for rows up to 4x the mean work

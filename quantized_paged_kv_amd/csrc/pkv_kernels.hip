@@ -1105,25 +1105,27 @@ combine_kernel(const CombineArgs a) {
     }
   }
 
-  // Static decomposition: issue every partial load before the weights are
-  // known (a short row's empty splits are read and ignored).  Live-balanced
-  // decomposition: most of the S slots of a row can be empty, so read only
-  // the splits with a nonzero weight.
+  // Partial loads are issued before the weights are known (an empty split's
+  // accumulator is read and ignored) -- for every split in the static
+  // decomposition, and for the first kSpecSplits in the live-balanced one,
+  // where most of the S slots of a short row can be empty; there the later
+  // slots are read only when their weight is nonzero.
+  constexpr int kSpecSplits = 16;
+  const int spec = a.skip_empty ? min(S, kSpecSplits) : S;
   const float* base = a.ws_acc + (size_t)pair * S * VD + cg * 4;
   float4 v[MAXI];
-  if (!a.skip_empty) {
 #pragma unroll
-    for (int i = 0; i < MAXI; ++i) {
-      const int k = ks + i * KS;
-      if (k < S) v[i] = *reinterpret_cast<const float4*>(base + (size_t)k * VD);
-    }
+  for (int i = 0; i < MAXI; ++i) {
+    const int k = ks + i * KS;
+    if (k < spec) v[i] = *reinterpret_cast<const float4*>(base + (size_t)k * VD);
   }
   __syncthreads();
-  if (a.skip_empty) {
+  if (spec < S) {
 #pragma unroll
     for (int i = 0; i < MAXI; ++i) {
       const int k = ks + i * KS;
-      if (k < S && s_w[k] != 0.0f) v[i] = *reinterpret_cast<const float4*>(base + (size_t)k * VD);
+      if (k >= spec && k < S && s_w[k] != 0.0f)
+        v[i] = *reinterpret_cast<const float4*>(base + (size_t)k * VD);
     }
   }
   float4 o = make_float4(0.f, 0.f, 0.f, 0.f);

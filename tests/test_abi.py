@@ -195,3 +195,27 @@ def test_gathered_and_scale_requirements():
     with pytest.raises(pkv.PkvError) as e:
         _call(p, g, _args(k_scale=A, value_cache=None, v_scale=A + 64), g.workspace_bytes)
     assert e.value.status == 1
+
+
+def test_automatic_chunk_floor_bounds_partial_traffic():
+    # latent rows (16 heads x 512 FP32 partials per split vs 576 B per token):
+    # the floor is the power of two keeping partials <= a quarter of the KV bytes
+    lat = pkv.make_problem(32, 16, 1, 576, 512, 64, 64, 2048, cache_dtype="fp8",
+                           k_quant="tensor", v_quant="tensor", layout="latent")
+    g = pkv.split_geometry(lat, num_cus=256, ctas_per_cu=2)
+    partial = 16 * (512 + 2) * 4
+    assert g.min_chunk == 256 and 4 * partial <= 576 * g.min_chunk < 8 * partial
+    assert g.num_splits == 4096 // 256
+    # gathered INT8 rows, group 12, head 256: two 64-candidate tiles per split
+    dsa = pkv.make_problem(8, 24, 2, 256, 256, 16, 2048, 2048, max_candidates=2048,
+                           cache_dtype="i8", k_quant="channel", v_quant="channel")
+    g = pkv.split_geometry(dsa, num_cus=256, ctas_per_cu=2)
+    assert g.min_chunk == 128 and g.num_splits == 16
+    # one row: the grid would fall below a quarter wave, keep the 64 floor
+    one = pkv.make_problem(1, 24, 2, 256, 256, 16, 256, 256, cache_dtype="i8",
+                           k_quant="tensor", v_quant="tensor")
+    g = pkv.split_geometry(one, num_cus=256, ctas_per_cu=2)
+    assert g.min_chunk == 64 and g.num_splits == 64
+    # an explicit floor is kept as given
+    g = pkv.split_geometry(lat, num_cus=256, ctas_per_cu=2, min_chunk=64)
+    assert g.min_chunk == 64
