@@ -329,6 +329,45 @@ __device__ __forceinline__ int static_p0(const SplitArgs& a, int split) {
   return split * a.static_chunk;
 }
 
+// s_waitcnt immediate (gfx9 encoding): vmcnt(0), expcnt and lgkmcnt not waited.
+constexpr int kWaitVmcnt0 = 0x0F70;
+
+// First position of the work item's range (the p0 split_range computes);
+// known before any row length is read in the static mode.
+__device__ __forceinline__ int split_p0(const SplitArgs& a, const Work& w) {
+  if (a.target_ctas > 0)
+    return w.n_row > 0 ? w.split * (((w.npos + w.n_row - 1) / w.n_row + 15) & ~15) : 0;
+  return static_p0(a, w.split);
+}
+
+// Block ids of one wave's tiles (dense rows).  The wave takes tiles
+// wave + W k; lane k of one VGPR holds the block of the wave's tile
+// 64 win + k, read with one vector load per 64 tiles and picked per tile
+// with readlane, so the tile loop has no dependent memory read (a scalar
+// load that misses would wait behind the streaming K/V traffic).
+struct WaveBlocks {
+  const int32_t* bt_row;
+  int p0, wave, win, ids;
+
+  __device__ __forceinline__ void load(const SplitArgs& a, int w_idx, int lane) {
+    win = w_idx;
+    const int t = wave + kWaves * (64 * w_idx + lane);
+    const int bi = min(max((p0 + 16 * t) >> a.log2_block, 0), a.max_blocks_per_row - 1);
+    ids = bt_row[bi];
+  }
+  // block id of the wave's tile t (t = wave + W k)
+  __device__ __forceinline__ int of(const SplitArgs& a, int t, int lane) {
+    const int k = (t - wave) / kWaves;
+    if ((k >> 6) != win) {
+      load(a, k >> 6, lane);
+      // wait here, in the rare refill, so that `ids` is never a pending load
+      // where this path joins the common one (which must not wait at all)
+      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    }
+    return __builtin_amdgcn_readlane(ids, k & 63);
+  }
+};
+
 __device__ __forceinline__ bool split_range(const SplitArgs& a, const Work& w, int& p0, int& p1) {
   const int S = a.num_splits;
   int chunk;
@@ -476,19 +515,12 @@ split_kernel(const SplitArgs a) {
   constexpr int QPT = (C::NKS * 64 + kThreads - 1) / kThreads;  // entries per thread
   uint4 qraw[QPT];
   float4 ksc[QPT][2];
+  const int32_t* bt_row = a.block_table + (size_t)r * a.max_blocks_per_row;
+  // block ids of this wave's first 64 tiles (static mode: before the length)
+  WaveBlocks wb{bt_row, split_p0(a, wk), wave, 0, 0};
+  if constexpr (!GATHER) wb.load(a, 0, lane);
   q_issue<C::NKS, C::EB, D>(a, wk, qraw, ksc);
   const Scales sc = load_scales<VD>(a, g);
-  const int32_t* bt_row = a.block_table + (size_t)r * a.max_blocks_per_row;
-  // static mode: the first tiles' block ids do not depend on the live length
-  int pre_blk[NST - 1];
-  if constexpr (!GATHER) {
-    const int p0s = static_p0(a, wk.split);
-#pragma unroll
-    for (int i = 0; i < NST - 1; ++i) {
-      const int bi = min((p0s + 16 * (wave + i * W)) >> a.log2_block, a.max_blocks_per_row - 1);
-      pre_blk[i] = balanced ? 0 : uniform_load(bt_row, bi);
-    }
-  }
   finish_item<GATHER>(a, wk, balanced, raw_npos, raw_len);
   const int len = wk.len;
 
@@ -509,8 +541,7 @@ split_kernel(const SplitArgs a) {
   // Issue the loads of tile t into T.  Tiles at or past ntiles issue loads
   // that read nothing (dense rows: an empty buffer descriptor) so every
   // iteration issues the same instruction stream.
-  // pre >= 0: the block id was read in the prologue (pre_blk[pre]).
-  auto issue = [&](Tile<C>& T, int t, int pre) {
+  auto issue = [&](Tile<C>& T, int t) {
     const int tp = p0 + 16 * t;  // first position of the tile
     uint32_t vm = 0;
     if constexpr (!GATHER) {
@@ -518,7 +549,7 @@ split_kernel(const SplitArgs a) {
       bool bv = false;
       if (t < ntiles) {
         // the address is wave-uniform; keep the block id in an SGPR
-        blk = (pre >= 0 && a.target_ctas == 0) ? pre_blk[pre] : uniform_load(bt_row, tp >> a.log2_block);
+        blk = wb.of(a, t, lane);
         bv = blk >= 0 && blk < a.num_pool_blocks;
       }
       const int64_t s0 = bv ? ((int64_t)blk << a.log2_block) + (tp & (a.block_size - 1)) : 0;
@@ -657,7 +688,7 @@ split_kernel(const SplitArgs a) {
   // tiles in flight while one is consumed -----------------------------------
   Tile<C> buf[NST];
 #pragma unroll
-  for (int i = 0; i < NST - 1; ++i) issue(buf[i], wave + i * W, i);
+  for (int i = 0; i < NST - 1; ++i) issue(buf[i], wave + i * W);
 
   // Q' into LDS (its loads were issued before the tile loads above)
   q_stage<C::NKS, C::EB, D>(qraw, ksc, sc.k_tensor, s_q);
@@ -669,7 +700,7 @@ split_kernel(const SplitArgs a) {
     for (int st = 0; st < NST; ++st) {
       const int tt = t + st * W;
       if (tt >= ntiles) break;
-      issue(buf[(st + NST - 1) % NST], tt + (NST - 1) * W, -1);
+      issue(buf[(st + NST - 1) % NST], tt + (NST - 1) * W);
       // keep the loads ahead of the wait for this tile's data
       __builtin_amdgcn_sched_barrier(0);
       consume(buf[st]);
@@ -681,68 +712,69 @@ split_kernel(const SplitArgs a) {
   l_part += __shfl_xor(l_part, 16);
   l_part += __shfl_xor(l_part, 32);
 
+  // Flat merge: every wave writes its rescaled accumulator to LDS, and after
+  // one barrier every thread sums the four wave slices (fixed order) for a
+  // strided set of float4 channel groups of one head and writes them -- the
+  // partial store is spread over the whole CTA and fully coalesced.
   __shared__ float sm_m[W][16];
   __shared__ float sm_l[W][16];
-  constexpr int NACC = C::NCT * 4;                 // accumulator floats per lane
-  __shared__ float sm_acc[(W / 2) * NACC * 64];    // [slot][element][lane]
+  constexpr int HS = VD + 4;  // padded head stride (floats): conflict-free float4 writes
+  __shared__ __attribute__((aligned(16))) float sm_acc[W * 16 * HS];
 
   if (lane < 16) {
     sm_m[wave][lane] = m_ref;
     sm_l[wave][lane] = l_part;
   }
   __syncthreads();
-  float M = kNegInf;
-#pragma unroll
-  for (int w = 0; w < W; ++w) M = fmaxf(M, sm_m[w][li]);
-  float L = 0.0f;
-#pragma unroll
-  for (int w = 0; w < W; ++w) {
-    const float mw = sm_m[w][li];
-    const float f = (mw == kNegInf) ? 0.0f : __builtin_amdgcn_exp2f((mw - M) * kLog2e);
-    L += f * sm_l[w][li];
-  }
   {
+    float M = kNegInf;
+#pragma unroll
+    for (int w = 0; w < W; ++w) M = fmaxf(M, sm_m[w][li]);
     const float f = (m_ref == kNegInf) ? 0.0f : __builtin_amdgcn_exp2f((m_ref - M) * kLog2e);
+    // lane holds channels (4 lj + q) * CPL + ct of head li
+    float* dst = sm_acc + (size_t)(wave * 16 + li) * HS;
 #pragma unroll
-    for (int ct = 0; ct < C::NCT; ++ct) acc[ct] *= f;
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int ct = 0; ct < C::NCT; ct += 4)
+        *reinterpret_cast<float4*>(dst + (4 * lj + q) * C::CPL + ct) =
+            make_float4(acc[ct][q] * f, acc[ct + 1][q] * f, acc[ct + 2][q] * f, acc[ct + 3][q] * f);
   }
+  __syncthreads();
+  {
+    const int hh = threadIdx.x >> 4;  // head of the CTA's block
+    const int cc = threadIdx.x & 15;  // float4 groups cc, cc + 16, ...
+    if (hh < nh) {
+      float M = kNegInf;
 #pragma unroll
-  for (int half = W / 2; half >= 1; half >>= 1) {
-    if (wave >= half && wave < 2 * half) {
-      float* dst = sm_acc + (size_t)(wave - half) * NACC * 64;
+      for (int w = 0; w < W; ++w) M = fmaxf(M, sm_m[w][hh]);
+      float L = 0.0f;
 #pragma unroll
-      for (int ct = 0; ct < C::NCT; ++ct)
+      for (int w = 0; w < W; ++w) {
+        const float mw = sm_m[w][hh];
+        L += ((mw == kNegInf) ? 0.0f : __builtin_amdgcn_exp2f((mw - M) * kLog2e)) * sm_l[w][hh];
+      }
+      const size_t pidx = ((size_t)r * a.heads + h0 + hh) * S + split;
+      if (cc == 0) reinterpret_cast<float2*>(a.ws_ml)[pidx] = make_float2(M, L);
+      float* dst = a.ws_acc + pidx * VD;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) dst[(ct * 4 + q) * 64 + lane] = acc[ct][q];
-    }
-    __syncthreads();
-    if (wave < half) {
-      const float* src = sm_acc + (size_t)wave * NACC * 64;
+      for (int j = 0; j < VD / 64; ++j) {
+        const int c = 4 * (cc + 16 * j);
+        float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-      for (int ct = 0; ct < C::NCT; ++ct)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) acc[ct][q] += src[(ct * 4 + q) * 64 + lane];
-    }
-    __syncthreads();
-  }
-
-  if (wave == 0 && li < nh) {
-    const int h = h0 + li;
-    const size_t pidx = ((size_t)r * a.heads + h) * S + split;
-    if (lj == 0) reinterpret_cast<float2*>(a.ws_ml)[pidx] = make_float2(M, L);
-    // lane holds channels (4 lj + q) * CPL + ct; write them with the value
-    // scale applied once.
-    float* dst = a.ws_acc + pidx * VD;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int cbase = (4 * lj + q) * C::CPL;
-#pragma unroll
-      for (int ct = 0; ct < C::NCT; ct += 4) {
-        float4 o;
-        float* op = reinterpret_cast<float*>(&o);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) op[e] = (acc[ct + e][q] * a.v_mult) * v_scale_of(a, sc, s_vs, cbase + ct + e);
-        *reinterpret_cast<float4*>(dst + cbase + ct) = o;
+        for (int w = 0; w < W; ++w) {
+          const float4 v = *reinterpret_cast<const float4*>(sm_acc + (size_t)(w * 16 + hh) * HS + c);
+          o.x += v.x;
+          o.y += v.y;
+          o.z += v.z;
+          o.w += v.w;
+        }
+        // value scale applied once, after accumulation
+        o.x *= a.v_mult * v_scale_of(a, sc, s_vs, c);
+        o.y *= a.v_mult * v_scale_of(a, sc, s_vs, c + 1);
+        o.z *= a.v_mult * v_scale_of(a, sc, s_vs, c + 2);
+        o.w *= a.v_mult * v_scale_of(a, sc, s_vs, c + 3);
+        *reinterpret_cast<float4*>(dst + c) = o;
       }
     }
   }
@@ -840,18 +872,12 @@ latent_kernel(const SplitArgs a) {
   constexpr int QPT = (C::NKS * 64 + kThreads - 1) / kThreads;
   uint4 qraw[QPT];
   float4 ksc[QPT][2];
+  const int32_t* bt_row = a.block_table + (size_t)r * a.max_blocks_per_row;
+  // block ids of this wave's first 64 tiles (static mode: before the length)
+  WaveBlocks wb{bt_row, split_p0(a, wk), wave, 0, 0};
+  if constexpr (!GATHER) wb.load(a, 0, lane);
   q_issue<C::NKS, C::EB, D>(a, wk, qraw, ksc);
   const Scales sc = load_scales<C::VD>(a, g);
-  const int32_t* bt_row = a.block_table + (size_t)r * a.max_blocks_per_row;
-  // static mode: block ids of the first two rounds' tiles of this wave
-  int pre_blk[2] = {0, 0};
-  if (!GATHER && !balanced) {
-    const int p0s = static_p0(a, wk.split);
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-      pre_blk[i] = uniform_load(bt_row, min((p0s + 16 * (wave + i * W)) >> a.log2_block,
-                                            a.max_blocks_per_row - 1));
-  }
   finish_item<GATHER>(a, wk, balanced, raw_npos, raw_len);
   const int len = wk.len;
 
@@ -864,15 +890,14 @@ latent_kernel(const SplitArgs a) {
   const uint32_t tok = (uint32_t)KVH * C::KROW;  // bytes per token slot
   const uint32_t koff = (uint32_t)li * tok + (uint32_t)g * C::KROW + 16u * lj;
 
-  // pre >= 0: the tile's block id was read in the prologue (static mode)
-  auto issue_k = [&](LatK<C>& T, int t, int pre) {
+  auto issue_k = [&](LatK<C>& T, int t) {
     uint32_t m = 0;
     if constexpr (!GATHER) {
       int64_t s0 = 0;
       bool bv = false;
       if (t < ntiles) {
         const int tp = p0 + 16 * t;
-        const int blk = (pre >= 0 && !balanced) ? pre_blk[pre] : uniform_load(bt_row, tp >> a.log2_block);
+        const int blk = wb.of(a, t, lane);
         bv = blk >= 0 && blk < a.num_pool_blocks;
         s0 = bv ? ((int64_t)blk << a.log2_block) + (tp & (a.block_size - 1)) : 0;
       }
@@ -964,7 +989,7 @@ latent_kernel(const SplitArgs a) {
     for (int s = 0; s < C::NKL; ++s)
       *reinterpret_cast<uint4*>(stage_k + 64 * s) =
           uint4{T.k[4 * s] & keep, T.k[4 * s + 1] & keep, T.k[4 * s + 2] & keep, T.k[4 * s + 3] & keep};
-    issue_k(T, (rd + 2) * W + wave, -1);
+    issue_k(T, (rd + 2) * W + wave);
     __builtin_amdgcn_sched_barrier(0);
 
     f32x4 st[W];
@@ -1025,8 +1050,8 @@ latent_kernel(const SplitArgs a) {
   };
 
   LatK<C> ka, kb;
-  issue_k(ka, wave, 0);
-  issue_k(kb, W + wave, 1);
+  issue_k(ka, wave);
+  issue_k(kb, W + wave);
   q_stage<C::NKS, C::EB, D>(qraw, ksc, sc.k_tensor, s_q);
   stage_scales<C::VD>(a, sc, s_vs);
   __syncthreads();
