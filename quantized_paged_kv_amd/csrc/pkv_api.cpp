@@ -150,7 +150,7 @@ pkv_status check_geometry(const pkv_problem& p, const pkv_geometry* g) {
     return fail(PKV_EINVAL, "geometry num_splits %d outside [1, %d]", g->num_splits, pkv::kMaxSplits);
   if (g->min_chunk < 16 || g->min_chunk % 16)
     return fail(PKV_EINVAL, "geometry min_chunk %d is not a positive multiple of 16", g->min_chunk);
-  if (g->head_blocks != ceil_div(group, 16) || g->threads != pkv::kThreads ||
+  if (g->head_blocks != ceil_div(group, 16) || g->threads != pkv::threads_of(variant_of(p)) ||
       g->grid_x != grid_ctas_for(p, g->num_splits, g->target_ctas) || g->grid_y != 1 ||
       g->grid_z != 1 || g->workspace_bytes != workspace_bytes_for(p, g->num_splits) ||
       g->target_ctas < 0 || (g->target_ctas > 0 && p.num_rows > kMaxBalancedRows))
@@ -387,7 +387,7 @@ pkv_status split_geometry(const pkv_problem* problem, const pkv_geometry_opts* o
 
   out->num_splits = S;
   out->min_chunk = min_chunk;
-  out->threads = pkv::kThreads;
+  out->threads = pkv::threads_of(variant_of(p));
   out->head_blocks = head_blocks;
   out->target_ctas = balanced ? (int32_t)std::min<int64_t>(target, INT32_MAX) : 0;
   const int64_t grid = grid_ctas_for(p, S, out->target_ctas);

@@ -54,6 +54,12 @@ struct Variant {
 
 constexpr int kWaves = 4;          // waves per split-kernel CTA
 constexpr int kThreads = 64 * kWaves;
+// latent kernel with one-byte codes: 8 waves per CTA (one CTA per CU, two
+// waves per SIMD); with FP16 codes its LDS stage only fits 4 waves
+constexpr int kLatentWaves = 4;
+inline int threads_of(const Variant& v) {
+  return (v.latent && v.cache_dtype != PKV_F16) ? 64 * kLatentWaves : kThreads;
+}
 constexpr int kMaxSplits = 64;     // the combine holds one split per lane
 constexpr int kMaxBalancedRows = 1024;  // live-balanced chunks up to this many rows
 

@@ -347,17 +347,17 @@ __device__ __forceinline__ int split_p0(const SplitArgs& a, const Work& w) {
 // load that misses would wait behind the streaming K/V traffic).
 struct WaveBlocks {
   const int32_t* bt_row;
-  int p0, wave, win, ids;
+  int p0, wave, nw, win, ids;  // nw: waves of the CTA
 
   __device__ __forceinline__ void load(const SplitArgs& a, int w_idx, int lane) {
     win = w_idx;
-    const int t = wave + kWaves * (64 * w_idx + lane);
+    const int t = wave + nw * (64 * w_idx + lane);
     const int bi = min(max((p0 + 16 * t) >> a.log2_block, 0), a.max_blocks_per_row - 1);
     ids = bt_row[bi];
   }
   // block id of the wave's tile t (t = wave + W k)
   __device__ __forceinline__ int of(const SplitArgs& a, int t, int lane) {
-    const int k = (t - wave) / kWaves;
+    const int k = (t - wave) / nw;
     if ((k >> 6) != win) {
       load(a, k >> 6, lane);
       // wait here, in the rare refill, so that `ids` is never a pending load
@@ -368,6 +368,7 @@ struct WaveBlocks {
   }
 };
 
+template <int NT = kThreads>
 __device__ __forceinline__ bool split_range(const SplitArgs& a, const Work& w, int& p0, int& p1) {
   const int S = a.num_splits;
   int chunk;
@@ -384,7 +385,7 @@ __device__ __forceinline__ bool split_range(const SplitArgs& a, const Work& w, i
   if (a.target_ctas > 0 && w.split == w.n_row - 1) {
     // the row's last split also publishes the splits n_row .. S-1, which have
     // no CTA in this mode
-    for (int e = threadIdx.x; e < w.nh * (S - w.n_row); e += kThreads)
+    for (int e = threadIdx.x; e < w.nh * (S - w.n_row); e += NT)
       ml[(pair0 + e % w.nh) * S + w.n_row + e / w.nh] = make_float2(kNegInf, 0.0f);
   }
   if (p0 >= w.npos || (a.target_ctas > 0 && w.split >= w.n_row)) {
@@ -404,12 +405,12 @@ __device__ __forceinline__ int q_channel(int ks, int lj) {
   else return 64 * (ks >> 1) + 16 * lj + 8 * (ks & 1);
 }
 
-template <int NKS, int EB, int D, int QPT>
+template <int NKS, int EB, int D, int QPT, int NT = kThreads>
 __device__ __forceinline__ void q_issue(const SplitArgs& a, const Work& w, uint4 (&qraw)[QPT],
                                         float4 (&ksc)[QPT][2]) {
 #pragma unroll
   for (int i = 0; i < QPT; ++i) {
-    const int e = threadIdx.x + i * kThreads;
+    const int e = threadIdx.x + i * NT;
     qraw[i] = uint4{0u, 0u, 0u, 0u};
     ksc[i][0] = ksc[i][1] = make_float4(1.f, 1.f, 1.f, 1.f);
     if (e < NKS * 64) {
@@ -427,12 +428,12 @@ __device__ __forceinline__ void q_issue(const SplitArgs& a, const Work& w, uint4
 }
 
 // ks_tensor: the per-tensor key scale (1 when not per tensor).
-template <int NKS, int EB, int D, int QPT>
+template <int NKS, int EB, int D, int QPT, int NT = kThreads>
 __device__ __forceinline__ void q_stage(const uint4 (&qraw)[QPT], const float4 (&ksc)[QPT][2],
                                         float ks_tensor, uint4* s_q) {
 #pragma unroll
   for (int i = 0; i < QPT; ++i) {
-    const int e = threadIdx.x + i * kThreads;
+    const int e = threadIdx.x + i * NT;
     if (e < NKS * 64) {
       const half8 q = __builtin_bit_cast(half8, qraw[i]);
       const float kc[8] = {ksc[i][0].x, ksc[i][0].y, ksc[i][0].z, ksc[i][0].w,
@@ -454,9 +455,9 @@ struct Scales {
   float4 vs;       // this thread's float4 of the per-channel value scales
 };
 
-template <int VD>
+template <int VD, int NT = kThreads>
 __device__ __forceinline__ Scales load_scales(const SplitArgs& a, int g) {
-  static_assert(VD / 4 <= kThreads, "one float4 of value scales per thread");
+  static_assert(VD / 4 <= NT, "one float4 of value scales per thread");
   Scales sc;
   sc.k_tensor = a.k_quant == PKV_QUANT_PER_TENSOR ? uniform_load(a.k_scale, 0) : 1.0f;
   sc.v_tensor = a.v_quant == PKV_QUANT_PER_TENSOR ? uniform_load(a.v_scale, 0) : 1.0f;
@@ -466,7 +467,7 @@ __device__ __forceinline__ Scales load_scales(const SplitArgs& a, int g) {
   return sc;
 }
 
-template <int VD>
+template <int VD, int NT = kThreads>
 __device__ __forceinline__ void stage_scales(const SplitArgs& a, const Scales& sc, float* s_vs) {
   if (a.v_quant == PKV_QUANT_PER_CHANNEL && threadIdx.x < VD / 4)
     reinterpret_cast<float4*>(s_vs)[threadIdx.x] = sc.vs;
@@ -517,7 +518,7 @@ split_kernel(const SplitArgs a) {
   float4 ksc[QPT][2];
   const int32_t* bt_row = a.block_table + (size_t)r * a.max_blocks_per_row;
   // block ids of this wave's first 64 tiles (static mode: before the length)
-  WaveBlocks wb{bt_row, split_p0(a, wk), wave, 0, 0};
+  WaveBlocks wb{bt_row, split_p0(a, wk), wave, W, 0, 0};
   if constexpr (!GATHER) wb.load(a, 0, lane);
   q_issue<C::NKS, C::EB, D>(a, wk, qraw, ksc);
   const Scales sc = load_scales<VD>(a, g);
@@ -783,17 +784,19 @@ split_kernel(const SplitArgs a) {
 // ---- the latent (absorbed-MLA) kernel -------------------------------------
 //
 // One cache row per token supplies K (all 576 channels) and V (its first 512
-// channels).  A CTA walks its position range in rounds of four 16-token
-// tiles.  In round rd wave w
+// channels).  A CTA of W waves (8 for one-byte codes: one CTA per CU, two
+// waves per SIMD; 4 for FP16 codes, whose stage is twice as large) walks its
+// position range in rounds of W 16-token tiles.  In round rd wave w
 //   * computes the scores S^T = K Q'^T of tile w from its K registers
 //     (fetched two rounds ahead) and publishes them in LDS,
 //   * copies the tile's raw codes into the round's LDS stage (64 rows),
-//   * runs, like every wave, the online softmax over all 64 tokens (so all
+//   * runs, like every wave, the online softmax over all 16 W tokens (so all
 //     waves hold the same running maximum and sum), and
-//   * accumulates V channels [128 w, 128 w + 128) of all 64 tokens, reading
-//     the V^T operands from the stage with the LDS transpose reads.
+//   * accumulates V channels [512 w / W, 512 (w + 1) / W) of all tokens of
+//     the round, reading the V^T operands from the stage with the LDS
+//     transpose reads.
 // Each row therefore crosses HBM and L2 once, V needs no registers while in
-// flight, and each wave keeps a 16 x 128 accumulator instead of 16 x 512.
+// flight, and each wave keeps a 16 x (512 / W) accumulator.
 // Stage rows are padded so that the four token groups of a transposed V
 // read fall on disjoint LDS banks.
 
@@ -805,10 +808,12 @@ struct LatCfg {
   static constexpr int NKS = D / 32;
   static constexpr int NKL = KROW / 64;          // 16-byte K loads per lane per tile
   static constexpr int NKW = NKL * 4;
-  static constexpr int VQ = VD / kWaves;         // V channels per wave
+  static constexpr int W = EB == 1 ? kLatentWaves : kWaves;  // waves per CTA
+  static constexpr int NT = 64 * W;              // threads per CTA
+  static constexpr int VQ = VD / W;              // V channels per wave
   static constexpr int CPL = VQ / 16;            // 16-channel column tiles per wave
   static constexpr int RS = KROW + 32 * EB;      // LDS stage row stride (bytes)
-  static constexpr int ROUND = 16 * kWaves;      // tokens per round
+  static constexpr int ROUND = 16 * W;          // tokens per round
   static constexpr int MIN_WAVES = EB == 1 ? 2 : 1;
   static_assert(RS % 16 == 0, "stage rows hold 16-byte chunks");
 };
@@ -838,11 +843,12 @@ __device__ __forceinline__ half4 lds_read_tr16(const uint8_t* p) {
 }
 
 template <int CT, bool GATHER>
-__global__ void __launch_bounds__(kThreads)
+__global__ void __launch_bounds__((LatCfg<CT, GATHER>::NT))
 __attribute__((amdgpu_waves_per_eu(LatCfg<CT, GATHER>::MIN_WAVES)))
 latent_kernel(const SplitArgs a) {
   using C = LatCfg<CT, GATHER>;
-  constexpr int W = kWaves;
+  constexpr int W = C::W;
+  constexpr int NT = C::NT;
   constexpr int D = C::D;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -869,20 +875,20 @@ latent_kernel(const SplitArgs a) {
   __shared__ f32x4 s_sc[W][64];                   // published scores of the round
   __shared__ __attribute__((aligned(16))) uint8_t s_stage[C::ROUND * C::RS];
   __shared__ float s_vs[C::VD];
-  constexpr int QPT = (C::NKS * 64 + kThreads - 1) / kThreads;
+  constexpr int QPT = (C::NKS * 64 + NT - 1) / NT;
   uint4 qraw[QPT];
   float4 ksc[QPT][2];
   const int32_t* bt_row = a.block_table + (size_t)r * a.max_blocks_per_row;
   // block ids of this wave's first 64 tiles (static mode: before the length)
-  WaveBlocks wb{bt_row, split_p0(a, wk), wave, 0, 0};
+  WaveBlocks wb{bt_row, split_p0(a, wk), wave, W, 0, 0};
   if constexpr (!GATHER) wb.load(a, 0, lane);
-  q_issue<C::NKS, C::EB, D>(a, wk, qraw, ksc);
-  const Scales sc = load_scales<C::VD>(a, g);
+  q_issue<C::NKS, C::EB, D, QPT, NT>(a, wk, qraw, ksc);
+  const Scales sc = load_scales<C::VD, NT>(a, g);
   finish_item<GATHER>(a, wk, balanced, raw_npos, raw_len);
   const int len = wk.len;
 
   int p0, p1;
-  if (!split_range(a, wk, p0, p1)) return;
+  if (!split_range<NT>(a, wk, p0, p1)) return;
   const int split = wk.split;
   const int ntiles = (p1 - p0 + 15) >> 4;
   const int nrounds = (ntiles + W - 1) / W;
@@ -1049,11 +1055,13 @@ latent_kernel(const SplitArgs a) {
     }
   };
 
+  // two rounds of K in flight (deeper register rings measured slower on
+  // MI355X: more outstanding misses per CU only lengthen the latency)
   LatK<C> ka, kb;
   issue_k(ka, wave);
   issue_k(kb, W + wave);
-  q_stage<C::NKS, C::EB, D>(qraw, ksc, sc.k_tensor, s_q);
-  stage_scales<C::VD>(a, sc, s_vs);
+  q_stage<C::NKS, C::EB, D, QPT, NT>(qraw, ksc, sc.k_tensor, s_q);
+  stage_scales<C::VD, NT>(a, sc, s_vs);
   __syncthreads();
   for (int rd = 0; rd < nrounds; rd += 2) {
     round(ka, rd);
@@ -1203,7 +1211,7 @@ template <int CT, int D, int VD, bool LAT, bool GA>
 static hipError_t launch_one(const SplitArgs& a, hipStream_t stream) {
   dim3 grid(a.grid_ctas);
   if constexpr (LAT)
-    hipLaunchKernelGGL((latent_kernel<CT, GA>), grid, dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((latent_kernel<CT, GA>), grid, dim3(LatCfg<CT, GA>::NT), 0, stream, a);
   else
     hipLaunchKernelGGL((split_kernel<CT, D, VD, LAT, GA>), grid, dim3(kThreads), 0, stream, a);
   return hipGetLastError();
@@ -1212,7 +1220,7 @@ static hipError_t launch_one(const SplitArgs& a, hipStream_t stream) {
 template <int CT, int D, int VD, bool LAT, bool GA>
 static hipError_t occupancy_one(int* n) {
   if constexpr (LAT)
-    return hipOccupancyMaxActiveBlocksPerMultiprocessor(n, latent_kernel<CT, GA>, kThreads, 0);
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(n, latent_kernel<CT, GA>, LatCfg<CT, GA>::NT, 0);
   else
     return hipOccupancyMaxActiveBlocksPerMultiprocessor(n, split_kernel<CT, D, VD, LAT, GA>,
                                                          kThreads, 0);
