@@ -198,6 +198,16 @@ pkv_status split_geometry(const pkv_problem* problem, const pkv_geometry_opts* o
  * (a hipStream_t; NULL = the default stream); no allocation, no memset, no
  * synchronisation.
  *
+ * Numerics (ONNX Runtime PR #33707, "Numerics" and its review thread): the
+ * key scale is folded into an FP16 query and the probabilities enter the PV
+ * products as FP16 high + residual tiles (scaled by 16).  Each CTA bounds
+ * the logit error of the folding per head and recomputes its partial on an
+ * FP32 path (unfolded query, exact running maximum, FP32 sums) when the
+ * bound exceeds 0.125 nats, or when quantised values with
+ * max|v_scale| * max|code| * positions >= 2^17 meet a probability below the
+ * FP16 tile's normal range.  Accuracy against an FP64 reference on
+ * unit-variance values: max abs error <= 2e-3, mean <= 2e-4.
+ *
  * Alignment: query, key_cache, value_cache, out, workspace and per-channel
  * scale arrays 16-byte aligned; integer arrays, per-tensor scales,
  * head_sink and lse_out 4-byte aligned.  softmax_scale must be finite and

@@ -259,7 +259,7 @@ pkv::SplitArgs split_args(const pkv_problem& p, const pkv_geometry& g, const Ptr
   a.v_quant = latent ? p.k_quant : p.v_quant;
   a.v_scale_stride = latent ? p.head_size : p.v_head_size;
   a.score_scale = softmax_scale;
-  a.v_mult = 1.0f;
+  a.v_mult = 1.0f / 16.0f;  // the kernels' probability tiles carry a factor 16
   return a;
 }
 

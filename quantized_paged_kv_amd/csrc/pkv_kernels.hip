@@ -32,6 +32,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "pkv_internal.h"
 
 namespace pkv {
@@ -86,6 +88,81 @@ template <int CT>
 __device__ __forceinline__ half4 codes4_to_half4(uint32_t x) {
   if constexpr (CT == PKV_I8) return i8x4_to_half4(x);
   else return fp8x4_to_half4(x);
+}
+
+// ---- robust numerics --------------------------------------------------------
+//
+// The fast path rounds two things to FP16: the folded query Q' = Q k_scale
+// and the probability tile P.  Following the INT8 DynamicSparseAttention
+// page (ONNX Runtime PR #33707, "Numerics": the table of review cases and
+// the follow-up review thread), each CTA guards both:
+//   * P enters the PV products as FP16(16 p) and, when the values are large
+//     enough for its rounding to matter, also as the FP16 residual (a second
+//     MFMA), so a probability keeps about 22 bits and values of opposite
+//     sign do not cancel through rounding; the factor 16 is exact and
+//     removed with the value scale (p <= e^8, the rescale slack, so 16 p
+//     stays below FP16's maximum);
+//   * the folding error of Q' is bounded per head,
+//       eps_h = scale * sum_d |fp16(Q_d ks_d) - Q_d ks_d| * max|code|,
+//     and a CTA with eps_h above 0.125 nats recomputes its partial on an
+//     FP32 path;
+//   * with quantised values, a CTA whose tile held a probability below
+//     FP16's normal range (16 p < 2^-14) recomputes on the FP32 path when
+//     max|value_scale| * max|code| * tokens >= 2^17, i.e. when such
+//     probabilities can move the output by more than about 2^-12.
+// The FP32 path evaluates the definition directly: unfolded Q k_scale in
+// FP32, exact running maximum in natural-log units, FP32 sums, and the value
+// scale applied after accumulation.
+constexpr float kProbScale = 16.0f;
+constexpr float kFoldBudget = 0.125f;          // nats
+constexpr float kTailLog = -12.47664925f;      // ln(2^-18): 16 p below 2^-14
+constexpr float kTailArm = 131072.0f;          // 2^17
+#ifndef PKV_RESIDUAL_TILE
+#define PKV_RESIDUAL_TILE 1
+#endif
+constexpr bool kResidualTile = PKV_RESIDUAL_TILE != 0;
+
+// largest |code| of a cache format (FP16: the largest finite value)
+template <int CT>
+__device__ __forceinline__ float code_bound() {
+  if constexpr (CT == PKV_I8) return 128.0f;
+  else if constexpr (CT == PKV_FP8_E4M3FN) return 448.0f;
+  else return 65504.0f;
+}
+
+// FP16(16 p) and, with LO, the FP16 residual of that rounding
+template <bool LO>
+__device__ __forceinline__ void split_prob(const float (&p)[4], half4& hi, half4& lo) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const float ps = p[q] * kProbScale;
+    hi[q] = (half_t)ps;
+    if constexpr (LO) lo[q] = (half_t)(ps - (float)hi[q]);
+  }
+}
+
+// exact value of the code at byte offset `i` of a row (FP16: element i)
+template <int CT>
+__device__ __forceinline__ float code_at(const uint8_t* row, int i) {
+  if constexpr (CT == PKV_F16) {
+    return (float)reinterpret_cast<const half_t*>(row)[i];
+  } else if constexpr (CT == PKV_I8) {
+    return (float)reinterpret_cast<const int8_t*>(row)[i];
+  } else {
+    return (float)__builtin_amdgcn_cvt_scalef32_pk_f16_fp8((uint32_t)row[i], 1.0f, false)[0];
+  }
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off);
+  return x;
+}
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
+  return x;
 }
 
 // ---- wave-uniform reads ----------------------------------------------------
@@ -430,7 +507,7 @@ __device__ __forceinline__ void q_issue(const SplitArgs& a, const Work& w, uint4
 // ks_tensor: the per-tensor key scale (1 when not per tensor).
 template <int NKS, int EB, int D, int QPT, int NT = kThreads>
 __device__ __forceinline__ void q_stage(const uint4 (&qraw)[QPT], const float4 (&ksc)[QPT][2],
-                                        float ks_tensor, uint4* s_q) {
+                                        float ks_tensor, uint4* s_q, float* s_err) {
 #pragma unroll
   for (int i = 0; i < QPT; ++i) {
     const int e = threadIdx.x + i * NT;
@@ -439,9 +516,15 @@ __device__ __forceinline__ void q_stage(const uint4 (&qraw)[QPT], const float4 (
       const float kc[8] = {ksc[i][0].x, ksc[i][0].y, ksc[i][0].z, ksc[i][0].w,
                            ksc[i][1].x, ksc[i][1].y, ksc[i][1].z, ksc[i][1].w};
       half8 o;
+      float err = 0.0f;  // folding error of the entry's eight channels
 #pragma unroll
-      for (int x = 0; x < 8; ++x) o[x] = (half_t)((float)q[x] * (kc[x] * ks_tensor));
+      for (int x = 0; x < 8; ++x) {
+        const float v = (float)q[x] * (kc[x] * ks_tensor);
+        o[x] = (half_t)v;
+        err += fabsf((float)o[x] - v);
+      }
       s_q[e] = __builtin_bit_cast(uint4, o);
+      s_err[e] = err;
     }
   }
 }
@@ -480,6 +563,144 @@ __device__ __forceinline__ float v_scale_of(const SplitArgs& a, const Scales& sc
   return a.v_quant == PKV_QUANT_PER_CHANNEL ? s_vs[c] : sc.v_tensor;
 }
 
+// ---- FP32 path of one work item (robust numerics) ----------------------------
+//
+// Recomputes the partial of the CTA's work item from the definition, one
+// query head at a time: every wave takes the positions p0 + wave + W j, the
+// score is the FP32 dot product of the unfolded Q k_scale with the exactly
+// decoded key codes (reduced across the wave), the running maximum is exact
+// (natural-log units), and the FP32 accumulator is multiplied by the value
+// scale after the W wave states are merged in a fixed order.  `scratch`
+// holds W * (VD + 2) floats of LDS; every thread of the CTA calls this.
+template <int CT, int D, int VD, bool LATENT, bool GATHER, int W>
+__device__ __forceinline__ void exact_partial(const SplitArgs& a, const Work& wk, int p0, int p1,
+                                           const Scales& sc, const float* s_vs, float* scratch) {
+  constexpr int NT = 64 * W;
+  constexpr int EB = (CT == PKV_F16) ? 2 : 1;
+  constexpr int KROW = D * EB;
+  constexpr int VROW = LATENT ? KROW : VD * EB;
+  constexpr int KD = (D + 63) / 64;
+  constexpr int KV = (VD + 63) / 64;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int S = a.num_splits;
+  const int KVH = a.kv_heads;
+  const int g = wk.g;
+  const int32_t* bt_row = a.block_table + (size_t)wk.r * a.max_blocks_per_row;
+  const uint8_t* vbase = LATENT ? a.key_cache : a.value_cache;
+  for (int hh = 0; hh < wk.nh; ++hh) {
+    const int h = wk.h0 + hh;
+    float qf[KD];
+#pragma unroll
+    for (int k = 0; k < KD; ++k) {
+      const int d = lane + 64 * k;
+      qf[k] = 0.0f;
+      if (d < D) {
+        const float ks = a.k_quant == PKV_QUANT_PER_CHANNEL ? a.k_scale[(size_t)g * D + d] : sc.k_tensor;
+        qf[k] = (float)reinterpret_cast<const half_t*>(a.query)[((size_t)wk.r * a.heads + h) * D + d] * ks;
+      }
+    }
+    float m = kNegInf, l = 0.0f;
+    float acc[KV];
+#pragma unroll
+    for (int k = 0; k < KV; ++k) acc[k] = 0.0f;
+    for (int pos = p0 + wave; pos < p1; pos += W) {
+      int t = pos;
+      if constexpr (GATHER) {
+        t = a.candidates[(size_t)wk.r * a.max_candidates + pos];
+        if (t < 0 || t >= wk.len) continue;
+      }
+      const int blk = bt_row[t >> a.log2_block];
+      if (blk < 0 || blk >= a.num_pool_blocks) continue;
+      const size_t slot = ((size_t)blk << a.log2_block) + (t & (a.block_size - 1));
+      const uint8_t* krow = a.key_cache + (slot * KVH + g) * KROW;
+      float part = 0.0f;
+#pragma unroll
+      for (int k = 0; k < KD; ++k) {
+        const int d = lane + 64 * k;
+        if (d < D) part += qf[k] * code_at<CT>(krow, d);
+      }
+      const float sv = wave_sum(part) * a.score_scale;
+      if (sv > m) {
+        const float alpha = (m == kNegInf) ? 0.0f : expf(m - sv);
+        l *= alpha;
+#pragma unroll
+        for (int k = 0; k < KV; ++k) acc[k] *= alpha;
+        m = sv;
+      }
+      const float pp = expf(sv - m);
+      l += pp;
+      const uint8_t* vrow = vbase + (slot * KVH + g) * VROW;
+#pragma unroll
+      for (int k = 0; k < KV; ++k) {
+        const int c = lane + 64 * k;
+        if (c < VD) acc[k] += pp * code_at<CT>(vrow, c);
+      }
+    }
+    float* sw = scratch + wave * (VD + 2);
+#pragma unroll
+    for (int k = 0; k < KV; ++k) {
+      const int c = lane + 64 * k;
+      if (c < VD) sw[c] = acc[k];
+    }
+    if (lane == 0) {
+      sw[VD] = m;
+      sw[VD + 1] = l;
+    }
+    __syncthreads();
+    float M = kNegInf;
+#pragma unroll
+    for (int w = 0; w < W; ++w) M = fmaxf(M, scratch[w * (VD + 2) + VD]);
+    float f[W];
+    float L = 0.0f;
+#pragma unroll
+    for (int w = 0; w < W; ++w) {
+      const float mw = scratch[w * (VD + 2) + VD];
+      f[w] = (mw == kNegInf) ? 0.0f : expf(mw - M);
+      L += f[w] * scratch[w * (VD + 2) + VD + 1];
+    }
+    const size_t pidx = ((size_t)wk.r * a.heads + h) * S + wk.split;
+    for (int c = threadIdx.x; c < VD; c += NT) {
+      float o = 0.0f;
+#pragma unroll
+      for (int w = 0; w < W; ++w) o += f[w] * scratch[w * (VD + 2) + c];
+      a.ws_acc[pidx * VD + c] = o * v_scale_of(a, sc, s_vs, c);
+    }
+    if (threadIdx.x == 0) reinterpret_cast<float2*>(a.ws_ml)[pidx] = make_float2(M, L);
+    __syncthreads();
+  }
+}
+
+// Folding bound of the CTA's heads (called by one wave after Q' is staged):
+// true when some head's eps_h exceeds the budget.  s_err holds, per Q'
+// entry, the summed |fp16(Q ks) - Q ks| of its eight channels.
+template <int CT, int NKS>
+__device__ __forceinline__ bool fold_over_budget(const SplitArgs& a, const float* s_err, int nh,
+                                                 int lane) {
+  float e = 0.0f;
+  if (lane < 16 && lane < nh) {
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+      for (int lj = 0; lj < 4; ++lj) e += s_err[ks * 64 + lj * 16 + lane];
+  }
+  return __any(e * code_bound<CT>() * a.score_scale > kFoldBudget);
+}
+
+// max |value| of the KV head's quantised values (0 when V is not quantised)
+template <int CT, int VD>
+__device__ __forceinline__ float value_bound(const SplitArgs& a, const Scales& sc, const float* s_vs,
+                                             int lane) {
+  if (a.v_quant == PKV_QUANT_NONE) return 0.0f;
+  float vm = fabsf(sc.v_tensor);
+  if (a.v_quant == PKV_QUANT_PER_CHANNEL) {
+    vm = 0.0f;
+    for (int c = lane; c < VD; c += 64) vm = fmaxf(vm, fabsf(s_vs[c]));
+    vm = wave_max(vm);
+  }
+  return vm * code_bound<CT>();
+}
+
 template <int CT, int D, int VD, bool LATENT, bool GATHER>
 __global__ void __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(SplitCfg<CT, D, VD, LATENT, GATHER>::MIN_WAVES)))
@@ -512,6 +733,8 @@ split_kernel(const SplitArgs a) {
   const int r = wk.r, g = wk.g, h0 = wk.h0, nh = wk.nh;
 
   __shared__ uint4 s_q[C::NKS * 64];
+  __shared__ float s_err[C::NKS * 64];  // folding error per Q' entry
+  __shared__ int s_flag[W + 1];         // per wave: a deep-tail probability; [W]: folding
   __shared__ float s_vs[VD];
   constexpr int QPT = (C::NKS * 64 + kThreads - 1) / kThreads;  // entries per thread
   uint4 qraw[QPT];
@@ -542,7 +765,7 @@ split_kernel(const SplitArgs a) {
   // Issue the loads of tile t into T.  Tiles at or past ntiles issue loads
   // that read nothing (dense rows: an empty buffer descriptor) so every
   // iteration issues the same instruction stream.
-  auto issue = [&](Tile<C>& T, int t) {
+  auto issue = [&](Tile<C>& T, int t) __attribute__((always_inline)) {
     const int tp = p0 + 16 * t;  // first position of the tile
     uint32_t vm = 0;
     if constexpr (!GATHER) {
@@ -603,9 +826,12 @@ split_kernel(const SplitArgs a) {
   for (int ct = 0; ct < C::NCT; ++ct) acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_ref = kNegInf;   // running reference maximum of head li (natural log units)
   float l_part = 0.0f;     // this lane's share of the running sum
+  float smin = __builtin_inff();  // smallest valid score of this lane (tail-depth check)
 
-  // Consume tile T: scores, online softmax, PV.
-  auto consume = [&](const Tile<C>& T) {
+  // Consume tile T: scores, online softmax, PV (lo: with the residual
+  // probability tile).
+  auto consume = [&](const Tile<C>& T, auto lo) __attribute__((always_inline)) {
+    constexpr bool LO = decltype(lo)::value;
     // S^T = K Q'^T : lane holds scores of tokens 4 lj + q for head li
     f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -630,7 +856,11 @@ split_kernel(const SplitArgs a) {
     }
     float sc[4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) sc[q] = ((T.vmask >> q) & 1u) ? sacc[q] * a.score_scale : kNegInf;
+    for (int q = 0; q < 4; ++q) {
+      const bool valid = (T.vmask >> q) & 1u;
+      sc[q] = valid ? sacc[q] * a.score_scale : kNegInf;
+      smin = fminf(smin, valid ? sc[q] : __builtin_inff());
+    }
     float mt = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
     mt = fmaxf(mt, __shfl_xor(mt, 16));
     mt = fmaxf(mt, __shfl_xor(mt, 32));
@@ -648,7 +878,8 @@ split_kernel(const SplitArgs a) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) p[q] = __builtin_amdgcn_exp2f((sc[q] - mu) * kLog2e);
     l_part += (p[0] + p[1]) + (p[2] + p[3]);
-    const half4 pop = {(half_t)p[0], (half_t)p[1], (half_t)p[2], (half_t)p[3]};
+    half4 pop, pol;  // FP16(16 p) and its residual
+    split_prob<LO>(p, pop, pol);
 
     // V^T operands: for col tile ct, lane holds channel li*CPL+ct of tokens
     // 4 lj .. 4 lj + 3 (rows q = 0..3 of its segments), transposed in registers
@@ -667,6 +898,10 @@ split_kernel(const SplitArgs a) {
         const half4 vb = __builtin_bit_cast(half4, uint2{b01, b23});
         acc[2 * w] = __builtin_amdgcn_mfma_f32_16x16x16f16(va, pop, acc[2 * w], 0, 0, 0);
         acc[2 * w + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(vb, pop, acc[2 * w + 1], 0, 0, 0);
+        if constexpr (LO) {
+          acc[2 * w] = __builtin_amdgcn_mfma_f32_16x16x16f16(va, pol, acc[2 * w], 0, 0, 0);
+          acc[2 * w + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(vb, pol, acc[2 * w + 1], 0, 0, 0);
+        }
       }
     } else {
 #pragma unroll
@@ -677,10 +912,18 @@ split_kernel(const SplitArgs a) {
         const uint32_t t2 = perm(r3, r2, 0x05010400u), t3 = perm(r3, r2, 0x07030602u);
         const uint32_t o0 = perm(t2, t0, 0x05040100u), o1 = perm(t2, t0, 0x07060302u);
         const uint32_t o2 = perm(t3, t1, 0x05040100u), o3 = perm(t3, t1, 0x07060302u);
-        acc[4 * w + 0] = __builtin_amdgcn_mfma_f32_16x16x16f16(codes4_to_half4<CT>(o0), pop, acc[4 * w + 0], 0, 0, 0);
-        acc[4 * w + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(codes4_to_half4<CT>(o1), pop, acc[4 * w + 1], 0, 0, 0);
-        acc[4 * w + 2] = __builtin_amdgcn_mfma_f32_16x16x16f16(codes4_to_half4<CT>(o2), pop, acc[4 * w + 2], 0, 0, 0);
-        acc[4 * w + 3] = __builtin_amdgcn_mfma_f32_16x16x16f16(codes4_to_half4<CT>(o3), pop, acc[4 * w + 3], 0, 0, 0);
+        const half4 h0 = codes4_to_half4<CT>(o0), h1 = codes4_to_half4<CT>(o1);
+        const half4 h2 = codes4_to_half4<CT>(o2), h3 = codes4_to_half4<CT>(o3);
+        acc[4 * w + 0] = __builtin_amdgcn_mfma_f32_16x16x16f16(h0, pop, acc[4 * w + 0], 0, 0, 0);
+        acc[4 * w + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(h1, pop, acc[4 * w + 1], 0, 0, 0);
+        acc[4 * w + 2] = __builtin_amdgcn_mfma_f32_16x16x16f16(h2, pop, acc[4 * w + 2], 0, 0, 0);
+        acc[4 * w + 3] = __builtin_amdgcn_mfma_f32_16x16x16f16(h3, pop, acc[4 * w + 3], 0, 0, 0);
+        if constexpr (LO) {
+          acc[4 * w + 0] = __builtin_amdgcn_mfma_f32_16x16x16f16(h0, pol, acc[4 * w + 0], 0, 0, 0);
+          acc[4 * w + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(h1, pol, acc[4 * w + 1], 0, 0, 0);
+          acc[4 * w + 2] = __builtin_amdgcn_mfma_f32_16x16x16f16(h2, pol, acc[4 * w + 2], 0, 0, 0);
+          acc[4 * w + 3] = __builtin_amdgcn_mfma_f32_16x16x16f16(h3, pol, acc[4 * w + 3], 0, 0, 0);
+        }
       }
     }
   };
@@ -692,21 +935,33 @@ split_kernel(const SplitArgs a) {
   for (int i = 0; i < NST - 1; ++i) issue(buf[i], wave + i * W);
 
   // Q' into LDS (its loads were issued before the tile loads above)
-  q_stage<C::NKS, C::EB, D>(qraw, ksc, sc.k_tensor, s_q);
+  q_stage<C::NKS, C::EB, D>(qraw, ksc, sc.k_tensor, s_q, s_err);
   stage_scales<VD>(a, sc, s_vs);
   __syncthreads();
-
-  for (int t = wave; t < ntiles; t += NST * W) {
-#pragma unroll
-    for (int st = 0; st < NST; ++st) {
-      const int tt = t + st * W;
-      if (tt >= ntiles) break;
-      issue(buf[(st + NST - 1) % NST], tt + (NST - 1) * W);
-      // keep the loads ahead of the wait for this tile's data
-      __builtin_amdgcn_sched_barrier(0);
-      consume(buf[st]);
-    }
+  // folding bound of the CTA's heads (read after the final barrier)
+  if (wave == 0) {
+    const bool fold = fold_over_budget<CT, C::NKS>(a, s_err, nh, lane);
+    if (lane == 0) s_flag[W] = fold ? 1 : 0;
   }
+
+  auto tile_loop = [&](auto lo) __attribute__((always_inline)) {
+    for (int t = wave; t < ntiles; t += NST * W) {
+#pragma unroll
+      for (int st = 0; st < NST; ++st) {
+        const int tt = t + st * W;
+        if (tt >= ntiles) break;
+        issue(buf[(st + NST - 1) % NST], tt + (NST - 1) * W);
+        // keep the loads ahead of the wait for this tile's data
+        __builtin_amdgcn_sched_barrier(0);
+        consume(buf[st], lo);
+      }
+    }
+  };
+  tile_loop(std::integral_constant<bool, kResidualTile>{});
+  // a valid probability that fell below the FP16 tile's normal range: some
+  // score more than ln 2^18 below the lane's final reference maximum (the
+  // reference never decreases, so this is conservative)
+  const bool deep = smin != __builtin_inff() && smin - m_ref < kTailLog;
 
   // ---- merge the W wave states (fixed order) and publish the partial -----
   // l: sum the four lane groups of head li
@@ -726,7 +981,23 @@ split_kernel(const SplitArgs a) {
     sm_m[wave][lane] = m_ref;
     sm_l[wave][lane] = l_part;
   }
+  {
+    const bool dw = __any(deep);
+    if (lane == 0) s_flag[wave] = dw ? 1 : 0;
+  }
   __syncthreads();
+  {
+    // robust numerics: recompute on the FP32 path when the folding bound or
+    // the tail-depth check fails (a CTA-uniform decision)
+    bool deep_any = false;
+#pragma unroll
+    for (int w = 0; w < W; ++w) deep_any |= s_flag[w] != 0;
+    const bool armed = deep_any && value_bound<CT, VD>(a, sc, s_vs, lane) * (float)(p1 - p0) >= kTailArm;
+    if (s_flag[W] != 0 || (deep_any && armed)) {
+      exact_partial<CT, D, VD, LATENT, GATHER, W>(a, wk, p0, p1, sc, s_vs, sm_acc);
+      return;
+    }
+  }
   {
     float M = kNegInf;
 #pragma unroll
@@ -872,6 +1143,8 @@ latent_kernel(const SplitArgs a) {
   const int r = wk.r, g = wk.g, h0 = wk.h0, nh = wk.nh;
 
   __shared__ uint4 s_q[C::NKS * 64];
+  __shared__ float s_err[C::NKS * 64];            // folding error per Q' entry
+  __shared__ int s_flag[W + 1];                   // per wave: a deep-tail probability; [W]: folding
   __shared__ f32x4 s_sc[W][64];                   // published scores of the round
   __shared__ __attribute__((aligned(16))) uint8_t s_stage[C::ROUND * C::RS];
   __shared__ float s_vs[C::VD];
@@ -896,7 +1169,7 @@ latent_kernel(const SplitArgs a) {
   const uint32_t tok = (uint32_t)KVH * C::KROW;  // bytes per token slot
   const uint32_t koff = (uint32_t)li * tok + (uint32_t)g * C::KROW + 16u * lj;
 
-  auto issue_k = [&](LatK<C>& T, int t) {
+  auto issue_k = [&](LatK<C>& T, int t) __attribute__((always_inline)) {
     uint32_t m = 0;
     if constexpr (!GATHER) {
       int64_t s0 = 0;
@@ -942,6 +1215,7 @@ latent_kernel(const SplitArgs a) {
   for (int ct = 0; ct < C::CPL; ++ct) acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_ref = kNegInf;
   float l_part = 0.0f;
+  float smin = __builtin_inff();  // smallest valid score of this wave's tiles (lane's head)
 
   // this lane's 16-byte K chunks of its tile row
   uint8_t* const stage_k = s_stage + (size_t)(16 * wave + li) * C::RS + 16 * lj;
@@ -959,7 +1233,8 @@ latent_kernel(const SplitArgs a) {
 
   // Round rd on the K tile in T; afterwards T is free and the loads of
   // round rd + 2 are issued into it.
-  auto round = [&](LatK<C>& T, int rd) {
+  auto round = [&](LatK<C>& T, int rd, auto lo) __attribute__((always_inline)) {
+    constexpr bool LO = decltype(lo)::value;
     // scores of this wave's tile
     f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -981,7 +1256,11 @@ latent_kernel(const SplitArgs a) {
     }
     f32x4 scw;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) scw[q] = ((T.mask >> q) & 1u) ? sacc[q] * a.score_scale : kNegInf;
+    for (int q = 0; q < 4; ++q) {
+      const bool valid = (T.mask >> q) & 1u;
+      scw[q] = valid ? sacc[q] * a.score_scale : kNegInf;
+      smin = fminf(smin, valid ? scw[q] : __builtin_inff());
+    }
     s_sc[wave][lane] = scw;
     // every wave is past the previous round's V reads and has published its
     // scores (one score buffer suffices: a wave reads the scores of round rd
@@ -1016,14 +1295,14 @@ latent_kernel(const SplitArgs a) {
       m_ref = mn;
     }
     const float mu = (m_ref == kNegInf) ? 0.0f : m_ref;
-    half4 pop[W];
+    half4 pop[W], pol[W];  // FP16(16 p) and its residual
 #pragma unroll
     for (int j = 0; j < W; ++j) {
       float p[4];
 #pragma unroll
       for (int q = 0; q < 4; ++q) p[q] = __builtin_amdgcn_exp2f((st[j][q] - mu) * kLog2e);
       l_part += (p[0] + p[1]) + (p[2] + p[3]);
-      pop[j] = half4{(half_t)p[0], (half_t)p[1], (half_t)p[2], (half_t)p[3]};
+      split_prob<LO>(p, pop[j], pol[j]);
     }
     // the stage holds all 64 rows of the round
     __syncthreads();
@@ -1034,6 +1313,10 @@ latent_kernel(const SplitArgs a) {
       for (int m = 0; m < W / 2; ++m) {
         const half8 pb = {pop[2 * m][0], pop[2 * m][1], pop[2 * m][2], pop[2 * m][3],
                           pop[2 * m + 1][0], pop[2 * m + 1][1], pop[2 * m + 1][2], pop[2 * m + 1][3]};
+        half8 pl = {};
+        if constexpr (LO)
+          pl = half8{pol[2 * m][0], pol[2 * m][1], pol[2 * m][2], pol[2 * m][3],
+                     pol[2 * m + 1][0], pol[2 * m + 1][1], pol[2 * m + 1][2], pol[2 * m + 1][3]};
 #pragma unroll
         for (int ct = 0; ct < C::CPL; ++ct) {
           const v2i32 raw = lds_read_tr8(stage_v + (size_t)(32 * m) * C::RS + 16 * ct);
@@ -1041,6 +1324,7 @@ latent_kernel(const SplitArgs a) {
           const half4 hi = codes4_to_half4<CT>((uint32_t)raw.y);
           const half8 va = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
           acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pb, acc[ct], 0, 0, 0);
+          if constexpr (LO) acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pl, acc[ct], 0, 0, 0);
         }
       }
     } else {
@@ -1050,6 +1334,7 @@ latent_kernel(const SplitArgs a) {
         for (int ct = 0; ct < C::CPL; ++ct) {
           const half4 va = lds_read_tr16(stage_v + (size_t)(16 * j) * C::RS + 32 * ct);
           acc[ct] = __builtin_amdgcn_mfma_f32_16x16x16f16(va, pop[j], acc[ct], 0, 0, 0);
+          if constexpr (LO) acc[ct] = __builtin_amdgcn_mfma_f32_16x16x16f16(va, pol[j], acc[ct], 0, 0, 0);
         }
       }
     }
@@ -1060,13 +1345,44 @@ latent_kernel(const SplitArgs a) {
   LatK<C> ka, kb;
   issue_k(ka, wave);
   issue_k(kb, W + wave);
-  q_stage<C::NKS, C::EB, D, QPT, NT>(qraw, ksc, sc.k_tensor, s_q);
+  q_stage<C::NKS, C::EB, D, QPT, NT>(qraw, ksc, sc.k_tensor, s_q, s_err);
   stage_scales<C::VD, NT>(a, sc, s_vs);
   __syncthreads();
-  for (int rd = 0; rd < nrounds; rd += 2) {
-    round(ka, rd);
-    if (rd + 1 >= nrounds) break;
-    round(kb, rd + 1);
+  // folding bound of the CTA's heads (read after the final barrier)
+  if (wave == 0) {
+    const bool fold = fold_over_budget<CT, C::NKS>(a, s_err, nh, lane);
+    if (lane == 0) s_flag[W] = fold ? 1 : 0;
+  }
+  auto round_loop = [&](auto lo) __attribute__((always_inline)) {
+    for (int rd = 0; rd < nrounds; rd += 2) {
+      round(ka, rd, lo);
+      if (rd + 1 >= nrounds) break;
+      round(kb, rd + 1, lo);
+    }
+  };
+  round_loop(std::integral_constant<bool, kResidualTile>{});
+  // a valid probability that fell below the FP16 tile's normal range: some
+  // score more than ln 2^18 below the final reference maximum (conservative)
+  const bool deep = smin != __builtin_inff() && smin - m_ref < kTailLog;
+
+  {
+    const bool dw = __any(deep);
+    if (lane == 0) s_flag[wave] = dw ? 1 : 0;
+  }
+  __syncthreads();
+  {
+    // robust numerics: recompute on the FP32 path when the folding bound or
+    // the tail-depth check fails (a CTA-uniform decision); the stage is free
+    bool deep_any = false;
+#pragma unroll
+    for (int w = 0; w < W; ++w) deep_any |= s_flag[w] != 0;
+    const bool armed = deep_any && value_bound<CT, C::VD>(a, sc, s_vs, lane) * (float)(p1 - p0) >= kTailArm;
+    if (s_flag[W] != 0 || (deep_any && armed)) {
+      static_assert(W * (C::VD + 2) * 4 <= C::ROUND * C::RS, "FP32-path scratch fits the stage");
+      exact_partial<CT, D, C::VD, true, GATHER, W>(a, wk, p0, p1, sc, s_vs,
+                                                   reinterpret_cast<float*>(s_stage));
+      return;
+    }
   }
 
   // every wave holds the same running maximum and sum; sum the lane groups

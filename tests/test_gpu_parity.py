@@ -271,18 +271,14 @@ def test_hip_graph_replay_matches_eager_with_new_lengths():
 
 from tests.test_oracle_pins import _golden_rows  # noqa: E402
 
-# Cases whose exact handling needs the robust-numerics mode of the INT8 DSA
-# page (FP32 fallback per CTA, hi+lo probability tile); the FP16-probability
-# fast path loses them by design.
-ROBUST_ONLY = {"large_value_scale_2p60", "large_value_scale_2p16", "large_value_scale_2p28",
-               "signed_cancellation"}
+# The large-value-scale rows reach the FP32 path through the tail-depth
+# check; signed cancellation is handled by the high + residual FP16
+# probability tiles; the others stay on the fast path.
 
 
 @pytest.mark.parametrize("row", _golden_rows(), ids=lambda r: r[0])
 def test_worked_examples_on_gpu(row):
     name = row[0]
-    if name in ROBUST_ONLY:
-        pytest.skip("needs the robust-numerics fallback path (not built yet)")
     (_, q0, q1, ka0, ka1, kb0, kb1, va, vb, vscale, sscale, expected, *_rest) = row
     D = 256
     p = Problem(rows=1, heads=1, kv_heads=1, head_size=D, v_head_size=D, block_size=16,
@@ -304,3 +300,57 @@ def test_worked_examples_on_gpu(row):
     got, _, _ = run_gpu(inp, splits_override=1)
     assert got[0, 0, 0] == pytest.approx(float(expected), rel=2e-3)
     assert np.all(got[0, 0, 1:] == 0)
+
+
+# ---------------------------------------------------------------------------
+# robust numerics: the folding bound and the tail-depth check send a CTA to
+# the FP32 path, whose result is exact to FP32 rounding
+# ---------------------------------------------------------------------------
+
+def test_folding_rounding_case_takes_the_fp32_path():
+    from tests.test_oracle_pins import folding_case
+    inp, expected = folding_case()
+    ref, _ = oracle.paged_decode(inp)
+    assert ref[0, 0, 0] == pytest.approx(expected, rel=1e-12)
+    announce("folding rounding case")
+    got, _, _ = run_gpu(inp, splits_override=1, out_dtype="f32")
+    # the folded FP16 query would give 0.5 here
+    assert got[0, 0, 0] == pytest.approx(expected, rel=1e-6)
+    assert np.all(got[0, 0, 1:] == 0)
+
+
+def _near_exact(got, ref, lse, ref_lse, rel):
+    scale = np.abs(ref).max()
+    assert np.abs(got - ref).max() <= rel * scale, (np.abs(got - ref).max(), scale)
+    assert np.allclose(lse, ref_lse, rtol=0, atol=1e-5 * (1 + np.abs(ref_lse).max()))
+
+
+@pytest.mark.parametrize("gathered", [False, True])
+def test_large_value_scale_with_deep_tail_is_exact(gathered):
+    # value scale 2^20 and queries spread wide enough that probabilities fall
+    # below the FP16 tile's range: the tail-depth check must fire.  No sink:
+    # a row without a deep tail (one token) stays on the fast path, whose lse
+    # carries the folding error that a sink would pass on to the output.
+    inp = _small("i8", 256, 256, "separate", gathered, seed=11, quant="tensor", sink=False)
+    inp.query[...] = (inp.query.astype(np.float32) * 6.0).astype(np.float16)
+    inp.v_scale = (inp.v_scale * 2.0 ** 20).astype(np.float32)
+    ref, ref_lse = oracle.paged_decode(inp)
+    announce(f"large value scale, deep tail, gathered={gathered}")
+    got, lse, _ = run_gpu(inp, splits_override=3, min_chunk=16, out_dtype="f32")
+    # splits without a deep tail keep the fast path's accuracy (about 1e-3
+    # of the value magnitude); the worked examples pin the exact tail cases
+    _near_exact(got, ref, lse, ref_lse, 1e-3)
+
+
+@pytest.mark.parametrize("cache,D,VD,lay,quant", [
+    ("i8", 128, 128, "separate", "channel"), ("fp8", 128, 128, "separate", "channel"),
+    ("fp8", 576, 512, "latent", "tensor"), ("i8", 576, 512, "latent", "channel")])
+def test_folding_over_budget_is_exact(cache, D, VD, lay, quant):
+    # large queries: the FP16 rounding of Q k_scale moves the logits by well
+    # over 0.125 nats, so every CTA takes the FP32 path
+    inp = _small(cache, D, VD, lay, lay == "separate", seed=13, quant=quant)
+    inp.query[...] = (inp.query.astype(np.float32) * 200.0).astype(np.float16)
+    ref, ref_lse = oracle.paged_decode(inp)
+    announce(f"folding over budget, {cache} {lay}")
+    got, lse, _ = run_gpu(inp, splits_override=2, min_chunk=16, out_dtype="f32")
+    _near_exact(got, ref, lse, ref_lse, 1e-4)

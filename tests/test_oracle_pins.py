@@ -371,3 +371,38 @@ def test_worked_examples(row):
     if printed != "-":
         assert abs(got - float(printed)) <= float(printed_tol)
     assert np.all(o[0, 0, 1:] == 0)
+
+
+def folding_case():
+    """The query-folding rounding case of the INT8 DynamicSparseAttention page
+    ("Numerics", first row of the review-case table), built with numbers of
+    our own: per-channel key scales make the products Q0 ks0 = 32768 and
+    Q1 ks1 = -32766, which FP16 rounds to 32768 and -32768.  Token 0 has key
+    codes (1, 1), token 1 zeros; at softmax scale 8 the exact logits are 16
+    and 0, so output channel 0 (value code 1 on token 0) is 1 / (1 + e^-16);
+    the folded FP16 query would give 0.5.  Returns (inputs, expected)."""
+    D = 256
+    p = Problem(rows=1, heads=1, kv_heads=1, head_size=D, v_head_size=D, block_size=16,
+                max_blocks_per_row=1, num_pool_blocks=1, cache_dtype="i8",
+                k_quant="channel", v_quant="channel", out_dtype="f32")
+    q = np.zeros((1, 1, D), dtype=np.float16)
+    q[0, 0, 0], q[0, 0, 1] = 2048.0, -2048.0
+    ks = np.ones((1, D), dtype=np.float32)
+    ks[0, 0], ks[0, 1] = 16.0, 16383.0 / 1024.0
+    assert float(np.float32(2048.0) * ks[0, 1]) == 32766.0
+    k = np.zeros((1, 16, 1, D), dtype=np.int8)
+    v = np.zeros((1, 16, 1, D), dtype=np.int8)
+    k[0, 0, 0, :2] = [1, 1]
+    v[0, 0, 0, 0] = 1
+    inp = Inputs(problem=p, query=q, key_cache=k, value_cache=v,
+                 block_table=np.zeros((1, 1), dtype=np.int32), seq_lens=np.array([2], np.int32),
+                 softmax_scale=8.0, k_scale=ks, v_scale=np.ones((1, D), np.float32))
+    return inp, 1.0 / (1.0 + math.exp(-16.0))
+
+
+def test_folding_case_closed_form():
+    inp, expected = folding_case()
+    out, lse = oracle.paged_decode(inp)
+    assert out[0, 0, 0] == pytest.approx(expected, rel=1e-13)
+    assert np.all(out[0, 0, 1:] == 0)
+    assert lse[0, 0] == pytest.approx(math.log(math.exp(16.0) + 1.0), rel=1e-13)
