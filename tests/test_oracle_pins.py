@@ -406,3 +406,63 @@ def test_folding_case_closed_form():
     assert out[0, 0, 0] == pytest.approx(expected, rel=1e-13)
     assert np.all(out[0, 0, 1:] == 0)
     assert lse[0, 0] == pytest.approx(math.log(math.exp(16.0) + 1.0), rel=1e-13)
+
+
+# ---------------------------------------------------------------------------
+# quantise-on-write (ONNX Runtime PR #29912, ReshapeAndCache with slot_mapping)
+# ---------------------------------------------------------------------------
+
+from oracle import cache_write  # noqa: E402
+
+
+def test_fp8_encode_matches_torch_cast_in_range():
+    rng = np.random.default_rng(0)
+    v = np.concatenate([rng.normal(0, 1, 20000) * np.exp2(rng.integers(-12, 9, 20000)),
+                        [0.0, -0.0, 2.0 ** -10, -(2.0 ** -10), 2.0 ** -9 * 1.5, 1.0625, 1.1875,
+                         447.0, 460.0, -463.9]])
+    v = v[np.abs(v) < 464].astype(np.float32)
+    ref = torch.from_numpy(v).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = cache_write.fp8_e4m3fn_encode(v)
+    assert np.array_equal(got, ref)
+
+
+def test_fp8_encode_saturates_and_round_trips():
+    got = cache_write.fp8_e4m3fn_encode(np.array([464.0, 480.0, 1e30, -500.0, np.inf]))
+    assert list(got) == [0x7E, 0x7E, 0x7E, 0xFE, 0x7E]
+    finite = [c for c in range(256) if c not in (0x7F, 0xFF)]
+    vals = np.array([oracle.fp8e4m3_to_f64(c) for c in finite])
+    assert np.array_equal(cache_write.fp8_e4m3fn_encode(vals), np.array(finite, np.uint8))
+
+
+def test_int8_encode_rounds_half_even_and_clips():
+    rng = np.random.default_rng(1)
+    v = np.concatenate([rng.uniform(-140, 140, 5000), np.arange(-130.5, 131, 0.5)]).astype(np.float32)
+    ref = np.array([min(127, max(-128, round(float(x)))) for x in v], dtype=np.int8)
+    assert np.array_equal(cache_write.int8_encode(v), ref)
+
+
+def test_reshape_and_cache_writes_only_mapped_slots():
+    p = Problem(rows=1, heads=4, kv_heads=2, head_size=64, v_head_size=64, block_size=16,
+                max_blocks_per_row=4, num_pool_blocks=4, cache_dtype="i8", k_quant="channel",
+                v_quant="tensor")
+    rng = np.random.default_rng(2)
+    kc = rng.integers(-128, 128, (4, 16, 2, 64)).astype(np.int8)
+    vc = rng.integers(-128, 128, (4, 16, 2, 64)).astype(np.int8)
+    key = rng.normal(0, 1, (5, 2, 64)).astype(np.float16)
+    val = rng.normal(0, 1, (5, 2, 64)).astype(np.float16)
+    ks = rng.uniform(0.005, 0.05, (2, 64)).astype(np.float32)
+    vs = np.array([0.03], np.float32)
+    slots = np.array([3, -1, 63, 64, 17], np.int64)
+    k2, v2 = cache_write.reshape_and_cache(p, key, val, slots, ks, vs, kc, vc)
+    written = {3: 0, 63: 2, 17: 4}
+    for b in range(4):
+        for o in range(16):
+            slot = b * 16 + o
+            if slot in written:
+                t = written[slot]
+                exp_k = np.clip(np.rint(key[t].astype(np.float32) / ks), -128, 127)
+                exp_v = np.clip(np.rint(val[t].astype(np.float32) / np.float32(0.03)), -128, 127)
+                assert np.array_equal(k2[b, o], exp_k.astype(np.int8))
+                assert np.array_equal(v2[b, o], exp_v.astype(np.int8))
+            else:
+                assert np.array_equal(k2[b, o], kc[b, o]) and np.array_equal(v2[b, o], vc[b, o])
