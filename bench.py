@@ -107,6 +107,109 @@ def cpu_baseline(inp, budget_s: float = 12.0):
                       f"{dt:.1f} s wall; {dt / reps * 1e3 * p.rows / nrows:.1f} ms per full step"}
 
 
+def bench_write(args, dev):
+    """The cache writer alone: --write-tokens new rows of the workload's
+    cache format (KV heads, head sizes, dtype, scale granularity) written at
+    distinct random slots, cycling over device replicas (inputs and caches)
+    of >= --replica-bytes so the traffic reaches HBM.  Algorithmic bytes per
+    call: the FP16 rows read, the codes written, the slot indices and the
+    per-channel scales."""
+    import dataclasses
+
+    import numpy as np
+    import torch
+
+    import quantized_paged_kv_amd as pkv
+    import workloads
+    from workloads.device import problem_kwargs
+
+    base = workloads.workload(args.workload).problem
+    T = args.write_tokens
+    p = dataclasses.replace(base, num_pool_blocks=-(-T // base.block_size))
+    nt = workloads.new_tokens(p, T, seed=31, skip_fraction=0.0)
+    prob = pkv.make_problem(**problem_kwargs(p))
+    latent = p.layout == "latent"
+    item = p.cache_itemsize
+    dims = p.head_size + (0 if latent else p.v_head_size)
+    scale_bytes = sum(4 * (p.kv_heads * d if q == "channel" else (1 if q == "tensor" else 0))
+                      for q, d in ([(p.k_quant, p.head_size)] if latent else
+                                   [(p.k_quant, p.head_size), (p.v_quant, p.v_head_size)]))
+    algo = T * p.kv_heads * dims * (2 + item) + 8 * T + scale_bytes
+
+    def dev_t(a):
+        if a is None:
+            return None
+        if a.dtype == np.float16:
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.float16)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    key, val = dev_t(nt.key), dev_t(nt.value)
+    slots, ks, vs = dev_t(nt.slot_mapping), dev_t(nt.k_scale), dev_t(nt.v_scale)
+    cdt = torch.float16 if p.cache_dtype == "f16" else torch.uint8
+    kc = torch.zeros((p.num_pool_blocks, p.block_size, p.kv_heads, p.head_size), dtype=cdt,
+                     device=dev)
+    vc = None if latent else torch.zeros((p.num_pool_blocks, p.block_size, p.kv_heads,
+                                          p.v_head_size), dtype=cdt, device=dev)
+    R = max(1, min(args.steps, math.ceil(args.replica_bytes / max(algo, 1))))
+    keys = [key] + [key.clone() for _ in range(R - 1)]
+    vals = [val] + ([val.clone() for _ in range(R - 1)] if val is not None else [None] * (R - 1))
+    kcs = [kc] + [kc.clone() for _ in range(R - 1)]
+    vcs = [vc] + ([vc.clone() for _ in range(R - 1)] if vc is not None else [None] * (R - 1))
+    log(f"writer {args.workload} format: {T} tokens, {algo} bytes/call, replicas {R}")
+
+    def call(i):
+        pkv.reshape_and_cache(prob, keys[i % R], vals[i % R], slots, ks, vs, kcs[i % R],
+                              vcs[i % R])
+
+    for i in range(args.warmup):
+        call(i)
+    torch.cuda.synchronize()
+    K = args.steps
+    if args.eager:
+        def replay():
+            for i in range(K):
+                call(i)
+    else:
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            call(0)
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            for i in range(K):
+                call(i)
+        replay = g.replay
+        replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / K
+    gbs = algo / (ms * 1e-3) / 1e9
+    log(f"writer {ms * 1e3:.2f} us per call ({gbs:.0f} GB/s)")
+    print(json.dumps({
+        "metric": "cache-writer GB/s (FP16 rows read + codes written, % of MI355X HBM peak)",
+        "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": round(ms, 6), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": f"reshape_and_cache, {T} tokens in the {args.workload} cache "
+                               f"format ({p.cache_dtype}, k {p.k_quant}, v {p.v_quant}, "
+                               f"{p.layout})",
+                   "cold_cache_replicas": R,
+                   "timing": ("K eager launches" if args.eager else
+                              "one HIP-graph replay of K calls") + ", HIP events"},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "traffic": None, "kernel": "cache_write_kernel",
+                     "kernel_us": round(ms * 1e3, 3), "algorithmic_bytes_per_launch": algo},
+    }), flush=True)
+    return 0
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -122,6 +225,11 @@ def main():
     ap.add_argument("--eager", action="store_true",
                     help="launch every step eagerly instead of from a HIP graph (for "
                          "per-dispatch hardware counters)")
+    ap.add_argument("--op", default="decode", choices=["decode", "write"],
+                    help="decode: the decode step (default); write: the quantise-on-write "
+                         "cache writer (reshape_and_cache) on the workload's cache format")
+    ap.add_argument("--write-tokens", type=int, default=16384,
+                    help="new tokens per writer call (--op write)")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="only run 4 plain device-to-device copies of this many bytes and exit "
                          "(calibrates the HBM byte counters)")
@@ -152,6 +260,8 @@ def main():
         log(f"copied {args.copy_bytes} bytes 4 times")
         return 0
     pkv.load()
+    if args.op == "write":
+        return bench_write(args, dev)
 
     log(f"generating {args.workload}")
     inp = workloads.workload(args.workload)

@@ -250,6 +250,44 @@ pkv_status split_combine(const pkv_problem* problem, const pkv_geometry* geometr
                          const void* workspace, size_t workspace_bytes, const float* head_sink,
                          void* out, float* lse_out, void* stream);
 
+/*
+ * reshape_and_cache -- quantise-on-write of new K/V rows into the paged cache
+ * (ONNX Runtime PR #29912, "Summary of Changes": ReshapeAndCache writes each
+ * new token at the slot its slot_mapping entry names, quantised with
+ * k_scale / v_scale at the granularity k_quant / v_quant give).
+ *
+ * For token t with slot = slot_mapping[t] in [0, num_pool_blocks *
+ * block_size), KV head g and channel d:
+ *   v    = float32(x[t, g, d]) / scale[g, d]   (FP32, correctly rounded;
+ *          scale = 1 for PKV_QUANT_NONE, scale[0] per tensor)
+ *   code = INT8: clamp(round-half-even(v), -128, 127)
+ *          FP8 e4m3fn: the nearest finite value, ties to the even code,
+ *            saturating at +-448, the sign kept on a rounding to zero
+ *          FP16: v rounded to half (round-half-even)
+ *   key_cache[slot / block_size][slot % block_size][g][d] = code (and the
+ *   same for value / value_cache).  A token whose slot lies outside the
+ *   pool is skipped (nothing is written for it).  LATENT: one cache; `value`
+ *   and `value_cache` must be NULL and the row is quantised with k_scale.
+ *
+ * Layouts (row-major, device memory):
+ *   key          [num_tokens, num_kv_heads, head_size]     float16
+ *   value        [num_tokens, num_kv_heads, v_head_size]   float16
+ *   slot_mapping [num_tokens]                              int64
+ *   caches and scales as for paged_decode_attention.
+ * Only the problem's num_kv_heads, head_size, v_head_size, block_size,
+ * num_pool_blocks, cache_dtype, k_quant, v_quant and layout are used.
+ * Alignment: key, value and the caches 16-byte aligned, head_size and
+ * v_head_size multiples of 8 (as everywhere), per-channel scales 16-byte
+ * and per-tensor scales 4-byte aligned, slot_mapping 8-byte aligned.
+ * Two tokens mapped to one slot race (the result is one of them).  One
+ * launch on `stream` (none when num_tokens == 0); no allocation, memset or
+ * synchronisation; graph safe.  Errors as for paged_decode_attention.
+ */
+pkv_status reshape_and_cache(const pkv_problem* problem, int32_t num_tokens, const void* key,
+                             const void* value, const int64_t* slot_mapping,
+                             const float* k_scale, const float* v_scale, void* key_cache,
+                             void* value_cache, void* stream);
+
 /* Static string for a status code. */
 const char* pkv_status_string(pkv_status status);
 

@@ -57,7 +57,7 @@ class PkvError(RuntimeError):
 _lib = None
 
 SYMBOLS = ("split_geometry", "paged_decode_attention", "paged_decode_partials", "split_combine",
-           "pkv_status_string", "pkv_last_error")
+           "reshape_and_cache", "pkv_status_string", "pkv_last_error")
 
 
 def load():
@@ -83,6 +83,8 @@ def load():
     lib.split_combine.restype = ctypes.c_int
     lib.split_combine.argtypes = [ctypes.POINTER(Problem), ctypes.POINTER(Geometry), P,
                                   ctypes.c_size_t, P, P, P, P]
+    lib.reshape_and_cache.restype = ctypes.c_int
+    lib.reshape_and_cache.argtypes = [ctypes.POINTER(Problem), ctypes.c_int32] + [P] * 8
     lib.pkv_status_string.restype = ctypes.c_char_p
     lib.pkv_status_string.argtypes = [ctypes.c_int]
     lib.pkv_last_error.restype = ctypes.c_char_p
@@ -169,6 +171,17 @@ def split_combine(problem: Problem, geometry: Geometry, workspace, head_sink, ou
     _check(load().split_combine(ctypes.byref(problem), ctypes.byref(geometry), _ptr(workspace),
                                 int(wb), _ptr(head_sink), _ptr(out), _ptr(lse_out),
                                 _stream(stream)))
+
+
+def reshape_and_cache(problem: Problem, key, value, slot_mapping, k_scale, v_scale, key_cache,
+                      value_cache, num_tokens=None, stream=None):
+    """Quantise the new rows `key` / `value` ([T, kv_heads, dim] float16) into
+    the caches at the slots `slot_mapping` (int64 [T]) names; slots outside
+    the pool are skipped.  LATENT: `value` and `value_cache` are None."""
+    t = int(key.shape[0]) if num_tokens is None else int(num_tokens)
+    _check(load().reshape_and_cache(ctypes.byref(problem), t, _ptr(key), _ptr(value),
+                                    _ptr(slot_mapping), _ptr(k_scale), _ptr(v_scale),
+                                    _ptr(key_cache), _ptr(value_cache), _stream(stream)))
 
 
 def workspace_for(geometry: Geometry, device="cuda"):

@@ -19,7 +19,7 @@ BUILD_DIR = os.path.join(HERE, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["pkv_kernels.hip", "pkv_api.cpp"]
+SOURCES = ["pkv_kernels.hip", "pkv_cache_write.hip", "pkv_api.cpp"]
 COMMON = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -279,6 +279,56 @@ pkv::CombineArgs combine_args(const pkv_problem& p, const pkv_geometry& g, const
   return c;
 }
 
+// Static checks for the quantise-on-write call: only the cache description
+// matters (no rows, heads or block tables are involved).
+pkv_status check_write(const pkv_problem* p, int32_t tokens, const void* key, const void* value,
+                       const int64_t* slots, const float* ks, const float* vs, const void* kc,
+                       const void* vc) {
+  if (!p) return fail(PKV_EINVAL, "problem is NULL");
+  if (tokens < 0) return fail(PKV_EINVAL, "num_tokens < 0");
+  if (p->num_kv_heads <= 0) return fail(PKV_EINVAL, "num_kv_heads must be positive");
+  if (p->head_size <= 0 || p->v_head_size <= 0 || p->head_size % 8 || p->v_head_size % 8)
+    return fail(PKV_EINVAL, "head sizes must be positive multiples of 8");
+  if (p->block_size <= 0 || p->num_pool_blocks <= 0)
+    return fail(PKV_EINVAL, "block_size and num_pool_blocks must be positive");
+  if (p->cache_dtype != PKV_F16 && p->cache_dtype != PKV_I8 && p->cache_dtype != PKV_FP8_E4M3FN)
+    return fail(PKV_EINVAL, "cache_dtype must be PKV_F16, PKV_I8 or PKV_FP8_E4M3FN");
+  if (p->layout != PKV_SEPARATE && p->layout != PKV_LATENT)
+    return fail(PKV_EINVAL, "layout must be PKV_SEPARATE or PKV_LATENT");
+  const bool latent = p->layout == PKV_LATENT;
+  for (int q : {p->k_quant, p->v_quant})
+    if (q < PKV_QUANT_NONE || q > PKV_QUANT_PER_CHANNEL)
+      return fail(PKV_EINVAL, "quant must be NONE, PER_TENSOR or PER_CHANNEL");
+  if (p->cache_dtype != PKV_F16) {
+    if (p->k_quant == PKV_QUANT_NONE)
+      return fail(PKV_EINVAL, "a quantised cache needs k_quant PER_TENSOR or PER_CHANNEL");
+    if (!latent && p->v_quant == PKV_QUANT_NONE)
+      return fail(PKV_EINVAL, "a quantised cache needs v_quant PER_TENSOR or PER_CHANNEL");
+  }
+  const int64_t chunks = (int64_t)p->num_kv_heads * ((p->head_size + (latent ? 0 : p->v_head_size)) / 8);
+  if (chunks > INT32_MAX || (chunks * tokens + 255) / 256 > INT32_MAX)
+    return fail(PKV_EUNSUPPORTED, "num_tokens * num_kv_heads * head sizes is too large");
+  if (tokens > 0) {
+    if (!key) return fail(PKV_EINVAL, "key is NULL");
+    if (!slots) return fail(PKV_EINVAL, "slot_mapping is NULL");
+  }
+  if (!kc) return fail(PKV_EINVAL, "key_cache is NULL");
+  if (latent && (value || vc))
+    return fail(PKV_EINVAL, "value and value_cache must be NULL for the LATENT layout");
+  if (!latent && !vc) return fail(PKV_EINVAL, "value_cache is NULL");
+  if (!latent && tokens > 0 && !value) return fail(PKV_EINVAL, "value is NULL");
+  if (p->k_quant != PKV_QUANT_NONE && !ks) return fail(PKV_EINVAL, "k_scale is NULL");
+  if (!latent && p->v_quant != PKV_QUANT_NONE && !vs) return fail(PKV_EINVAL, "v_scale is NULL");
+  for (const void* q : {key, value, kc, vc})
+    if (q && !aligned(q, 16)) return fail(PKV_EALIGN, "a K/V array or cache is not 16-byte aligned");
+  if (slots && !aligned(slots, 8)) return fail(PKV_EALIGN, "slot_mapping is not 8-byte aligned");
+  if (ks && !aligned(ks, p->k_quant == PKV_QUANT_PER_CHANNEL ? 16 : 4))
+    return fail(PKV_EALIGN, "k_scale is not aligned");
+  if (!latent && vs && !aligned(vs, p->v_quant == PKV_QUANT_PER_CHANNEL ? 16 : 4))
+    return fail(PKV_EALIGN, "v_scale is not aligned");
+  return PKV_OK;
+}
+
 pkv_status hip_status(hipError_t e, const char* what) {
   if (e == hipSuccess) return PKV_OK;
   return fail(PKV_EHIP, "%s: %s", what, hipGetErrorString(e));
@@ -471,6 +521,38 @@ pkv_status paged_decode_attention(const pkv_problem* problem, const pkv_geometry
   const pkv::CombineArgs c = combine_args(*problem, *geometry, workspace, head_sink, out, lse_out);
   return hip_status(pkv::launch_combine(problem->v_head_size, problem->out_dtype, c, s),
                     "combine kernel launch");
+}
+
+pkv_status reshape_and_cache(const pkv_problem* problem, int32_t num_tokens, const void* key,
+                             const void* value, const int64_t* slot_mapping,
+                             const float* k_scale, const float* v_scale, void* key_cache,
+                             void* value_cache, void* stream) {
+  g_err[0] = 0;
+  const pkv_status st = check_write(problem, num_tokens, key, value, slot_mapping, k_scale,
+                                    v_scale, key_cache, value_cache);
+  if (st != PKV_OK) return st;
+  if (num_tokens == 0) return PKV_OK;
+  const pkv_problem& p = *problem;
+  const bool latent = p.layout == PKV_LATENT;
+  pkv::WriteArgs a{};
+  a.key = static_cast<const uint16_t*>(key);
+  a.value = latent ? nullptr : static_cast<const uint16_t*>(value);
+  a.slot_mapping = slot_mapping;
+  a.k_scale = k_scale;
+  a.v_scale = latent ? nullptr : v_scale;
+  a.key_cache = static_cast<uint8_t*>(key_cache);
+  a.value_cache = latent ? nullptr : static_cast<uint8_t*>(value_cache);
+  a.n_slots = (int64_t)p.num_pool_blocks * p.block_size;
+  a.tokens = num_tokens;
+  a.kv_heads = p.num_kv_heads;
+  a.head_size = p.head_size;
+  a.v_head_size = p.v_head_size;
+  a.chunks_k = p.head_size / 8;
+  a.chunks_v = latent ? 0 : p.v_head_size / 8;
+  a.k_quant = p.k_quant;
+  a.v_quant = latent ? PKV_QUANT_NONE : p.v_quant;
+  return hip_status(pkv::launch_cache_write(p.cache_dtype, a, static_cast<hipStream_t>(stream)),
+                    "cache write launch");
 }
 
 }  // extern "C"

@@ -44,6 +44,23 @@ struct CombineArgs {
   int skip_empty;               // read only splits with a nonzero weight
 };
 
+// Everything the quantise-on-write kernel reads.  One thread per 8 channels:
+// chunks_k = head_size / 8 key chunks, then chunks_v value chunks (0 for
+// LATENT) per (token, KV head).
+struct WriteArgs {
+  const uint16_t* key;          // [tokens, kv_heads, head_size] fp16 bits
+  const uint16_t* value;        // [tokens, kv_heads, v_head_size] or null
+  const int64_t* slot_mapping;  // [tokens]
+  const float* k_scale;
+  const float* v_scale;
+  uint8_t* key_cache;
+  uint8_t* value_cache;
+  int64_t n_slots;              // num_pool_blocks * block_size
+  int tokens, kv_heads, head_size, v_head_size;
+  int chunks_k, chunks_v;
+  int k_quant, v_quant;
+};
+
 // Kernel variant key.
 struct Variant {
   int cache_dtype;  // pkv_dtype
@@ -54,8 +71,8 @@ struct Variant {
 
 constexpr int kWaves = 4;          // waves per split-kernel CTA
 constexpr int kThreads = 64 * kWaves;
-// latent kernel with one-byte codes: 8 waves per CTA (one CTA per CU, two
-// waves per SIMD); with FP16 codes its LDS stage only fits 4 waves
+// waves per CTA of the latent kernel with one-byte codes (with FP16 codes it
+// uses kWaves)
 constexpr int kLatentWaves = 4;
 inline int threads_of(const Variant& v) {
   return (v.latent && v.cache_dtype != PKV_F16) ? 64 * kLatentWaves : kThreads;
@@ -69,5 +86,6 @@ bool variant_supported(const Variant& v);
 hipError_t launch_split(const Variant& v, const SplitArgs& a, hipStream_t stream);
 hipError_t launch_combine(int v_head_size, int out_dtype, const CombineArgs& a, hipStream_t stream);
 hipError_t split_occupancy(const Variant& v, int* ctas_per_cu);
+hipError_t launch_cache_write(int cache_dtype, const WriteArgs& a, hipStream_t stream);
 
 }  // namespace pkv

@@ -219,3 +219,53 @@ def test_automatic_chunk_floor_bounds_partial_traffic():
     # an explicit floor is kept as given
     g = pkv.split_geometry(lat, num_cus=256, ctas_per_cu=2, min_chunk=64)
     assert g.min_chunk == 64
+
+
+def _write(p, tokens=4, **over):
+    a = dict(key=A, value=A, slot_mapping=A, k_scale=A, v_scale=A, key_cache=A, value_cache=A)
+    a.update(over)
+    pkv.reshape_and_cache(p, a["key"], a["value"], a["slot_mapping"], a["k_scale"],
+                          a["v_scale"], a["key_cache"], a["value_cache"], num_tokens=tokens,
+                          stream=0)
+
+
+@pytest.mark.parametrize("over,status,what", [
+    (dict(key=None), 1, "key"), (dict(value=None), 1, "value"),
+    (dict(slot_mapping=None), 1, "slot_mapping"), (dict(key_cache=None), 1, "key_cache"),
+    (dict(value_cache=None), 1, "value_cache"), (dict(k_scale=None), 1, "k_scale"),
+    (dict(v_scale=None), 1, "v_scale"), (dict(key=A + 8), 3, "aligned"),
+    (dict(value_cache=A + 4), 3, "aligned"), (dict(slot_mapping=A + 4), 3, "slot_mapping"),
+    (dict(k_scale=A + 4), 3, "k_scale"), (dict(tokens=-1), 1, "num_tokens"),
+])
+def test_cache_write_validation(over, status, what):
+    p = pkv.make_problem(1, 8, 2, 128, 128, 16, 8, 32, cache_dtype="i8", k_quant="channel",
+                         v_quant="tensor")
+    tokens = over.pop("tokens", 4)
+    with pytest.raises(pkv.PkvError) as e:
+        _write(p, tokens, **over)
+    assert e.value.status == status and what in str(e.value)
+
+
+def test_cache_write_problem_rules():
+    # head sizes must be multiples of 8; a quantised cache needs scales of some kind
+    p = pkv.make_problem(1, 8, 2, 100, 128, 16, 8, 32)
+    with pytest.raises(pkv.PkvError) as e:
+        _write(p, k_scale=None, v_scale=None)
+    assert e.value.status == 1 and "multiples of 8" in str(e.value)
+    p = pkv.make_problem(1, 8, 2, 128, 128, 16, 8, 32, cache_dtype="fp8", k_quant="tensor")
+    with pytest.raises(pkv.PkvError) as e:
+        _write(p)
+    assert e.value.status == 1 and "v_quant" in str(e.value)
+    # latent: one cache, no value rows
+    p = pkv.make_problem(1, 16, 1, 576, 512, 64, 8, 32, cache_dtype="fp8", k_quant="tensor",
+                         layout="latent")
+    with pytest.raises(pkv.PkvError) as e:
+        _write(p, v_scale=None, value_cache=None)
+    assert e.value.status == 1 and "LATENT" in str(e.value)
+    with pytest.raises(pkv.PkvError) as e:
+        _write(p, value=None, v_scale=None)
+    assert e.value.status == 1 and "LATENT" in str(e.value)
+    # zero tokens with every array valid enqueues nothing and succeeds, also
+    # without key / value / slot arrays
+    p = pkv.make_problem(1, 8, 2, 128, 128, 16, 8, 32)
+    _write(p, tokens=0, key=None, value=None, slot_mapping=None, k_scale=None, v_scale=None)

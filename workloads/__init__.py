@@ -381,3 +381,72 @@ WORKLOADS = {"C1": c1, "C2": c2, "C3": c3, "C4": c4, "C5": c5}
 def workload(name: str, seed: Optional[int] = None) -> Inputs:
     f = WORKLOADS[name]
     return f() if seed is None else f(seed)
+
+
+# ----------------------------------------------------------------------------
+# new rows for the quantise-on-write cache writer
+# ----------------------------------------------------------------------------
+
+@dataclass
+class NewTokens:
+    """Fresh K/V rows, their slots and the scales to quantise them with."""
+    key: np.ndarray                      # float16 [T, kv_heads, head_size]
+    value: Optional[np.ndarray]          # float16 [T, kv_heads, v_head_size] or None
+    slot_mapping: np.ndarray             # int64 [T]
+    k_scale: Optional[np.ndarray]        # float32 [1] or [kv_heads, head_size]
+    v_scale: Optional[np.ndarray]
+
+
+def _writer_scale(rng, quant, kv_heads, dim, code_max, x_std):
+    """Scales that put about 4 standard deviations at the top code, so a few
+    values saturate; per channel they vary by a factor of 4."""
+    if quant == "none":
+        return None
+    base = 4.0 * x_std / code_max
+    if quant == "tensor":
+        return np.array([base * rng.uniform(0.7, 1.4)], dtype=np.float32)
+    return (base * rng.uniform(0.5, 2.0, size=(kv_heads, dim))).astype(np.float32)
+
+
+def new_tokens(problem: Problem, num_tokens: int, seed: int, *, x_std: float = 1.0,
+               skip_fraction: float = 0.1, slots=None) -> NewTokens:
+    """Draw ``num_tokens`` new rows ~ N(0, x_std^2) as float16 (a tenth of
+    them ten times larger, to reach saturation), per-tensor or per-channel
+    scales, and a slot mapping: distinct random slots of the pool, with
+    ``skip_fraction`` of the tokens given -1 or a slot past the pool (the
+    writer skips those).  ``slots`` replaces the drawn mapping."""
+    p = problem
+    rng = np.random.default_rng(seed)
+    T, KVH = int(num_tokens), p.kv_heads
+    latent = p.layout == "latent"
+
+    def rows(dim):
+        x = rng.standard_normal((T, KVH, dim), dtype=np.float32) * x_std
+        big = rng.random((T, KVH, dim)) < 0.1
+        return np.where(big, x * 10.0, x).astype(np.float16)
+
+    key = rows(p.head_size)
+    value = None if latent else rows(p.v_head_size)
+    code_max = {"f16": 1.0, "i8": 127.0, "fp8": 448.0}[p.cache_dtype]
+    k_scale = _writer_scale(rng, p.k_quant, KVH, p.head_size, code_max, x_std)
+    v_scale = None if latent else _writer_scale(rng, p.v_quant, KVH, p.v_head_size, code_max, x_std)
+    n_slots = p.num_pool_blocks * p.block_size
+    if slots is None:
+        if T > n_slots:
+            raise ValueError("more new tokens than pool slots")
+        slot_mapping = rng.choice(n_slots, size=T, replace=False).astype(np.int64)
+        skip = rng.random(T) < skip_fraction
+        past = rng.integers(n_slots, 2 * n_slots, size=T)
+        slot_mapping = np.where(skip, np.where(rng.random(T) < 0.5, -1, past), slot_mapping)
+    else:
+        slot_mapping = np.asarray(slots, dtype=np.int64)
+    return NewTokens(key=key, value=value, slot_mapping=slot_mapping.astype(np.int64),
+                     k_scale=k_scale, v_scale=v_scale)
+
+
+def every_fp16_value() -> np.ndarray:
+    """All binary16 values except NaN (both zeros and both infinities
+    included), in bit-pattern order."""
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    v = bits.view(np.float16)
+    return v[~np.isnan(v)]
