@@ -54,7 +54,8 @@ def _load():
     lib.oracle_paged_decode.restype = ctypes.c_int
     P = ctypes.c_void_p
     I = ctypes.c_int
-    lib.oracle_paged_decode.argtypes = [I] * 13 + [P] * 9 + [ctypes.c_double, P, I, I, P, I, P, P]
+    lib.oracle_paged_decode.argtypes = ([I] * 13 + [P] * 9 + [ctypes.c_double, P, ctypes.c_double]
+                                        + [I, I, I, P, I, P, P])
     _lib = lib
     return lib
 
@@ -106,7 +107,8 @@ def paged_decode(inp, chunk: int = 0, threads: int | None = None, rows=None):
         p.max_blocks_per_row, p.num_pool_blocks, p.max_candidates, DTYPE_CODE[p.cache_dtype],
         QUANT_CODE[p.k_quant], QUANT_CODE[p.v_quant], 1 if p.layout == "latent" else 0,
         _ptr(q), _ptr(kc), _ptr(vc), _ptr(bt), _ptr(sl), _ptr(cand), _ptr(ncand), _ptr(ks),
-        _ptr(vs), float(inp.softmax_scale), _ptr(sink), int(chunk), int(threads), _ptr(sub),
+        _ptr(vs), float(inp.softmax_scale), _ptr(sink), float(p.softcap), int(p.sliding_window),
+        int(chunk), int(threads), _ptr(sub),
         0 if sub is None else len(sub), _ptr(out), _ptr(lse))
     if rc != 0:
         raise RuntimeError(f"oracle_paged_decode failed with code {rc}")

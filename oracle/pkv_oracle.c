@@ -10,11 +10,13 @@
  *
  *   For row r and query head h with KV head g = h / (heads / kv_heads):
  *     len  = clamp(seq_lens[r], 0, max_blocks_per_row * block_size)
- *     T    = [0, len)                                   (dense rows), or
+ *     lo   = max(0, len - W) with a sliding window of W > 0 tokens, else 0
+ *     T    = [lo, len)                                  (dense rows), or
  *            candidates[r][0 : num_candidates[r]] in list order, keeping only
- *            entries in [0, len)                          (gathered rows)
+ *            entries in [lo, len)                         (gathered rows)
  *     slot(t) = block_table[r][t / block_size] * block_size + t % block_size
  *     x_t  = softmax_scale * sum_d Q[r,h,d] * Khat[slot(t), g, d]
+ *            then, with a soft cap c > 0:  x_t <- c * tanh(x_t / c)
  *     m    = max_t x_t ;  w_t = exp(x_t - m) ;  l = sum_t w_t ;  lse = m + log l
  *     O[c] = sum_t w_t * Vhat[slot(t), g, c] / l
  *     with a head sink s_h:  O <- O / (1 + exp(s_h - lse))
@@ -38,7 +40,9 @@
  *     block table and block size, k_scale / v_scale with PER_TENSOR or
  *     PER_CHANNEL granularity, the float8e4m3fn cache type, the LATENT layout
  *     (V = leading v_head_size channels of the row that supplies K), and the
- *     exact post-hoc head-sink rescale 1 / (1 + exp(s_h - lse)).
+ *     exact post-hoc head-sink rescale 1 / (1 + exp(s_h - lse)); its paged
+ *     decode kernel also supports a logit soft cap and a sliding window, whose
+ *     arithmetic the page does not spell out (readings below).
  *   - The split-and-merge variant (oracle_paged_decode with chunk > 0) follows
  *     the flash-decoding partial/merge description of PR #33707 section 2 and
  *     onnx-genai PR #1350 "Summary"; it exists to pin the invariant that
@@ -49,7 +53,10 @@
  *   scales of shape [kv_heads, head_size]; symmetric dequantisation
  *   x = code * scale; OCP e4m3fn decoding (bias 7, no infinities, S.1111.111
  *   is NaN); head_sink per query head, in scaled-logit units; seq_len clamped
- *   to the block-table capacity; duplicate candidates count twice.
+ *   to the block-table capacity; duplicate candidates count twice; the soft
+ *   cap acts on the scaled logit, x <- c tanh(x / c); a window of W tokens
+ *   keeps the W most recent positions [len - W, len) of the row (the decode
+ *   query is the token at position len - 1).
  *
  * Numerics: every decoded input is exact in double; sums run in logical token
  * order with plain loops, so permuting the physical blocks cannot change a
@@ -129,6 +136,8 @@ typedef struct {
   const float* k_scale;
   const float* v_scale;
   double softmax_scale;
+  double softcap;
+  int window;
   const float* head_sink;
   int chunk;
   /* outputs */
@@ -176,16 +185,18 @@ static int token_list(const oracle_job* J, int r, int32_t* T, int64_t* slots) {
   int64_t len = J->seq_lens[r];
   if (len < 0) len = 0;
   if (len > cap) len = cap;
+  int64_t lo = 0;
+  if (J->window > 0 && len > J->window) lo = len - J->window;
   int n = 0;
   if (J->max_candidates == 0) {
-    for (int64_t t = 0; t < len; ++t) T[n++] = (int32_t)t;
+    for (int64_t t = lo; t < len; ++t) T[n++] = (int32_t)t;
   } else {
     int nc = J->num_candidates[r];
     if (nc < 0) nc = 0;
     if (nc > J->max_candidates) nc = J->max_candidates;
     for (int j = 0; j < nc; ++j) {
       int32_t c = J->candidates[(size_t)r * J->max_candidates + j];
-      if (c >= 0 && c < len) T[n++] = c;
+      if (c >= lo && c < len) T[n++] = c;
     }
   }
   for (int i = 0; i < n; ++i) {
@@ -219,6 +230,7 @@ static int run_unit(oracle_job* J, int r, int g, int32_t* T, int64_t* slots, dou
       double dot = 0.0;
       for (int d = 0; d < D; ++d) dot += oracle_f16_to_f64(q[d]) * khat(J, slots[i], g, d);
       x[i] = J->softmax_scale * dot;
+      if (J->softcap > 0.0) x[i] = J->softcap * tanh(x[i] / J->softcap);
     }
     double M, L;
     for (int c = 0; c < VD; ++c) o[c] = 0.0;
@@ -318,6 +330,8 @@ static void* worker(void* arg) {
  *   k_scale      [1] or [kv_heads, head_size]; v_scale [1] or
  *                [kv_heads, v_head_size]; unused for quant NONE
  *   head_sink    [heads] or NULL
+ *   softcap      > 0: logit soft cap c; 0: none
+ *   window       > 0: sliding window of that many tokens; 0: none
  *   chunk        0: monolithic softmax; > 0: split into chunks of `chunk`
  *                list entries, partials merged in FP64
  *   row_subset   optional list of rows to evaluate (others untouched)
@@ -333,13 +347,14 @@ int oracle_paged_decode(int rows, int heads, int kv_heads, int head_size, int v_
                         const int32_t* seq_lens, const int32_t* candidates,
                         const int32_t* num_candidates, const float* k_scale,
                         const float* v_scale, double softmax_scale, const float* head_sink,
-                        int chunk, int num_threads, const int32_t* row_subset,
+                        double softcap, int window, int chunk, int num_threads, const int32_t* row_subset,
                         int n_row_subset, double* out, double* lse) {
   if (rows < 0 || heads <= 0 || kv_heads <= 0 || heads % kv_heads != 0 || head_size <= 0 ||
       v_head_size <= 0 || block_size <= 0 || max_blocks_per_row < 0 || max_candidates < 0)
     return -3;
   if (latent && v_head_size > head_size) return -3;
   if (cache_dtype < OR_F16 || cache_dtype > OR_FP8E4M3) return -3;
+  if (!(softcap >= 0.0) || window < 0) return -3;
   oracle_job J;
   memset(&J, 0, sizeof(J));
   J.rows = rows; J.heads = heads; J.kv_heads = kv_heads; J.head_size = head_size;
@@ -351,7 +366,7 @@ int oracle_paged_decode(int rows, int heads, int kv_heads, int head_size, int v_
   J.block_table = block_table; J.seq_lens = seq_lens; J.candidates = candidates;
   J.num_candidates = num_candidates; J.k_scale = k_scale;
   J.v_scale = latent ? k_scale : v_scale; J.softmax_scale = softmax_scale;
-  J.head_sink = head_sink; J.chunk = chunk; J.out = out; J.lse = lse;
+  J.head_sink = head_sink; J.softcap = softcap; J.window = window; J.chunk = chunk; J.out = out; J.lse = lse;
 
   int nrows_eval = row_subset ? n_row_subset : rows;
   int32_t* units = (int32_t*)malloc(sizeof(int32_t) * (size_t)(nrows_eval * kv_heads + 1));

@@ -466,3 +466,143 @@ def test_reshape_and_cache_writes_only_mapped_slots():
                 assert np.array_equal(v2[b, o], exp_v.astype(np.int8))
             else:
                 assert np.array_equal(k2[b, o], kc[b, o]) and np.array_equal(v2[b, o], vc[b, o])
+
+
+# ---------------------------------------------------------------------------
+# sliding window and logit soft cap (ONNX Runtime PR #29912, "Summary of
+# Changes": the paged decode kernel supports both; readings: a window of W
+# keeps positions [len - W, len), the cap maps a scaled logit x to
+# c tanh(x / c))
+# ---------------------------------------------------------------------------
+
+def _windowed(inp, W):
+    return Inputs(**{**inp.__dict__, "problem": replace(inp.problem, sliding_window=W)})
+
+
+def test_window_wider_than_the_row_changes_nothing():
+    inp = _small(cache="i8", sink=True, lens=(45, 1, 64, 17))
+    o0, l0 = oracle.paged_decode(inp)
+    o1, l1 = oracle.paged_decode(_windowed(inp, 64))
+    assert np.array_equal(o0, o1) and np.array_equal(l0, l1)
+
+
+def test_window_of_one_returns_the_newest_value():
+    inp = _windowed(_small(lens=(45, 1, 64, 17)), 1)
+    o, l = oracle.paged_decode(inp)
+    for r in range(4):
+        t = int(inp.seq_lens[r]) - 1
+        blk = inp.block_table[r, t // 16]
+        for h in range(4):
+            assert np.array_equal(o[r, h], inp.value_cache[blk, t % 16, h // 2].astype(np.float64))
+
+
+def test_window_equals_the_row_started_at_its_first_block():
+    """A window that starts on a block boundary attends exactly what a row
+    whose table begins at that block attends: outputs are bitwise equal."""
+    inp = _small(cache="i8", sink=True, lens=(64, 48, 40, 33))
+    W = 32
+    win = _windowed(inp, W)
+    o1, l1 = oracle.paged_decode(win)
+    lens = inp.seq_lens.astype(np.int64)
+    for r in range(4):
+        lo = max(0, int(lens[r]) - W)
+        if lo % 16:
+            continue
+        bt = np.full_like(inp.block_table, inp.block_table[r, 0])
+        nb = inp.block_table.shape[1] - lo // 16
+        bt[:, :nb] = inp.block_table[r, lo // 16:]
+        shifted = Inputs(**{**inp.__dict__, "block_table": bt,
+                            "seq_lens": np.full_like(inp.seq_lens, int(lens[r]) - lo)})
+        o2, l2 = oracle.paged_decode(shifted, rows=[r])
+        assert np.array_equal(o1[r], o2[r]) and np.array_equal(l1[r], l2[r])
+
+
+def test_window_ignores_positions_before_it():
+    """Poisoning every position before the window (NaN values, extreme keys)
+    leaves the output bitwise unchanged."""
+    inp = _small(cache="f16", lens=(64, 50, 37, 20))
+    W = 19
+    o0, l0 = oracle.paged_decode(_windowed(inp, W))
+    k2, v2 = inp.key_cache.copy(), inp.value_cache.copy()
+    for r in range(4):
+        for t in range(max(0, int(inp.seq_lens[r]) - W)):
+            blk = inp.block_table[r, t // 16]
+            k2[blk, t % 16] = np.float16(60000.0)
+            v2[blk, t % 16] = np.float16(np.nan)
+    bad = Inputs(**{**inp.__dict__, "key_cache": k2, "value_cache": v2,
+                    "problem": replace(inp.problem, sliding_window=W)})
+    o1, l1 = oracle.paged_decode(bad)
+    assert np.array_equal(o0, o1) and np.array_equal(l0, l1)
+
+
+def test_window_on_candidate_lists_filters_them():
+    """Gathered rows: the window equals dropping the candidates before it."""
+    p = Problem(rows=2, heads=4, kv_heads=1, head_size=16, v_head_size=16, block_size=16,
+                max_blocks_per_row=8, num_pool_blocks=0, max_candidates=12, cache_dtype="i8",
+                k_quant="channel", v_quant="tensor")
+    rng = np.random.default_rng(5)
+    cand = np.stack([rng.permutation(128)[:12] for _ in range(2)]).astype(np.int32)
+    inp = workloads.make_inputs(p, 5, [128, 100], candidates=cand)
+    W = 40
+    o1, l1 = oracle.paged_decode(_windowed(inp, W))
+    c2 = cand.copy()
+    n2 = np.zeros(2, np.int32)
+    for r in range(2):
+        lo = int(inp.seq_lens[r]) - W
+        keep = [c for c in cand[r] if lo <= c < int(inp.seq_lens[r])]
+        c2[r, :len(keep)] = keep
+        c2[r, len(keep):] = -1
+        n2[r] = len(keep)
+    o2, l2 = oracle.paged_decode(Inputs(**{**inp.__dict__, "candidates": c2, "num_candidates": n2}))
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+def _two_token_case(x0, x1, cap):
+    """One head, two tokens whose scaled logits are x0 and x1 (set by one-hot
+    keys against a query of ones, softmax scale 1); value channel 0 is 1 on
+    token 0 and 0 on token 1, so O[0] is token 0's weight."""
+    D = 16
+    p = Problem(rows=1, heads=1, kv_heads=1, head_size=D, v_head_size=D, block_size=16,
+                max_blocks_per_row=1, num_pool_blocks=1, cache_dtype="f16", out_dtype="f32",
+                softcap=cap)
+    q = np.zeros((1, 1, D), dtype=np.float16)
+    q[0, 0, :2] = 1.0
+    k = np.zeros((1, 16, 1, D), dtype=np.float16)
+    v = np.zeros((1, 16, 1, D), dtype=np.float16)
+    k[0, 0, 0, 0], k[0, 1, 0, 1] = x0, x1
+    v[0, 0, 0, 0] = 1.0
+    return Inputs(problem=p, query=q, key_cache=k, value_cache=v,
+                  block_table=np.zeros((1, 1), np.int32), seq_lens=np.array([2], np.int32),
+                  softmax_scale=1.0)
+
+
+def test_softcap_closed_form():
+    """Cap 2 with logits 2 atanh(1/2) and 0 gives capped logits exactly 1 and
+    0: token 0's weight is 1 / (1 + e^-1) and lse = log(e + 1).  Capping
+    before the scale, or c tanh(x) without the division, gives other values."""
+    x0 = float(np.float16(2.0 * math.atanh(0.5)))
+    inp = _two_token_case(x0, 0.0, 2.0)
+    o, l = oracle.paged_decode(inp)
+    y = 2.0 * math.tanh(x0 / 2.0)  # x0 is the FP16-rounded logit: y is within 1e-3 of 1
+    assert abs(y - 1.0) < 1e-3
+    assert o[0, 0, 0] == pytest.approx(1.0 / (1.0 + math.exp(-y)), rel=1e-14)
+    assert l[0, 0] == pytest.approx(math.log(math.exp(y) + 1.0), rel=1e-14)
+    assert o[0, 0, 0] == pytest.approx(1.0 / (1.0 + math.exp(-1.0)), abs=3e-4)
+
+
+def test_softcap_bounds_and_limits():
+    # a huge logit is held under the cap: lse < cap + log 2
+    o, l = oracle.paged_decode(_two_token_case(60000.0, -60000.0, 30.0))
+    assert l[0, 0] < 30.0 + math.log(2.0)
+    assert o[0, 0, 0] == pytest.approx(1.0 / (1.0 + math.exp(-60.0)), rel=1e-12)
+    # a cap far above the logits changes them by at most x^3 / (3 c^2)
+    inp = _small(cache="i8", lens=(45, 1, 64, 17))
+    o0, l0 = oracle.paged_decode(inp)
+    capped = Inputs(**{**inp.__dict__, "problem": replace(inp.problem, softcap=1e4)})
+    o1, l1 = oracle.paged_decode(capped)
+    np.testing.assert_allclose(o1, o0, rtol=0, atol=1e-6)
+    np.testing.assert_allclose(l1, l0, rtol=0, atol=1e-6)
+    # and a binding cap does change them
+    tight = Inputs(**{**inp.__dict__, "problem": replace(inp.problem, softcap=0.5)})
+    o2, _ = oracle.paged_decode(tight)
+    assert np.abs(o2 - o0).max() > 1e-3

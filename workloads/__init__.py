@@ -72,6 +72,8 @@ class Problem:
     v_quant: str = "none"
     layout: str = "separate"
     out_dtype: str = "f16"
+    sliding_window: int = 0  # > 0: attend to the last sliding_window positions only
+    softcap: float = 0.0     # > 0: logits x -> softcap * tanh(x / softcap)
 
     @property
     def group(self) -> int:
@@ -122,13 +124,14 @@ def live_token_counts(inp: Inputs) -> np.ndarray:
     candidates; clamped context length for dense rows)."""
     p = inp.problem
     lens = np.clip(inp.seq_lens.astype(np.int64), 0, p.capacity)
+    lo = np.maximum(lens - p.sliding_window, 0) if p.sliding_window > 0 else np.zeros_like(lens)
     if p.max_candidates == 0:
-        return lens
+        return lens - lo
     out = np.zeros(p.rows, dtype=np.int64)
     for r in range(p.rows):
         nc = int(np.clip(inp.num_candidates[r], 0, p.max_candidates))
         c = inp.candidates[r, :nc].astype(np.int64)
-        out[r] = int(((c >= 0) & (c < lens[r])).sum())
+        out[r] = int(((c >= lo[r]) & (c < lens[r])).sum())
     return out
 
 

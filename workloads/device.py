@@ -32,7 +32,8 @@ def problem_kwargs(p, out_dtype: Optional[str] = None) -> dict:
                 max_blocks_per_row=p.max_blocks_per_row, num_pool_blocks=p.num_pool_blocks,
                 max_candidates=p.max_candidates, cache_dtype=p.cache_dtype,
                 out_dtype=out_dtype or p.out_dtype, k_quant=p.k_quant,
-                v_quant="none" if p.layout == "latent" else p.v_quant, layout=p.layout)
+                v_quant="none" if p.layout == "latent" else p.v_quant, layout=p.layout,
+                sliding_window=p.sliding_window, softcap=p.softcap)
 
 
 def _t(a, device):
