@@ -17,6 +17,9 @@
  *     entries, a finite non-negative softmax scale, the split-K partial
  *     (running maximum in natural-log units, running sum, value-scaled
  *     accumulator) and its merge, a statically sized workspace;
+ *   - ONNX Runtime PR #29912, "Summary of Changes", paged decode kernel:
+ *     the logit soft cap and the sliding window (their arithmetic is not
+ *     spelled out there; the definition below takes the usual forms);
  *   - onnx-genai PR #1350 "Summary": the split count comes from the static
  *     capacity and the row count so that about one occupancy wave of CTAs
  *     runs, never from live lengths.
@@ -24,12 +27,14 @@
  * Definition.  For row r (one decode query token) and query head h with KV
  * head g = h / (num_heads / num_kv_heads):
  *   len    = clamp(seq_lens[r], 0, max_blocks_per_row * block_size)
- *   T      = [0, len) for dense rows (max_candidates == 0); for gathered rows
+ *   lo     = max(0, len - sliding_window) when sliding_window > 0, else 0
+ *   T      = [lo, len) for dense rows (max_candidates == 0); for gathered rows
  *            the list candidates[r][0 : clamp(num_candidates[r], 0,
- *            max_candidates)] in list order, keeping entries in [0, len)
+ *            max_candidates)] in list order, keeping entries in [lo, len)
  *            (duplicates count twice)
  *   slot t = block_table[r][t / block_size] * block_size + t % block_size
- *   x_t    = softmax_scale * sum_d Q[r,h,d] * K^[slot t, g, d]
+ *   x_t    = softmax_scale * sum_d Q[r,h,d] * K^[slot t, g, d], then with
+ *            softcap c > 0:  x_t <- c * tanh(x_t / c)
  *   O      = sum_t exp(x_t - m) V^[slot t, g, :] / sum_t exp(x_t - m),
  *            m = max_t x_t;  lse = m + log sum_t exp(x_t - m)
  *   sink   O <- O / (1 + exp(head_sink[h] - lse)) when head_sink != NULL
@@ -68,7 +73,7 @@
  * offending argument (thread-local).  Device-resident data cannot be checked
  * without a synchronisation, so it has defined semantics instead: seq_lens
  * are clamped to [0, capacity]; num_candidates to [0, max_candidates];
- * candidate indices outside [0, len) are skipped; a block-table entry
+ * candidate indices outside [lo, len) are skipped; a block-table entry
  * outside [0, num_pool_blocks) makes its tokens contribute nothing (they are
  * never read); block-table entries past the live length are never read.
  *
@@ -120,6 +125,8 @@ typedef struct {
   int32_t k_quant;         /* pkv_quant */
   int32_t v_quant;         /* pkv_quant; LATENT: ignored (V uses the K scales) */
   int32_t layout;          /* pkv_layout */
+  int32_t sliding_window;  /* > 0: attend to the last sliding_window positions only; 0: all */
+  float softcap;           /* > 0: logit soft cap c, x <- c tanh(x / c); 0: none */
 } pkv_problem;
 
 /* Optional knobs of split_geometry (pass NULL for all defaults; 0 = default). */
@@ -149,8 +156,10 @@ typedef struct {
  * split_geometry -- choose the split count S from static shapes only.
  *
  * units = num_rows * num_kv_heads * ceil(group / 16);
- * cap   = max_blocks_per_row * block_size (dense) or max_candidates
- *         (gathered);  resident = num_cus * ctas_per_cu.
+ * cap   = max_blocks_per_row * block_size (dense; with a sliding window W
+ *         at most W + 15, the positions from the window start rounded down
+ *         to a multiple of 16) or max_candidates (gathered);
+ *         resident = num_cus * ctas_per_cu.
  * Dense rows (onnx-genai PR #1350 "Summary"; target = waves * resident):
  *   S = min(ceil(target / units), ceil(cap / min_chunk), max_splits)
  *   (see below for the factor 4 of the live-balanced mode)

@@ -30,7 +30,7 @@ class Problem(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "num_rows", "num_heads", "num_kv_heads", "head_size", "v_head_size", "block_size",
         "max_blocks_per_row", "num_pool_blocks", "max_candidates", "cache_dtype", "out_dtype",
-        "k_quant", "v_quant", "layout")]
+        "k_quant", "v_quant", "layout", "sliding_window")] + [("softcap", ctypes.c_float)]
 
 
 class GeometryOpts(ctypes.Structure):
@@ -100,7 +100,8 @@ def _check(status: int):
 
 def make_problem(num_rows, num_heads, num_kv_heads, head_size, v_head_size, block_size,
                  max_blocks_per_row, num_pool_blocks, max_candidates=0, cache_dtype="f16",
-                 out_dtype="f16", k_quant="none", v_quant="none", layout="separate") -> Problem:
+                 out_dtype="f16", k_quant="none", v_quant="none", layout="separate",
+                 sliding_window=0, softcap=0.0) -> Problem:
     def code(table, v):
         return table[v] if isinstance(v, str) else int(v)
 
@@ -108,7 +109,7 @@ def make_problem(num_rows, num_heads, num_kv_heads, head_size, v_head_size, bloc
                    int(v_head_size), int(block_size), int(max_blocks_per_row),
                    int(num_pool_blocks), int(max_candidates), code(DTYPES, cache_dtype),
                    code(DTYPES, out_dtype), code(QUANTS, k_quant), code(QUANTS, v_quant),
-                   code(LAYOUTS, layout))
+                   code(LAYOUTS, layout), int(sliding_window), float(softcap))
 
 
 def split_geometry(problem: Problem, num_cus=0, ctas_per_cu=0, splits_override=0, min_chunk=0,

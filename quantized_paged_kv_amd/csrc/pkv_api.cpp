@@ -40,7 +40,18 @@ pkv::Variant variant_of(const pkv_problem& p) {
   v.v_head_size = p.v_head_size;
   v.latent = p.layout == PKV_LATENT;
   v.gathered = p.max_candidates > 0;
+  v.ext = p.sliding_window > 0 || p.softcap > 0.0f;
   return v;
+}
+
+// Most positions one row can have: the candidate-list capacity (gathered
+// rows), else the block-table capacity -- with a sliding window of W
+// tokens at most W + 15, since a row's range starts at the window start
+// rounded down to a multiple of 16 (so tiles never straddle a block).
+int64_t positions_cap(const pkv_problem& p) {
+  if (p.max_candidates > 0) return p.max_candidates;
+  const int64_t cap = (int64_t)p.max_blocks_per_row * p.block_size;
+  return p.sliding_window > 0 ? std::min<int64_t>(cap, (int64_t)p.sliding_window + 15) : cap;
 }
 
 // Static checks of the problem description.
@@ -78,6 +89,9 @@ pkv_status check_problem(const pkv_problem* p) {
   if ((int64_t)p->num_rows * p->num_kv_heads * ceil_div(p->num_heads / p->num_kv_heads, 16) * 64 >
       INT32_MAX)
     return fail(PKV_EUNSUPPORTED, "num_rows * num_kv_heads * ceil(group / 16) is too large");
+  if (p->sliding_window < 0) return fail(PKV_EINVAL, "sliding_window < 0");
+  if (!(p->softcap >= 0.0f) || !std::isfinite(p->softcap))
+    return fail(PKV_EINVAL, "softcap must be finite and >= 0");
   if (p->layout == PKV_LATENT && p->v_head_size > p->head_size)
     return fail(PKV_EINVAL, "LATENT needs v_head_size <= head_size");
   if (!pkv::variant_supported(variant_of(*p)))
@@ -114,7 +128,7 @@ std::unordered_map<int, DeviceInfo> g_dev;
 
 uint64_t variant_key(const pkv::Variant& v) {
   return ((uint64_t)v.cache_dtype << 40) | ((uint64_t)v.head_size << 24) |
-         ((uint64_t)v.v_head_size << 8) | (v.latent << 1) | v.gathered;
+         ((uint64_t)v.v_head_size << 8) | (v.ext << 2) | (v.latent << 1) | v.gathered;
 }
 
 pkv_status device_numbers(const pkv::Variant& v, int* cus, int* occ) {
@@ -250,8 +264,7 @@ pkv::SplitArgs split_args(const pkv_problem& p, const pkv_geometry& g, const Ptr
   a.target_ctas = g.target_ctas;
   a.grid_ctas = g.grid_x;
   {
-    const int64_t cap_pos = p.max_candidates > 0 ? p.max_candidates
-                                                 : (int64_t)p.max_blocks_per_row * p.block_size;
+    const int64_t cap_pos = positions_cap(p);
     a.static_chunk = std::max<int>(g.min_chunk,
                                    (int)((((cap_pos + g.num_splits - 1) / g.num_splits) + 15) / 16 * 16));
   }
@@ -259,6 +272,9 @@ pkv::SplitArgs split_args(const pkv_problem& p, const pkv_geometry& g, const Ptr
   a.v_quant = latent ? p.k_quant : p.v_quant;
   a.v_scale_stride = latent ? p.head_size : p.v_head_size;
   a.score_scale = softmax_scale;
+  a.window = p.sliding_window;
+  a.softcap = p.softcap;
+  a.inv_softcap = p.softcap > 0.0f ? 1.0f / p.softcap : 0.0f;
   a.v_mult = 1.0f / 16.0f;  // the kernels' probability tiles carry a factor 16
   return a;
 }
@@ -375,7 +391,7 @@ pkv_status split_geometry(const pkv_problem* problem, const pkv_geometry_opts* o
   const int group = p.num_heads / p.num_kv_heads;
   const int head_blocks = ceil_div(group, 16);
   const int64_t units = std::max<int64_t>(1, (int64_t)p.num_rows * p.num_kv_heads * head_blocks);
-  const int64_t cap = gathered ? p.max_candidates : (int64_t)p.max_blocks_per_row * p.block_size;
+  const int64_t cap = positions_cap(p);
 
   // The device balances chunk sizes across rows from the live lengths when
   // the row count is modest (each CTA reads every row's length).

@@ -31,6 +31,9 @@ struct SplitArgs {
   int k_quant, v_quant;         // pkv_quant
   int v_scale_stride;           // per-channel V scale row stride (VD, or D for LATENT)
   float score_scale;            // softmax_scale (codes enter the MFMAs at their value)
+  float softcap;                // > 0: scores x -> softcap * tanh(x / softcap)
+  float inv_softcap;            // 1 / softcap (0 without a cap)
+  int window;                   // > 0: sliding window (positions [len - window, len))
   float v_mult;                 // factor applied with the value scale (1)
 };
 
@@ -67,6 +70,7 @@ struct Variant {
   int head_size, v_head_size;
   int latent;
   int gathered;
+  int ext;          // a sliding window or a soft cap is set
 };
 
 constexpr int kWaves = 4;          // waves per split-kernel CTA

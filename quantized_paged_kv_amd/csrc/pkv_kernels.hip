@@ -286,7 +286,44 @@ __device__ __forceinline__ int row_positions(const SplitArgs& a, int i, int cap)
 struct Work {
   int r, u, split, n_row, npos, len;
   int g, hb, h0, nh;  // KV head, head block, first query head, query heads (<= 16)
+  // Sliding window: the row attends tokens [lo, len).  Dense rows number
+  // their positions from base = lo rounded down to a multiple of 16 (token =
+  // base + position, so tiles never straddle a block); positions before
+  // lo - base are masked.  Without a window lo = base = 0.
+  int lo, base;
 };
+
+// The kernels are instantiated twice: EXT = false for problems without a
+// sliding window or soft cap (none of the code below is compiled in), and
+// EXT = true for the rest.
+
+// First token of a row's sliding window (0 without one).
+template <bool EXT>
+__device__ __forceinline__ int window_lo(const SplitArgs& a, int len) {
+  if constexpr (!EXT) return 0;
+  return (a.window > 0 && len > a.window) ? len - a.window : 0;
+}
+
+// Logit soft cap x -> c tanh(x / c) (identity without one).
+template <bool EXT>
+__device__ __forceinline__ float soft_cap(const SplitArgs& a, float x) {
+  if constexpr (!EXT) return x;
+  return a.softcap > 0.0f ? a.softcap * tanhf(x * a.inv_softcap) : x;
+}
+
+// Scaled (and capped) scores of a 4-token MFMA column; the cap is one
+// uniform branch around all four, taken before the masking select.
+template <bool EXT>
+__device__ __forceinline__ void scaled_scores(const SplitArgs& a, const f32x4& acc, float (&x)[4]) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) x[q] = acc[q] * a.score_scale;
+  if constexpr (EXT) {
+    if (a.softcap > 0.0f) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) x[q] = a.softcap * tanhf(x[q] * a.inv_softcap);
+    }
+  }
+}
 
 // Locate this CTA's work item (device-side, graph safe).  Returns false for
 // a padding CTA past the last item.
@@ -298,7 +335,7 @@ struct Work {
 // CTA launches only to find nothing to do (except trailing padding).  All
 // row lengths are read in one round trip (lane i holds rows i + 64 k; the
 // loads are issued unconditionally, from clamped indices).
-template <bool GATHER>
+template <bool GATHER, bool EXT>
 __device__ __forceinline__ bool locate_balanced(const SplitArgs& a, int lane, Work& w) {
   const int S = a.num_splits;
   const int units_row = a.kv_heads * a.head_blocks;
@@ -317,6 +354,16 @@ __device__ __forceinline__ bool locate_balanced(const SplitArgs& a, int lane, Wo
   for (int i = 0; i < NR; ++i) {
     const int rr = lane + 64 * i;
     np[i] = rr < a.rows ? min(max(raw[i], 0), GATHER ? a.max_candidates : cap) : 0;
+  }
+  // dense rows with a sliding window: positions from the window start
+  // rounded down to 16 (one uniform branch; np holds the clamped lengths)
+  if constexpr (!GATHER && EXT)
+    if (a.window > 0) {
+#pragma unroll
+      for (int i = 0; i < NR; ++i) np[i] -= window_lo<EXT>(a, np[i]) & ~15;
+    }
+#pragma unroll
+  for (int i = 0; i < NR; ++i) {
     tot += np[i];
   }
 #pragma unroll
@@ -325,7 +372,7 @@ __device__ __forceinline__ bool locate_balanced(const SplitArgs& a, int lane, Wo
   const int64_t cl = (work + a.target_ctas - 1) / a.target_ctas;
   const int cgl = max(a.min_chunk, (int)min<int64_t>(((cl + 15) >> 4) << 4, 1 << 30));
   int base = 0;
-  int r = -1, u = 0, split = 0, n_row = 0, npos = 0;
+  int r = -1, u = 0, split = 0, n_row = 0, npos = 0, rlen = 0;
 #pragma unroll
   for (int i = 0; i < NR; ++i) {
     if (64 * i >= a.rows) break;
@@ -347,6 +394,7 @@ __device__ __forceinline__ bool locate_balanced(const SplitArgs& a, int lane, Wo
       const int off = c - base - __shfl(excl, src);
       n_row = __shfl(n, src);
       npos = __shfl(np[i], src);
+      if constexpr (!GATHER && EXT) rlen = min(max(__shfl(raw[i], src), 0), cap);
       u = off / n_row;
       split = off - u * n_row;
       break;
@@ -360,7 +408,11 @@ __device__ __forceinline__ bool locate_balanced(const SplitArgs& a, int lane, Wo
   w.split = __builtin_amdgcn_readfirstlane(split);
   w.n_row = __builtin_amdgcn_readfirstlane(n_row);
   w.npos = __builtin_amdgcn_readfirstlane(npos);
-  w.len = w.npos;
+  // dense rows: the clamped length (npos without a window); gathered rows
+  // get theirs in finish_item
+  w.len = (!GATHER && EXT) ? __builtin_amdgcn_readfirstlane(rlen) : w.npos;
+  w.lo = GATHER ? 0 : window_lo<EXT>(a, w.len);
+  w.base = GATHER ? 0 : (w.lo & ~15);
   return true;
 }
 
@@ -376,6 +428,7 @@ __device__ __forceinline__ void static_item(const SplitArgs& a, Work& w) {
   w.split = rem - w.u * S;
   w.n_row = S;
   w.npos = w.len = 0;
+  w.lo = w.base = 0;
 }
 
 __device__ __forceinline__ void unit_heads(const SplitArgs& a, Work& w) {
@@ -388,12 +441,21 @@ __device__ __forceinline__ void unit_heads(const SplitArgs& a, Work& w) {
 // Clamped lengths from the raw values read in the prologue: raw_npos (static
 // mode: seq_len, or num_candidates of gathered rows) and raw_len (gathered
 // rows: seq_len, which bounds the valid candidate indices).
-template <bool GATHER>
+template <bool GATHER, bool EXT>
 __device__ __forceinline__ void finish_item(const SplitArgs& a, Work& w, bool balanced,
                                             int raw_npos, int raw_len) {
   const int cap = a.max_blocks_per_row * a.block_size;
-  if (!balanced) w.npos = min(max(raw_npos, 0), GATHER ? a.max_candidates : cap);
-  w.len = GATHER ? min(max(raw_len, 0), cap) : w.npos;
+  if constexpr (GATHER) {
+    if (!balanced) w.npos = min(max(raw_npos, 0), a.max_candidates);
+    w.len = min(max(raw_len, 0), cap);
+    w.lo = window_lo<EXT>(a, w.len);
+    w.base = 0;
+  } else {
+    if (!balanced) w.len = min(max(raw_npos, 0), cap);
+    w.lo = window_lo<EXT>(a, w.len);
+    w.base = w.lo & ~15;
+    w.npos = w.len - w.base;
+  }
 }
 
 // Position range [p0, p1) of the work item; publishes the empty partials
@@ -405,6 +467,10 @@ __device__ __forceinline__ void finish_item(const SplitArgs& a, Work& w, bool ba
 __device__ __forceinline__ int static_p0(const SplitArgs& a, int split) {
   return split * a.static_chunk;
 }
+
+// Added to a buffer offset, puts the access past any descriptor's range, so
+// the load returns zeros without a memory request.
+constexpr uint32_t kPastDescriptor = 0x40000000u;
 
 // s_waitcnt immediate (gfx9 encoding): vmcnt(0), expcnt and lgkmcnt not waited.
 constexpr int kWaitVmcnt0 = 0x0F70;
@@ -424,7 +490,7 @@ __device__ __forceinline__ int split_p0(const SplitArgs& a, const Work& w) {
 // load that misses would wait behind the streaming K/V traffic).
 struct WaveBlocks {
   const int32_t* bt_row;
-  int p0, wave, nw, win, ids;  // nw: waves of the CTA
+  int p0, wave, nw, win, ids;  // p0: token of the wave's tile 0 position; nw: waves of the CTA
 
   __device__ __forceinline__ void load(const SplitArgs& a, int w_idx, int lane) {
     win = w_idx;
@@ -572,7 +638,7 @@ __device__ __forceinline__ float v_scale_of(const SplitArgs& a, const Scales& sc
 // (natural-log units), and the FP32 accumulator is multiplied by the value
 // scale after the W wave states are merged in a fixed order.  `scratch`
 // holds W * (VD + 2) floats of LDS; every thread of the CTA calls this.
-template <int CT, int D, int VD, bool LATENT, bool GATHER, int W>
+template <int CT, int D, int VD, bool LATENT, bool GATHER, int W, bool EXT>
 __device__ __forceinline__ void exact_partial(const SplitArgs& a, const Work& wk, int p0, int p1,
                                            const Scales& sc, const float* s_vs, float* scratch) {
   constexpr int NT = 64 * W;
@@ -605,11 +671,9 @@ __device__ __forceinline__ void exact_partial(const SplitArgs& a, const Work& wk
 #pragma unroll
     for (int k = 0; k < KV; ++k) acc[k] = 0.0f;
     for (int pos = p0 + wave; pos < p1; pos += W) {
-      int t = pos;
-      if constexpr (GATHER) {
-        t = a.candidates[(size_t)wk.r * a.max_candidates + pos];
-        if (t < 0 || t >= wk.len) continue;
-      }
+      int t = wk.base + pos;
+      if constexpr (GATHER) t = a.candidates[(size_t)wk.r * a.max_candidates + pos];
+      if (t < wk.lo || t >= wk.len) continue;
       const int blk = bt_row[t >> a.log2_block];
       if (blk < 0 || blk >= a.num_pool_blocks) continue;
       const size_t slot = ((size_t)blk << a.log2_block) + (t & (a.block_size - 1));
@@ -620,7 +684,7 @@ __device__ __forceinline__ void exact_partial(const SplitArgs& a, const Work& wk
         const int d = lane + 64 * k;
         if (d < D) part += qf[k] * code_at<CT>(krow, d);
       }
-      const float sv = wave_sum(part) * a.score_scale;
+      const float sv = soft_cap<EXT>(a, wave_sum(part) * a.score_scale);
       if (sv > m) {
         const float alpha = (m == kNegInf) ? 0.0f : expf(m - sv);
         l *= alpha;
@@ -701,7 +765,7 @@ __device__ __forceinline__ float value_bound(const SplitArgs& a, const Scales& s
   return vm * code_bound<CT>();
 }
 
-template <int CT, int D, int VD, bool LATENT, bool GATHER>
+template <int CT, int D, int VD, bool LATENT, bool GATHER, bool EXT>
 __global__ void __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(SplitCfg<CT, D, VD, LATENT, GATHER>::MIN_WAVES)))
 split_kernel(const SplitArgs a) {
@@ -723,7 +787,7 @@ split_kernel(const SplitArgs a) {
   Work wk;
   int raw_npos = 0, raw_len = 0;
   if (balanced) {
-    if (!locate_balanced<GATHER>(a, lane, wk)) return;  // padding CTA
+    if (!locate_balanced<GATHER, EXT>(a, lane, wk)) return;  // padding CTA
   } else {
     static_item(a, wk);
     raw_npos = GATHER ? uniform_load(a.num_candidates, wk.r) : uniform_load(a.seq_lens, wk.r);
@@ -740,13 +804,23 @@ split_kernel(const SplitArgs a) {
   uint4 qraw[QPT];
   float4 ksc[QPT][2];
   const int32_t* bt_row = a.block_table + (size_t)r * a.max_blocks_per_row;
-  // block ids of this wave's first 64 tiles (static mode: before the length)
-  WaveBlocks wb{bt_row, split_p0(a, wk), wave, W, 0, 0};
+  // block ids of this wave's first 64 tiles (static mode: before the length;
+  // read again below when a sliding window moves the row's first token)
+  WaveBlocks wb{bt_row, wk.base + split_p0(a, wk), wave, W, 0, 0};
   if constexpr (!GATHER) wb.load(a, 0, lane);
   q_issue<C::NKS, C::EB, D>(a, wk, qraw, ksc);
   const Scales sc = load_scales<VD>(a, g);
-  finish_item<GATHER>(a, wk, balanced, raw_npos, raw_len);
+  finish_item<GATHER, EXT>(a, wk, balanced, raw_npos, raw_len);
   const int len = wk.len;
+  if constexpr (!GATHER && EXT)
+    if (!balanced && wk.base > 0) {
+      wb.p0 = wk.base + split_p0(a, wk);
+      wb.load(a, 0, lane);
+    }
+  // positions of the row before its window start (first tile only)
+  const int skip = wk.lo - wk.base;
+  const int base = wk.base;
+  const int lo = wk.lo;
 
   int p0, p1;
   if (!split_range(a, wk, p0, p1)) return;
@@ -776,27 +850,42 @@ split_kernel(const SplitArgs a) {
         blk = wb.of(a, t, lane);
         bv = blk >= 0 && blk < a.num_pool_blocks;
       }
-      const int64_t s0 = bv ? ((int64_t)blk << a.log2_block) + (tp & (a.block_size - 1)) : 0;
+      const int64_t s0 =
+          bv ? ((int64_t)blk << a.log2_block) + ((base + tp) & (a.block_size - 1)) : 0;
       // the descriptors cover the tile's valid rows only: rows past the end
       // (and a whole tile with an invalid block) read as zeros, so the V
-      // operands need no mask
+      // operands need no mask; rows before a sliding window's start (first
+      // tile only) get an offset past the descriptor and read as zeros too
       const uint32_t nv = bv ? (uint32_t)min(16, p1 - tp) : 0u;
       const auto krs = make_rsrc(a.key_cache + s0 * tok_k, nv * tok_k);
 #pragma unroll
       for (int s = 0; s < C::NKL; ++s) buffer_bytes<16>(krs, koff + 64 * s, 0, &T.k[4 * s]);
       const uint8_t* vbase = LATENT ? a.key_cache : a.value_cache;
       const auto vrs = make_rsrc(vbase + s0 * tok_v, nv * tok_v);
+      if (EXT && tp < skip) {
+        // the row's first tile under a sliding window: its rows before the
+        // window start are masked and their V reads go past the descriptor
+        const int sk = skip - tp;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        buffer_bytes<C::VSEG>(vrs, voff + (uint32_t)q * tok_v, 0, T.v[q]);
-        vm |= (4 * lj + q < (int)nv) ? (1u << q) : 0u;
+        for (int q = 0; q < 4; ++q) {
+          const int row = 4 * lj + q;
+          const uint32_t past = row < sk ? kPastDescriptor : 0u;
+          buffer_bytes<C::VSEG>(vrs, voff + (uint32_t)q * tok_v + past, 0, T.v[q]);
+          vm |= (row < (int)nv && row >= sk) ? (1u << q) : 0u;
+        }
+      } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          buffer_bytes<C::VSEG>(vrs, voff + (uint32_t)q * tok_v, 0, T.v[q]);
+          vm |= (4 * lj + q < (int)nv) ? (1u << q) : 0u;
+        }
       }
     } else {
       // gathered rows: per-token slots; invalid entries (and tiles past the
       // end) read token slot 0 of the pool and are masked
       const int pos = tp + li;
       int c = (t < ntiles && pos < p1) ? a.candidates[(size_t)r * a.max_candidates + pos] : -1;
-      bool v = c >= 0 && c < len;
+      bool v = c >= lo && c < len;
       int blk = v ? bt_row[c >> a.log2_block] : 0;
       v = v && blk >= 0 && blk < a.num_pool_blocks;
       const int64_t s = v ? ((int64_t)blk << a.log2_block) + (c & (a.block_size - 1)) : 0;
@@ -855,10 +944,11 @@ split_kernel(const SplitArgs a) {
       }
     }
     float sc[4];
+    scaled_scores<EXT>(a, sacc, sc);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const bool valid = (T.vmask >> q) & 1u;
-      sc[q] = valid ? sacc[q] * a.score_scale : kNegInf;
+      sc[q] = valid ? sc[q] : kNegInf;
       smin = fminf(smin, valid ? sc[q] : __builtin_inff());
     }
     float mt = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
@@ -994,7 +1084,7 @@ split_kernel(const SplitArgs a) {
     for (int w = 0; w < W; ++w) deep_any |= s_flag[w] != 0;
     const bool armed = deep_any && value_bound<CT, VD>(a, sc, s_vs, lane) * (float)(p1 - p0) >= kTailArm;
     if (s_flag[W] != 0 || (deep_any && armed)) {
-      exact_partial<CT, D, VD, LATENT, GATHER, W>(a, wk, p0, p1, sc, s_vs, sm_acc);
+      exact_partial<CT, D, VD, LATENT, GATHER, W, EXT>(a, wk, p0, p1, sc, s_vs, sm_acc);
       return;
     }
   }
@@ -1055,9 +1145,8 @@ split_kernel(const SplitArgs a) {
 // ---- the latent (absorbed-MLA) kernel -------------------------------------
 //
 // One cache row per token supplies K (all 576 channels) and V (its first 512
-// channels).  A CTA of W waves (8 for one-byte codes: one CTA per CU, two
-// waves per SIMD; 4 for FP16 codes, whose stage is twice as large) walks its
-// position range in rounds of W 16-token tiles.  In round rd wave w
+// channels).  A CTA of W = 4 waves walks its position range in rounds of W
+// 16-token tiles.  In round rd wave w
 //   * computes the scores S^T = K Q'^T of tile w from its K registers
 //     (fetched two rounds ahead) and publishes them in LDS,
 //   * copies the tile's raw codes into the round's LDS stage (64 rows),
@@ -1113,7 +1202,7 @@ __device__ __forceinline__ half4 lds_read_tr16(const uint8_t* p) {
       half4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)p));
 }
 
-template <int CT, bool GATHER>
+template <int CT, bool GATHER, bool EXT>
 __global__ void __launch_bounds__((LatCfg<CT, GATHER>::NT))
 __attribute__((amdgpu_waves_per_eu(LatCfg<CT, GATHER>::MIN_WAVES)))
 latent_kernel(const SplitArgs a) {
@@ -1133,7 +1222,7 @@ latent_kernel(const SplitArgs a) {
   Work wk;
   int raw_npos = 0, raw_len = 0;
   if (balanced) {
-    if (!locate_balanced<GATHER>(a, lane, wk)) return;  // padding CTA
+    if (!locate_balanced<GATHER, EXT>(a, lane, wk)) return;  // padding CTA
   } else {
     static_item(a, wk);
     raw_npos = GATHER ? uniform_load(a.num_candidates, wk.r) : uniform_load(a.seq_lens, wk.r);
@@ -1152,13 +1241,22 @@ latent_kernel(const SplitArgs a) {
   uint4 qraw[QPT];
   float4 ksc[QPT][2];
   const int32_t* bt_row = a.block_table + (size_t)r * a.max_blocks_per_row;
-  // block ids of this wave's first 64 tiles (static mode: before the length)
-  WaveBlocks wb{bt_row, split_p0(a, wk), wave, W, 0, 0};
+  // block ids of this wave's first 64 tiles (static mode: before the length;
+  // read again below when a sliding window moves the row's first token)
+  WaveBlocks wb{bt_row, wk.base + split_p0(a, wk), wave, W, 0, 0};
   if constexpr (!GATHER) wb.load(a, 0, lane);
   q_issue<C::NKS, C::EB, D, QPT, NT>(a, wk, qraw, ksc);
   const Scales sc = load_scales<C::VD, NT>(a, g);
-  finish_item<GATHER>(a, wk, balanced, raw_npos, raw_len);
+  finish_item<GATHER, EXT>(a, wk, balanced, raw_npos, raw_len);
   const int len = wk.len;
+  if constexpr (!GATHER && EXT)
+    if (!balanced && wk.base > 0) {
+      wb.p0 = wk.base + split_p0(a, wk);
+      wb.load(a, 0, lane);
+    }
+  const int skip = wk.lo - wk.base;  // positions of the row before its window start
+  const int base = wk.base;
+  const int lo = wk.lo;
 
   int p0, p1;
   if (!split_range<NT>(a, wk, p0, p1)) return;
@@ -1178,24 +1276,39 @@ latent_kernel(const SplitArgs a) {
         const int tp = p0 + 16 * t;
         const int blk = wb.of(a, t, lane);
         bv = blk >= 0 && blk < a.num_pool_blocks;
-        s0 = bv ? ((int64_t)blk << a.log2_block) + (tp & (a.block_size - 1)) : 0;
+        s0 = bv ? ((int64_t)blk << a.log2_block) + ((base + tp) & (a.block_size - 1)) : 0;
       }
       // the descriptor covers the tile's valid rows only: rows past the end
-      // (and a whole tile with an invalid block) read as zeros
+      // (and a whole tile with an invalid block) read as zeros; so do rows
+      // before a sliding window's start (an offset past the descriptor)
       const int tp = p0 + 16 * t;
       const uint32_t nv = bv ? (uint32_t)min(16, p1 - tp) : 0u;
       const auto rs = make_rsrc(a.key_cache + s0 * tok, nv * tok);
+      if (EXT && tp < skip) {
+        // the row's first tile under a sliding window: rows before the
+        // window start read past the descriptor (zeros) and are masked
+        const int sk = skip - tp;
+        const uint32_t past = li < sk ? kPastDescriptor : 0u;
 #pragma unroll
-      for (int s = 0; s < C::NKL; ++s) buffer_bytes<16>(rs, koff + 64 * s, 0, &T.k[4 * s]);
+        for (int s = 0; s < C::NKL; ++s) buffer_bytes<16>(rs, koff + 64 * s + past, 0, &T.k[4 * s]);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) m |= (4 * lj + q < (int)nv) ? (1u << q) : 0u;
+        for (int q = 0; q < 4; ++q) {
+          const int row = 4 * lj + q;
+          m |= (row < (int)nv && row >= sk) ? (1u << q) : 0u;
+        }
+      } else {
+#pragma unroll
+        for (int s = 0; s < C::NKL; ++s) buffer_bytes<16>(rs, koff + 64 * s, 0, &T.k[4 * s]);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) m |= (4 * lj + q < (int)nv) ? (1u << q) : 0u;
+      }
       T.row_ok = true;
     } else {
       // per-token slots; invalid entries (and tiles past the end) read token
       // slot 0 of the pool and are masked
       const int pos = p0 + 16 * t + li;
       const int c = (t < ntiles && pos < p1) ? a.candidates[(size_t)r * a.max_candidates + pos] : -1;
-      bool v = c >= 0 && c < len;
+      bool v = c >= lo && c < len;
       const int blk = v ? bt_row[c >> a.log2_block] : 0;
       v = v && blk >= 0 && blk < a.num_pool_blocks;
       const int64_t sl = v ? ((int64_t)blk << a.log2_block) + (c & (a.block_size - 1)) : 0;
@@ -1255,10 +1368,12 @@ latent_kernel(const SplitArgs a) {
       }
     }
     f32x4 scw;
+    float xs[4];
+    scaled_scores<EXT>(a, sacc, xs);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const bool valid = (T.mask >> q) & 1u;
-      scw[q] = valid ? sacc[q] * a.score_scale : kNegInf;
+      scw[q] = valid ? xs[q] : kNegInf;
       smin = fminf(smin, valid ? scw[q] : __builtin_inff());
     }
     s_sc[wave][lane] = scw;
@@ -1379,7 +1494,7 @@ latent_kernel(const SplitArgs a) {
     const bool armed = deep_any && value_bound<CT, C::VD>(a, sc, s_vs, lane) * (float)(p1 - p0) >= kTailArm;
     if (s_flag[W] != 0 || (deep_any && armed)) {
       static_assert(W * (C::VD + 2) * 4 <= C::ROUND * C::RS, "FP32-path scratch fits the stage");
-      exact_partial<CT, D, C::VD, true, GATHER, W>(a, wk, p0, p1, sc, s_vs,
+      exact_partial<CT, D, C::VD, true, GATHER, W, EXT>(a, wk, p0, p1, sc, s_vs,
                                                    reinterpret_cast<float*>(s_stage));
       return;
     }
@@ -1523,31 +1638,32 @@ combine_kernel(const CombineArgs a) {
 
 // ---- dispatch ---------------------------------------------------------------
 
-template <int CT, int D, int VD, bool LAT, bool GA>
+template <int CT, int D, int VD, bool LAT, bool GA, bool EXT>
 static hipError_t launch_one(const SplitArgs& a, hipStream_t stream) {
   dim3 grid(a.grid_ctas);
   if constexpr (LAT)
-    hipLaunchKernelGGL((latent_kernel<CT, GA>), grid, dim3(LatCfg<CT, GA>::NT), 0, stream, a);
+    hipLaunchKernelGGL((latent_kernel<CT, GA, EXT>), grid, dim3(LatCfg<CT, GA>::NT), 0, stream, a);
   else
-    hipLaunchKernelGGL((split_kernel<CT, D, VD, LAT, GA>), grid, dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((split_kernel<CT, D, VD, LAT, GA, EXT>), grid, dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 
-template <int CT, int D, int VD, bool LAT, bool GA>
+template <int CT, int D, int VD, bool LAT, bool GA, bool EXT>
 static hipError_t occupancy_one(int* n) {
   if constexpr (LAT)
-    return hipOccupancyMaxActiveBlocksPerMultiprocessor(n, latent_kernel<CT, GA>, LatCfg<CT, GA>::NT, 0);
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(n, latent_kernel<CT, GA, EXT>,
+                                                         LatCfg<CT, GA>::NT, 0);
   else
-    return hipOccupancyMaxActiveBlocksPerMultiprocessor(n, split_kernel<CT, D, VD, LAT, GA>,
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(n, split_kernel<CT, D, VD, LAT, GA, EXT>,
                                                          kThreads, 0);
 }
 
-// Calls F<CT, D, VD, LAT, GA>(args...) for the compiled variant; returns
-// hipErrorInvalidValue for a variant that is not compiled.
+// Calls F<CT, D, VD, LAT, GA, EXT>(args...) for the compiled variant;
+// returns hipErrorInvalidValue for a variant that is not compiled.
 #define PKV_FOR_VARIANT(v, CALL)                                                   \
   do {                                                                             \
     const int hs = (v).head_size, vhs = (v).v_head_size;                           \
-    const bool lat = (v).latent != 0, ga = (v).gathered != 0;                      \
+    const bool lat = (v).latent != 0, ga = (v).gathered != 0, ext = (v).ext != 0;  \
     switch ((v).cache_dtype) {                                                     \
       case PKV_F16: PKV_SHAPES(PKV_F16, CALL); break;                              \
       case PKV_I8: PKV_SHAPES(PKV_I8, CALL); break;                                \
@@ -1556,8 +1672,11 @@ static hipError_t occupancy_one(int* n) {
     }                                                                              \
   } while (0)
 
+#define PKV_EXT(CT, D, VD, LAT, GA, CALL) \
+  do { if (ext) { CALL(CT, D, VD, LAT, GA, true); } else { CALL(CT, D, VD, LAT, GA, false); } } while (0)
+
 #define PKV_GATHER(CT, D, VD, LAT, CALL) \
-  do { if (ga) { CALL(CT, D, VD, LAT, true); } else { CALL(CT, D, VD, LAT, false); } } while (0)
+  do { if (ga) { PKV_EXT(CT, D, VD, LAT, true, CALL); } else { PKV_EXT(CT, D, VD, LAT, false, CALL); } } while (0)
 
 #define PKV_SHAPES(CT, CALL)                                                       \
   do {                                                                             \
@@ -1569,7 +1688,7 @@ static hipError_t occupancy_one(int* n) {
 
 bool variant_supported(const Variant& v) {
   bool ok = false;
-#define PKV_MARK(CT, D, VD, LAT, GA) ok = true
+#define PKV_MARK(CT, D, VD, LAT, GA, EXT) ok = true
   PKV_FOR_VARIANT(v, PKV_MARK);
 #undef PKV_MARK
   return ok;
@@ -1577,7 +1696,7 @@ bool variant_supported(const Variant& v) {
 
 hipError_t launch_split(const Variant& v, const SplitArgs& a, hipStream_t stream) {
   hipError_t err = hipErrorInvalidValue;
-#define PKV_LAUNCH(CT, D, VD, LAT, GA) err = launch_one<CT, D, VD, LAT, GA>(a, stream)
+#define PKV_LAUNCH(CT, D, VD, LAT, GA, EXT) err = launch_one<CT, D, VD, LAT, GA, EXT>(a, stream)
   PKV_FOR_VARIANT(v, PKV_LAUNCH);
 #undef PKV_LAUNCH
   return err;
@@ -1585,7 +1704,7 @@ hipError_t launch_split(const Variant& v, const SplitArgs& a, hipStream_t stream
 
 hipError_t split_occupancy(const Variant& v, int* ctas_per_cu) {
   hipError_t err = hipErrorInvalidValue;
-#define PKV_OCC(CT, D, VD, LAT, GA) err = occupancy_one<CT, D, VD, LAT, GA>(ctas_per_cu)
+#define PKV_OCC(CT, D, VD, LAT, GA, EXT) err = occupancy_one<CT, D, VD, LAT, GA, EXT>(ctas_per_cu)
   PKV_FOR_VARIANT(v, PKV_OCC);
 #undef PKV_OCC
   return err;

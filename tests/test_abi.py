@@ -269,3 +269,24 @@ def test_cache_write_problem_rules():
     # without key / value / slot arrays
     p = pkv.make_problem(1, 8, 2, 128, 128, 16, 8, 32)
     _write(p, tokens=0, key=None, value=None, slot_mapping=None, k_scale=None, v_scale=None)
+
+
+def test_window_and_softcap_validation_and_geometry():
+    for kw in (dict(sliding_window=-1), dict(softcap=-1.0), dict(softcap=float("nan")),
+               dict(softcap=float("inf"))):
+        p = pkv.make_problem(2, 8, 2, 128, 128, 16, 8, 32, **kw)
+        with pytest.raises(pkv.PkvError) as e:
+            pkv.split_geometry(p, num_cus=4, ctas_per_cu=1)
+        assert e.value.status == 1
+    # a window bounds the positions a row can have (W + 15), and with it the
+    # split count and the static chunk
+    big = pkv.make_problem(1, 8, 2, 128, 128, 16, 512, 600)
+    win = pkv.make_problem(1, 8, 2, 128, 128, 16, 512, 600, sliding_window=100)
+    gb = pkv.split_geometry(big, num_cus=256, ctas_per_cu=2, min_chunk=16, balance=2)
+    gw = pkv.split_geometry(win, num_cus=256, ctas_per_cu=2, min_chunk=16, balance=2)
+    assert gb.num_splits == 64
+    assert gw.num_splits == -(-(100 + 15) // 16)
+    # a window wider than the capacity changes nothing
+    wide = pkv.make_problem(1, 8, 2, 128, 128, 16, 512, 600, sliding_window=1 << 20)
+    assert pkv.split_geometry(wide, num_cus=256, ctas_per_cu=2).as_dict() == \
+        pkv.split_geometry(big, num_cus=256, ctas_per_cu=2).as_dict()
