@@ -33,20 +33,22 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+MFMA_F16_PEAK_TFLOPS = 2500.0  # dense FP16 MFMA (the contractions run in FP16)
 METRIC = "µs/decode step and effective KV-cache GB/s (% of MI355X HBM peak)"
 KERNEL_SRC = os.path.join(ROOT, "quantized_paged_kv_amd", "csrc", "pkv_kernels.hip")
+WRITER_SRC = os.path.join(ROOT, "quantized_paged_kv_amd", "csrc", "pkv_cache_write.hip")
 
 
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def kernel_source_hash() -> str:
-    with open(KERNEL_SRC, "rb") as f:
+def kernel_source_hash(src: str = KERNEL_SRC) -> str:
+    with open(src, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def read_traffic(kernel: str, workload: str):
+def read_traffic(kernel: str, workload: str, src: str = KERNEL_SRC):
     """HBM bytes per launch of `kernel` from the committed counter summary,
     if it was taken on this kernel source; else None."""
     path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_counters.txt")
@@ -57,7 +59,7 @@ def read_traffic(kernel: str, workload: str):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             fields[k.strip()] = v.strip()
-    if fields.get("kernel_source_sha256_16") != kernel_source_hash():
+    if fields.get("kernel_source_sha256_16") != kernel_source_hash(src):
         return None
     try:
         return float(fields["hbm_bytes_per_launch"])
@@ -190,6 +192,7 @@ def bench_write(args, dev):
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / K
     gbs = algo / (ms * 1e-3) / 1e9
+    traffic = read_traffic("cache_write_kernel", f"{args.workload}_T{T}", WRITER_SRC)
     log(f"writer {ms * 1e3:.2f} us per call ({gbs:.0f} GB/s)")
     print(json.dumps({
         "metric": "cache-writer GB/s (FP16 rows read + codes written, % of MI355X HBM peak)",
@@ -204,7 +207,7 @@ def bench_write(args, dev):
                               "one HIP-graph replay of K calls") + ", HIP events"},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
-                     "traffic": None, "kernel": "cache_write_kernel",
+                     "traffic": traffic, "kernel": "cache_write_kernel",
                      "kernel_us": round(ms * 1e3, 3), "algorithmic_bytes_per_launch": algo},
     }), flush=True)
     return 0
@@ -215,7 +218,10 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="C2", choices=["C1", "C2", "C3", "C4", "C5"])
+    ap.add_argument("--workload", default="C2",
+                    choices=["C1", "C2", "C3", "C4", "C5", "P128", "P2048", "P8192"],
+                    help="C1..C5: the decode configurations; P<rows>: the dynamic-sparse "
+                         "prefill shape (rows x 2048 gathered candidates, MFMA-bound)")
     ap.add_argument("--replica-bytes", type=float, default=1.0 * (1 << 30),
                     help="cold-cache protocol: replicate the cache until this many bytes")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -352,6 +358,17 @@ def main():
 
     value = kv_bytes / (ms_step * 1e-3) / 1e9
     achieved = kv_bytes / (ms_split * 1e-3) / 1e9
+    # prefill shapes gather cache-resident rows many times over: there the
+    # contractions bound the kernel (QK^T and PV, 2 (D + VD) flops per head
+    # and attended token; the GQA group is padded to the 16-wide MFMA tile,
+    # which is not counted)
+    prefill = args.workload.startswith("P")
+    flops = 0
+    if prefill:
+        from workloads import live_token_counts
+        dims = p.head_size + p.v_head_size
+        flops = int(live_token_counts(inp).sum()) * p.heads * 2 * dims
+        tflops = flops / (ms_split * 1e-3) / 1e12
     kernel = "latent_kernel" if p.layout == "latent" else "split_kernel"
     traffic = read_traffic(kernel, args.workload)
     log(f"step {ms_step * 1e3:.2f} us ({value:.0f} GB/s), split kernel {ms_split * 1e3:.2f} us "
@@ -395,6 +412,19 @@ def main():
             "algorithmic_bytes_per_launch": kv_bytes,
         },
     }
+    if prefill:
+        line["roofline"] = {
+            "bound": "mfma",
+            "achieved": round(tflops, 2),
+            "peak": MFMA_F16_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(tflops / MFMA_F16_PEAK_TFLOPS, 4),
+            "traffic": traffic,
+            "kernel": f"{kernel} (paged_decode_partials)",
+            "kernel_us": round(ms_split * 1e3, 3),
+            "algorithmic_flops_per_launch": flops,
+            "gathered_kv_bytes_per_launch": kv_bytes,
+        }
     if not args.no_cpu_baseline:
         log("timing the oracle on the host cores")
         line["cpu_baseline"] = cpu_baseline(inp)

@@ -188,10 +188,12 @@ typedef struct {
  *   S = min(ceil(4 * target / units), ceil(cap / min_chunk), max_splits).
  * Defaults: max_splits 64.  min_chunk: 64, raised to the smallest power of
  * two c for which a split's partial P = group * (v_head_size + 2) * 4 bytes
- * is at most a quarter of the KV bytes of c positions -- unless the grid
- * would then hold fewer than a quarter of the resident CTAs
- * (units * ceil(cap / c) * 4 < resident), a latency-bound step that gains
- * from more, shorter splits.  waves: 2 in the live-balanced mode when 2 P is
+ * is at most an eighth of the KV bytes of c positions, if the grid then
+ * still gives every CU a CTA (units * ceil(cap / c) >= num_cus); else to
+ * the smallest c with P at most a quarter of them, if the grid then still
+ * holds a quarter of the resident CTAs (units * ceil(cap / c) * 4 >=
+ * resident); else kept at 64 -- a latency-bound step gains from more,
+ * shorter splits.  waves: 2 in the live-balanced mode when 2 P is
  * less than the KV bytes of min_chunk positions, else 1.
  * Returns PKV_EINVAL / PKV_EUNSUPPORTED as paged_decode_attention would, or
  * PKV_EHIP if the device query fails.  Does not touch device memory.
@@ -205,7 +207,9 @@ pkv_status split_geometry(const pkv_problem* problem, const pkv_geometry_opts* o
  * order, so results are bitwise repeatable), applies the head sink and writes
  * `out` (and `lse_out` if not NULL).  Two kernel launches on `stream`
  * (a hipStream_t; NULL = the default stream); no allocation, no memset, no
- * synchronisation.
+ * synchronisation.  With one split (geometry->num_splits == 1, e.g. many
+ * rows) the split kernel writes `out` and `lse_out` itself, bitwise what
+ * the combine would write, in one launch; the workspace is then unused.
  *
  * Numerics (ONNX Runtime PR #33707, "Numerics" and its review thread): the
  * key scale is folded into an FP16 query and the probabilities enter the PV

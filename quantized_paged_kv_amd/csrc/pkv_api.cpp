@@ -416,17 +416,24 @@ pkv_status split_geometry(const pkv_problem* problem, const pkv_geometry_opts* o
                                                              : p.head_size + p.v_head_size) *
                             (p.cache_dtype == PKV_F16 ? 2 : 1);
   // Automatic chunk floor: 64 positions, raised to the power of two that
-  // keeps a split's partial at most a quarter of the KV bytes it covers --
-  // unless the grid would then hold fewer than a quarter of the resident
-  // CTAs (a small step is bound by latency, and more, shorter splits finish
-  // sooner).
+  // keeps a split's partial (written once, read back once by the combine) at
+  // most an eighth of the KV bytes it covers while the grid still gives
+  // every CU a CTA; else at most a quarter while it still fills a quarter
+  // of the resident CTAs; else 64 (a small step is bound by latency, and
+  // more, shorter splits finish sooner).
   int min_chunk = o.min_chunk;
   if (min_chunk == 0) {
     min_chunk = 64;
-    int64_t by_partial = 16;
-    while (by_partial < ceil_div(4 * partial_bytes, row_bytes)) by_partial *= 2;
-    if (by_partial > min_chunk && units * ceil_div(cap, by_partial) * 4 >= (int64_t)cus * occ)
-      min_chunk = (int)std::min<int64_t>(by_partial, 1 << 20);
+    auto floor_for = [&](int64_t frac) {
+      int64_t c = 16;
+      while (c < ceil_div(frac * partial_bytes, row_bytes)) c *= 2;
+      return std::min<int64_t>(c, 1 << 20);
+    };
+    const int64_t c8 = floor_for(8), c4 = floor_for(4);
+    if (c8 > min_chunk && units * ceil_div(cap, c8) >= (int64_t)cus)
+      min_chunk = (int)c8;
+    else if (c4 > min_chunk && units * ceil_div(cap, c4) * 4 >= (int64_t)cus * occ)
+      min_chunk = (int)c4;
   }
   const bool cheap_partials = 2 * partial_bytes < row_bytes * min_chunk;
   const int waves = waves_req ? waves_req : (balanced && cheap_partials ? 2 : 1);
@@ -531,7 +538,17 @@ pkv_status paged_decode_attention(const pkv_problem* problem, const pkv_geometry
   if (st != PKV_OK) return st;
   if (problem->num_rows == 0) return PKV_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const pkv::SplitArgs a = split_args(*problem, *geometry, x, softmax_scale, workspace);
+  pkv::SplitArgs a = split_args(*problem, *geometry, x, softmax_scale, workspace);
+  if (geometry->num_splits == 1) {
+    // one split per row: the split kernel writes the output itself (exactly
+    // what the combine would), and there is no second launch
+    a.direct = 1;
+    a.out_f32 = problem->out_dtype == PKV_F32;
+    a.out = out;
+    a.lse_out = lse_out;
+    a.head_sink = head_sink;
+    return hip_status(pkv::launch_split(variant_of(*problem), a, s), "split kernel launch");
+  }
   st = hip_status(pkv::launch_split(variant_of(*problem), a, s), "split kernel launch");
   if (st != PKV_OK) return st;
   const pkv::CombineArgs c = combine_args(*problem, *geometry, workspace, head_sink, out, lse_out);

@@ -35,6 +35,13 @@ struct SplitArgs {
   float inv_softcap;            // 1 / softcap (0 without a cap)
   int window;                   // > 0: sliding window (positions [len - window, len))
   float v_mult;                 // factor applied with the value scale (1)
+  // direct output (S = 1): the split kernel writes what the combine would
+  // -- O = partial / l with the head sink, and lse -- and no partial
+  int direct;
+  int out_f32;                  // direct output dtype: FP32 (else FP16)
+  void* out;                    // [rows, heads, VD]
+  float* lse_out;               // [rows, heads] or null
+  const float* head_sink;       // [heads] or null
 };
 
 struct CombineArgs {

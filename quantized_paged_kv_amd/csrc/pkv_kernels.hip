@@ -468,6 +468,41 @@ __device__ __forceinline__ int static_p0(const SplitArgs& a, int split) {
   return split * a.static_chunk;
 }
 
+// ---- direct output (one split per row) -------------------------------------
+//
+// With S = 1 the combine would take the single partial unchanged: M = m,
+// L = 1 * l, O = (0 + 1 * partial) / L, lse = M + log L, then the head sink.
+// The split kernel does exactly these operations itself (same order, so
+// the result is bitwise the combine's) and writes the output.
+struct Final {
+  float f;    // factor applied to the partial (0 for an empty row)
+  float lse;
+};
+
+__device__ __forceinline__ Final final_of(const SplitArgs& a, int h, float M, float L) {
+  Final r{0.0f, kNegInf};
+  if (L > 0.0f) {
+    r.lse = M + logf(L);
+    r.f = 1.0f / L;
+    if (a.head_sink) r.f *= 1.0f / (1.0f + expf(a.head_sink[h] - r.lse));
+  }
+  return r;
+}
+
+// Four output channels c .. c+3 of (row, head) pair `pair` from partial values.
+template <int VD>
+__device__ __forceinline__ void store_final(const SplitArgs& a, size_t pair, int c, float4 part,
+                                            float f) {
+  const float4 r = make_float4(0.0f + part.x, 0.0f + part.y, 0.0f + part.z, 0.0f + part.w);
+  if (a.out_f32) {
+    *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.out) + pair * VD + c) =
+        make_float4(r.x * f, r.y * f, r.z * f, r.w * f);
+  } else {
+    const half4 hv = {(half_t)(r.x * f), (half_t)(r.y * f), (half_t)(r.z * f), (half_t)(r.w * f)};
+    *reinterpret_cast<half4*>(reinterpret_cast<half_t*>(a.out) + pair * VD + c) = hv;
+  }
+}
+
 // Added to a buffer offset, puts the access past any descriptor's range, so
 // the load returns zeros without a memory request.
 constexpr uint32_t kPastDescriptor = 0x40000000u;
@@ -511,7 +546,7 @@ struct WaveBlocks {
   }
 };
 
-template <int NT = kThreads>
+template <int VD, int NT = kThreads>
 __device__ __forceinline__ bool split_range(const SplitArgs& a, const Work& w, int& p0, int& p1) {
   const int S = a.num_splits;
   int chunk;
@@ -532,7 +567,15 @@ __device__ __forceinline__ bool split_range(const SplitArgs& a, const Work& w, i
       ml[(pair0 + e % w.nh) * S + w.n_row + e / w.nh] = make_float2(kNegInf, 0.0f);
   }
   if (p0 >= w.npos || (a.target_ctas > 0 && w.split >= w.n_row)) {
-    if (threadIdx.x < w.nh) ml[(pair0 + threadIdx.x) * S + w.split] = make_float2(kNegInf, 0.0f);
+    if (a.direct) {
+      // an empty row: O = 0, lse = -inf
+      for (int e = threadIdx.x; e < w.nh * (VD / 4); e += NT)
+        store_final<VD>(a, pair0 + e / (VD / 4), 4 * (e % (VD / 4)), make_float4(0.f, 0.f, 0.f, 0.f),
+                        0.0f);
+      if (a.lse_out && threadIdx.x < w.nh) a.lse_out[pair0 + threadIdx.x] = kNegInf;
+    } else if (threadIdx.x < w.nh) {
+      ml[(pair0 + threadIdx.x) * S + w.split] = make_float2(kNegInf, 0.0f);
+    }
     return false;
   }
   return true;
@@ -724,13 +767,31 @@ __device__ __forceinline__ void exact_partial(const SplitArgs& a, const Work& wk
       L += f[w] * scratch[w * (VD + 2) + VD + 1];
     }
     const size_t pidx = ((size_t)wk.r * a.heads + h) * S + wk.split;
-    for (int c = threadIdx.x; c < VD; c += NT) {
-      float o = 0.0f;
+    if (a.direct) {
+      const Final fin = final_of(a, h, M, L);
+      const size_t pair = (size_t)wk.r * a.heads + h;
+      for (int c4 = threadIdx.x; c4 < VD / 4; c4 += NT) {
+        float part[4];
 #pragma unroll
-      for (int w = 0; w < W; ++w) o += f[w] * scratch[w * (VD + 2) + c];
-      a.ws_acc[pidx * VD + c] = o * v_scale_of(a, sc, s_vs, c);
+        for (int j = 0; j < 4; ++j) {
+          const int c = 4 * c4 + j;
+          float o = 0.0f;
+#pragma unroll
+          for (int w = 0; w < W; ++w) o += f[w] * scratch[w * (VD + 2) + c];
+          part[j] = o * v_scale_of(a, sc, s_vs, c);
+        }
+        store_final<VD>(a, pair, 4 * c4, make_float4(part[0], part[1], part[2], part[3]), fin.f);
+      }
+      if (a.lse_out && threadIdx.x == 0) a.lse_out[pair] = fin.lse;
+    } else {
+      for (int c = threadIdx.x; c < VD; c += NT) {
+        float o = 0.0f;
+#pragma unroll
+        for (int w = 0; w < W; ++w) o += f[w] * scratch[w * (VD + 2) + c];
+        a.ws_acc[pidx * VD + c] = o * v_scale_of(a, sc, s_vs, c);
+      }
+      if (threadIdx.x == 0) reinterpret_cast<float2*>(a.ws_ml)[pidx] = make_float2(M, L);
     }
-    if (threadIdx.x == 0) reinterpret_cast<float2*>(a.ws_ml)[pidx] = make_float2(M, L);
     __syncthreads();
   }
 }
@@ -823,7 +884,7 @@ split_kernel(const SplitArgs a) {
   const int lo = wk.lo;
 
   int p0, p1;
-  if (!split_range(a, wk, p0, p1)) return;
+  if (!split_range<VD>(a, wk, p0, p1)) return;
   const int split = wk.split;
   const int ntiles = (p1 - p0 + 15) >> 4;
 
@@ -1117,7 +1178,14 @@ split_kernel(const SplitArgs a) {
         L += ((mw == kNegInf) ? 0.0f : __builtin_amdgcn_exp2f((mw - M) * kLog2e)) * sm_l[w][hh];
       }
       const size_t pidx = ((size_t)r * a.heads + h0 + hh) * S + split;
-      if (cc == 0) reinterpret_cast<float2*>(a.ws_ml)[pidx] = make_float2(M, L);
+      const size_t pair = (size_t)r * a.heads + h0 + hh;
+      Final fin{0.0f, kNegInf};
+      if (a.direct) {
+        fin = final_of(a, h0 + hh, M, L);
+        if (a.lse_out && cc == 0) a.lse_out[pair] = fin.lse;
+      } else if (cc == 0) {
+        reinterpret_cast<float2*>(a.ws_ml)[pidx] = make_float2(M, L);
+      }
       float* dst = a.ws_acc + pidx * VD;
 #pragma unroll
       for (int j = 0; j < VD / 64; ++j) {
@@ -1136,7 +1204,10 @@ split_kernel(const SplitArgs a) {
         o.y *= a.v_mult * v_scale_of(a, sc, s_vs, c + 1);
         o.z *= a.v_mult * v_scale_of(a, sc, s_vs, c + 2);
         o.w *= a.v_mult * v_scale_of(a, sc, s_vs, c + 3);
-        *reinterpret_cast<float4*>(dst + c) = o;
+        if (a.direct)
+          store_final<VD>(a, pair, c, o, fin.f);
+        else
+          *reinterpret_cast<float4*>(dst + c) = o;
       }
     }
   }
@@ -1259,7 +1330,7 @@ latent_kernel(const SplitArgs a) {
   const int lo = wk.lo;
 
   int p0, p1;
-  if (!split_range<NT>(a, wk, p0, p1)) return;
+  if (!split_range<C::VD, NT>(a, wk, p0, p1)) return;
   const int split = wk.split;
   const int ntiles = (p1 - p0 + 15) >> 4;
   const int nrounds = (ntiles + W - 1) / W;
@@ -1344,10 +1415,14 @@ latent_kernel(const SplitArgs a) {
   else
     stage_v = s_stage + (size_t)(4 * lj + (li >> 2)) * C::RS + (size_t)(wave * C::VQ + 4 * (li & 3)) * 2;
 
-  // Round rd on the K tile in T; afterwards T is free and the loads of
-  // round rd + 2 are issued into it.
-  auto round = [&](LatK<C>& T, int rd, auto lo) __attribute__((always_inline)) {
+  // Round rd on the K tile in T.  One-byte codes: the loads of round rd + 2
+  // go into the third buffer Tn (free since round rd - 1) before anything
+  // else, which measured faster than waiting for T; two-byte codes (whose
+  // tiles are twice as large) issue them into T once it is staged.
+  constexpr bool kEarly = C::EB == 1;
+  auto round = [&](LatK<C>& T, LatK<C>& Tn, int rd, auto lo) __attribute__((always_inline)) {
     constexpr bool LO = decltype(lo)::value;
+    if constexpr (kEarly) issue_k(Tn, (rd + 2) * W + wave);
     // scores of this wave's tile
     f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -1389,7 +1464,7 @@ latent_kernel(const SplitArgs a) {
     for (int s = 0; s < C::NKL; ++s)
       *reinterpret_cast<uint4*>(stage_k + 64 * s) =
           uint4{T.k[4 * s] & keep, T.k[4 * s + 1] & keep, T.k[4 * s + 2] & keep, T.k[4 * s + 3] & keep};
-    issue_k(T, (rd + 2) * W + wave);
+    if constexpr (!kEarly) issue_k(T, (rd + 2) * W + wave);
     __builtin_amdgcn_sched_barrier(0);
 
     f32x4 st[W];
@@ -1455,9 +1530,9 @@ latent_kernel(const SplitArgs a) {
     }
   };
 
-  // two rounds of K in flight (deeper register rings measured slower on
-  // MI355X: more outstanding misses per CU only lengthen the latency)
-  LatK<C> ka, kb;
+  // two rounds of K in flight (deeper rings measured slower on MI355X: more
+  // outstanding misses per CU only lengthen the latency)
+  LatK<C> ka, kb, kc;
   issue_k(ka, wave);
   issue_k(kb, W + wave);
   q_stage<C::NKS, C::EB, D, QPT, NT>(qraw, ksc, sc.k_tensor, s_q, s_err);
@@ -1469,10 +1544,20 @@ latent_kernel(const SplitArgs a) {
     if (lane == 0) s_flag[W] = fold ? 1 : 0;
   }
   auto round_loop = [&](auto lo) __attribute__((always_inline)) {
-    for (int rd = 0; rd < nrounds; rd += 2) {
-      round(ka, rd, lo);
-      if (rd + 1 >= nrounds) break;
-      round(kb, rd + 1, lo);
+    if constexpr (kEarly) {
+      for (int rd = 0; rd < nrounds; rd += 3) {
+        round(ka, kc, rd, lo);
+        if (rd + 1 >= nrounds) break;
+        round(kb, ka, rd + 1, lo);
+        if (rd + 2 >= nrounds) break;
+        round(kc, kb, rd + 2, lo);
+      }
+    } else {
+      for (int rd = 0; rd < nrounds; rd += 2) {
+        round(ka, ka, rd, lo);
+        if (rd + 1 >= nrounds) break;
+        round(kb, kb, rd + 1, lo);
+      }
     }
   };
   round_loop(std::integral_constant<bool, kResidualTile>{});
@@ -1506,7 +1591,14 @@ latent_kernel(const SplitArgs a) {
   if (li < nh) {
     const int h = h0 + li;
     const size_t pidx = ((size_t)r * a.heads + h) * S + split;
-    if (wave == 0 && lj == 0) reinterpret_cast<float2*>(a.ws_ml)[pidx] = make_float2(m_ref, l_part);
+    const size_t pair = (size_t)r * a.heads + h;
+    Final fin{0.0f, kNegInf};
+    if (a.direct) {
+      fin = final_of(a, h, m_ref, l_part);
+      if (a.lse_out && wave == 0 && lj == 0) a.lse_out[pair] = fin.lse;
+    } else if (wave == 0 && lj == 0) {
+      reinterpret_cast<float2*>(a.ws_ml)[pidx] = make_float2(m_ref, l_part);
+    }
     float* dst = a.ws_acc + pidx * C::VD;
     // column tile ct holds channels 16 ct + 4 lj + q of this wave's range
 #pragma unroll
@@ -1516,7 +1608,10 @@ latent_kernel(const SplitArgs a) {
       float* op = reinterpret_cast<float*>(&o);
 #pragma unroll
       for (int q = 0; q < 4; ++q) op[q] = (acc[ct][q] * a.v_mult) * v_scale_of(a, sc, s_vs, cbase + q);
-      *reinterpret_cast<float4*>(dst + cbase) = o;
+      if (a.direct)
+        store_final<C::VD>(a, pair, cbase, o, fin.f);
+      else
+        *reinterpret_cast<float4*>(dst + cbase) = o;
     }
   }
 }

@@ -199,13 +199,19 @@ def test_gathered_and_scale_requirements():
 
 def test_automatic_chunk_floor_bounds_partial_traffic():
     # latent rows (16 heads x 512 FP32 partials per split vs 576 B per token):
-    # the floor is the power of two keeping partials <= a quarter of the KV bytes
+    # the floor is the power of two keeping partials <= an eighth of the KV
+    # bytes (32 rows x 8 splits still give each of the 256 CUs a CTA)
     lat = pkv.make_problem(32, 16, 1, 576, 512, 64, 64, 2048, cache_dtype="fp8",
                            k_quant="tensor", v_quant="tensor", layout="latent")
     g = pkv.split_geometry(lat, num_cus=256, ctas_per_cu=2)
     partial = 16 * (512 + 2) * 4
+    assert g.min_chunk == 512 and 8 * partial <= 576 * g.min_chunk < 16 * partial
+    assert g.num_splits == 4096 // 512
+    # half the rows: an eighth would leave CUs idle, a quarter is kept
+    lat16 = pkv.make_problem(16, 16, 1, 576, 512, 64, 64, 2048, cache_dtype="fp8",
+                             k_quant="tensor", v_quant="tensor", layout="latent")
+    g = pkv.split_geometry(lat16, num_cus=256, ctas_per_cu=2)
     assert g.min_chunk == 256 and 4 * partial <= 576 * g.min_chunk < 8 * partial
-    assert g.num_splits == 4096 // 256
     # gathered INT8 rows, group 12, head 256: two 64-candidate tiles per split
     dsa = pkv.make_problem(8, 24, 2, 256, 256, 16, 2048, 2048, max_candidates=2048,
                            cache_dtype="i8", k_quant="channel", v_quant="channel")

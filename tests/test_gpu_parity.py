@@ -354,3 +354,55 @@ def test_folding_over_budget_is_exact(cache, D, VD, lay, quant):
     announce(f"folding over budget, {cache} {lay}")
     got, lse, _ = run_gpu(inp, splits_override=2, min_chunk=16, out_dtype="f32")
     _near_exact(got, ref, lse, ref_lse, 1e-4)
+
+
+# ---------------------------------------------------------------------------
+# one split per row: the split kernel writes the output itself
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("v", [("i8", 256, 256, "separate", False), ("f16", 128, 128, "separate", True),
+                               ("fp8", 576, 512, "latent", False), ("i8", 576, 512, "latent", True)],
+                         ids=lambda v: "-".join(map(str, v)))
+@pytest.mark.parametrize("out_dtype", ["f16", "f32"])
+def test_single_split_direct_output_equals_partials_and_combine(v, out_dtype):
+    """With S = 1 paged_decode_attention skips the combine launch; its output
+    and lse are bitwise those of paged_decode_partials + split_combine (rows
+    include an empty one; the head sink is on)."""
+    inp = _small(*v, seed=9)
+    ref, ref_lse = oracle.paged_decode(inp)
+    announce(f"direct output {v} {out_dtype}")
+    a, la, g = run_gpu(inp, out_dtype=out_dtype, splits_override=1, min_chunk=16)
+    assert g.num_splits == 1
+    b, lb, _ = run_gpu(inp, out_dtype=out_dtype, geometry=g, partials_then_combine=True)
+    assert np.array_equal(a, b) and np.array_equal(la, lb)
+    assert_close_to_oracle(a, la, ref, ref_lse, what=f"direct {v}")
+
+
+def test_single_split_direct_output_on_the_fp32_path():
+    """A CTA that takes the FP32 path (folding over budget) with S = 1 also
+    writes the final output directly, bitwise as the combine would."""
+    inp = _small("i8", 256, 256, "separate", False, seed=10, quant="channel")
+    # Q k_scale products that FP16 cannot hold exactly, and large: the
+    # folding bound is far over budget for every head
+    inp.k_scale[...] = np.float32(1.0 / 3.0)
+    inp.query[...] = (inp.query.astype(np.float32) * 1000.0).astype(np.float16)
+    ref, ref_lse = oracle.paged_decode(inp)
+    announce("direct output, FP32 path")
+    a, la, g = run_gpu(inp, splits_override=1, min_chunk=16)
+    b, lb, _ = run_gpu(inp, geometry=g, partials_then_combine=True)
+    assert np.array_equal(a, b) and np.array_equal(la, lb)
+    fin = np.isfinite(ref_lse)
+    np.testing.assert_allclose(la[fin], ref_lse[fin], rtol=1e-5, atol=1e-3)
+
+
+def test_prefill_shape_sampled_rows():
+    """The dynamic-sparse prefill shape (128 rows x 2048 gathered candidates,
+    INT8 per-channel, one split per row by default geometry) against the
+    oracle on a sample of rows."""
+    inp = workloads.workload("P128")
+    rows = list(range(0, 128, 9))
+    ref, ref_lse = oracle.paged_decode(inp, rows=rows)
+    announce("P128 prefill shape")
+    got, lse, g = run_gpu(inp)
+    assert_close_to_oracle(got[rows], lse[rows], ref[rows], ref_lse[rows], what="P128")
+    announce(f"P128: S={g.num_splits}")

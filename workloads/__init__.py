@@ -378,7 +378,29 @@ def c5(seed: int = 5) -> Inputs:
                        name="C5 absorbed-MLA latent FP8 e4m3fn: 32 rows, context 4096, 16q/1 latent head, 576/512, block 64")
 
 
-WORKLOADS = {"C1": c1, "C2": c2, "C3": c3, "C4": c4, "C5": c5}
+def dsa_prefill(rows: int, ctx: int = 8192, seed: int = 6) -> Inputs:
+    """The dynamic-sparse prefill shape: ``rows`` query rows of one sequence
+    of ``ctx`` tokens, each attending its own 2048 sorted random candidates,
+    with C4's head shapes, distributions and scales (24q/2kv, head 256, INT8
+    per-channel, codes clip(rint(N(0, 40^2))), Q ~ N(0, 1.4^2), scale 1/16).
+    Every row is evaluated whole (one split), so the work is the MFMA
+    contractions over gathered, cache-resident rows."""
+    rng = np.random.default_rng(seed + 1000)
+    k = 2048
+    cand = sorted_subsets(rng, rows, ctx, k)
+    p = Problem(rows=rows, heads=24, kv_heads=2, head_size=256, v_head_size=256, block_size=16,
+                max_blocks_per_row=ctx // 16, num_pool_blocks=0, max_candidates=k,
+                cache_dtype="i8", k_quant="channel", v_quant="channel")
+    return make_inputs(p, seed, ctx, softmax_scale=0.0625, q_std=1.4, candidates=cand,
+                       code_std=40.0, shared_table=True,
+                       name=f"DSA prefill INT8 per-channel: {rows} rows, 24q/2kv, head 256, "
+                            f"context {ctx}, 2048 candidates per row")
+
+
+WORKLOADS = {"C1": c1, "C2": c2, "C3": c3, "C4": c4, "C5": c5,
+             "P128": lambda seed=6: dsa_prefill(128, seed=seed),
+             "P2048": lambda seed=6: dsa_prefill(2048, seed=seed),
+             "P8192": lambda seed=6: dsa_prefill(8192, seed=seed)}
 
 
 def workload(name: str, seed: Optional[int] = None) -> Inputs:
