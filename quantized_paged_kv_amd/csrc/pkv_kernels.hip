@@ -1731,6 +1731,93 @@ combine_kernel(const CombineArgs a) {
   }
 }
 
+// ---- the combine for few splits -------------------------------------------
+//
+// For S <= kSmallSplits: one wave per (row, query head), four per CTA, so a
+// step with many rows does not launch one 512-thread CTA per pair.  The
+// (m, l) pairs are wave-uniform and come through scalar loads; every lane
+// owns VD / 64 consecutive channels, issues all of its partial loads first
+// and sums the weighted partials in split order (deterministic).  Same
+// arithmetic as combine_kernel, so S = 1 gives what the kernels' direct
+// output gives.
+
+constexpr int kSmallSplits = 8;
+
+template <int VD, bool OUT_F32>
+__global__ void __launch_bounds__(256) combine_small_kernel(const CombineArgs a) {
+  constexpr int CPL = VD / 64;  // channels per lane
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int pair = blockIdx.x * 4 + wave;
+  if (pair >= a.rows * a.heads) return;
+  const int S = a.num_splits;
+  const int h = pair % a.heads;
+
+  const float* base = a.ws_acc + (size_t)pair * S * VD + lane * CPL;
+  float v[kSmallSplits][CPL];
+#pragma unroll
+  for (int k = 0; k < kSmallSplits; ++k) {
+    if (k < S) {
+      if constexpr (CPL % 4 == 0) {
+#pragma unroll
+        for (int j = 0; j < CPL; j += 4) {
+          const float4 q = *reinterpret_cast<const float4*>(base + (size_t)k * VD + j);
+          v[k][j] = q.x; v[k][j + 1] = q.y; v[k][j + 2] = q.z; v[k][j + 3] = q.w;
+        }
+      } else if constexpr (CPL == 2) {
+        const float2 q = *reinterpret_cast<const float2*>(base + (size_t)k * VD);
+        v[k][0] = q.x; v[k][1] = q.y;
+      } else {
+        v[k][0] = base[(size_t)k * VD];
+      }
+    }
+  }
+  float mk[kSmallSplits], lk[kSmallSplits];
+  float M = kNegInf;
+#pragma unroll
+  for (int k = 0; k < kSmallSplits; ++k) {
+    mk[k] = kNegInf;
+    lk[k] = 0.0f;
+    if (k < S) {
+      mk[k] = uniform_load(a.ws_ml, 2 * ((size_t)pair * S + k));
+      lk[k] = uniform_load(a.ws_ml, 2 * ((size_t)pair * S + k) + 1);
+    }
+    M = fmaxf(M, mk[k]);
+  }
+  float L = 0.0f;
+  float o[CPL];
+#pragma unroll
+  for (int j = 0; j < CPL; ++j) o[j] = 0.0f;
+#pragma unroll
+  for (int k = 0; k < kSmallSplits; ++k) {
+    if (k < S) {
+      const float w = (mk[k] == kNegInf) ? 0.0f : expf(mk[k] - M);
+      L += w * lk[k];
+      if (w != 0.0f) {  // empty splits' accumulators are never used
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) o[j] += w * v[k][j];
+      }
+    }
+  }
+  float lse = kNegInf;
+  float f = 0.0f;
+  if (L > 0.0f) {
+    lse = M + logf(L);
+    f = 1.0f / L;
+    if (a.head_sink) f *= 1.0f / (1.0f + expf(a.head_sink[h] - lse));
+  }
+  if (a.lse_out && lane == 0) a.lse_out[pair] = lse;
+  if constexpr (OUT_F32) {
+    float* dst = reinterpret_cast<float*>(a.out) + (size_t)pair * VD + lane * CPL;
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) dst[j] = o[j] * f;
+  } else {
+    half_t* dst = reinterpret_cast<half_t*>(a.out) + (size_t)pair * VD + lane * CPL;
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) dst[j] = (half_t)(o[j] * f);
+  }
+}
+
 // ---- dispatch ---------------------------------------------------------------
 
 template <int CT, int D, int VD, bool LAT, bool GA, bool EXT>
@@ -1808,7 +1895,10 @@ hipError_t split_occupancy(const Variant& v, int* ctas_per_cu) {
 template <int VD, bool F32>
 static hipError_t launch_combine_t(const CombineArgs& a, hipStream_t stream) {
   const int pairs = a.rows * a.heads;
-  hipLaunchKernelGGL((combine_kernel<VD, F32>), dim3(pairs), dim3(kCombineThreads), 0, stream, a);
+  if (a.num_splits <= kSmallSplits)
+    hipLaunchKernelGGL((combine_small_kernel<VD, F32>), dim3((pairs + 3) / 4), dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL((combine_kernel<VD, F32>), dim3(pairs), dim3(kCombineThreads), 0, stream, a);
   return hipGetLastError();
 }
 
