@@ -213,15 +213,22 @@ def bench_write(args, dev):
     return 0
 
 
+def workloads_names():
+    import workloads
+
+    return list(workloads.WORKLOADS)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="C2",
-                    choices=["C1", "C2", "C3", "C4", "C5", "P128", "P2048", "P8192"],
+    ap.add_argument("--workload", default="C2", choices=sorted(workloads_names()),
                     help="C1..C5: the decode configurations; P<rows>: the dynamic-sparse "
-                         "prefill shape (rows x 2048 gathered candidates, MFMA-bound)")
+                         "prefill shape (rows x 2048 gathered candidates, MFMA-bound); "
+                         "X<ctx>b<batch><dtype>: the PagedAttention page's isolated decode "
+                         "shapes (64q/8kv, head 64, block 256)")
     ap.add_argument("--replica-bytes", type=float, default=1.0 * (1 << 30),
                     help="cold-cache protocol: replicate the cache until this many bytes")
     ap.add_argument("--no-cpu-baseline", action="store_true")

@@ -1733,17 +1733,16 @@ combine_kernel(const CombineArgs a) {
 
 // ---- the combine for few splits -------------------------------------------
 //
-// For S <= kSmallSplits: one wave per (row, query head), four per CTA, so a
-// step with many rows does not launch one 512-thread CTA per pair.  The
+// For few splits (S <= 8, or S <= 16 with many pairs and VD <= 256): one
+// wave per (row, query head), four per CTA, so a step with many rows does
+// not launch one 512-thread CTA per pair.  The
 // (m, l) pairs are wave-uniform and come through scalar loads; every lane
 // owns VD / 64 consecutive channels, issues all of its partial loads first
 // and sums the weighted partials in split order (deterministic).  Same
 // arithmetic as combine_kernel, so S = 1 gives what the kernels' direct
 // output gives.
 
-constexpr int kSmallSplits = 8;
-
-template <int VD, bool OUT_F32>
+template <int VD, bool OUT_F32, int kSmallSplits>
 __global__ void __launch_bounds__(256) combine_small_kernel(const CombineArgs a) {
   constexpr int CPL = VD / 64;  // channels per lane
   const int lane = threadIdx.x & 63;
@@ -1895,8 +1894,14 @@ hipError_t split_occupancy(const Variant& v, int* ctas_per_cu) {
 template <int VD, bool F32>
 static hipError_t launch_combine_t(const CombineArgs& a, hipStream_t stream) {
   const int pairs = a.rows * a.heads;
-  if (a.num_splits <= kSmallSplits)
-    hipLaunchKernelGGL((combine_small_kernel<VD, F32>), dim3((pairs + 3) / 4), dim3(256), 0, stream, a);
+  // measured on MI355X: the wave-per-pair combine wins up to 8 splits, and up
+  // to 16 once there are enough pairs to fill the chip with its small CTAs
+  if (a.num_splits <= 8)
+    hipLaunchKernelGGL((combine_small_kernel<VD, F32, 8>), dim3((pairs + 3) / 4), dim3(256), 0,
+                       stream, a);
+  else if (a.num_splits <= 16 && VD <= 256 && pairs >= 512)
+    hipLaunchKernelGGL((combine_small_kernel<VD, F32, 16>), dim3((pairs + 3) / 4), dim3(256), 0,
+                       stream, a);
   else
     hipLaunchKernelGGL((combine_kernel<VD, F32>), dim3(pairs), dim3(kCombineThreads), 0, stream, a);
   return hipGetLastError();

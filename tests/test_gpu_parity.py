@@ -406,3 +406,16 @@ def test_prefill_shape_sampled_rows():
     got, lse, g = run_gpu(inp)
     assert_close_to_oracle(got[rows], lse[rows], ref[rows], ref_lse[rows], what="P128")
     announce(f"P128: S={g.num_splits}")
+
+
+@pytest.mark.parametrize("name", ["X4096b8i8", "X1024b32fp8"])
+@pytest.mark.parametrize("S", [0, 12, 16])
+def test_paged_page_shapes(name, S):
+    """The PagedAttention page's isolated decode shapes (64q/8kv, head 64,
+    block 256, INT8 / FP8 per tensor): default geometry, and 12 or 16 splits,
+    which with 512+ (row, head) pairs take the wave-per-pair combine."""
+    inp, (ref, ref_lse) = named(name)
+    announce(f"{name} S={S}")
+    geo = {} if S == 0 else dict(splits_override=S, min_chunk=16)
+    got, lse, g = run_gpu(inp, **geo)
+    assert_close_to_oracle(got, lse, ref, ref_lse, what=f"{name} S={g.num_splits}")

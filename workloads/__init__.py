@@ -397,7 +397,23 @@ def dsa_prefill(rows: int, ctx: int = 8192, seed: int = 6) -> Inputs:
                             f"context {ctx}, 2048 candidates per row")
 
 
+def paged_quantized(ctx: int, batch: int, cache_dtype: str, seed: int = 7) -> Inputs:
+    """The PagedAttention page's isolated paged-decode shape: ``batch`` rows
+    of ``ctx`` tokens, 64 query / 8 KV heads, head size 64, block 256, INT8
+    or FP8 per-tensor cache from N(0, 1) values (s = max|x| / 127 or / 448),
+    Q ~ N(0, 1), scale 1/8, shuffled blocks."""
+    p = Problem(rows=batch, heads=64, kv_heads=8, head_size=64, v_head_size=64, block_size=256,
+                max_blocks_per_row=ctx // 256, num_pool_blocks=0, cache_dtype=cache_dtype,
+                k_quant="tensor", v_quant="tensor")
+    return make_inputs(p, seed, ctx, softmax_scale=0.125,
+                       name=f"paged {cache_dtype} per-tensor decode: {batch} rows x {ctx} tokens, "
+                            f"64q/8kv, head 64, block 256")
+
+
 WORKLOADS = {"C1": c1, "C2": c2, "C3": c3, "C4": c4, "C5": c5,
+             **{f"X{c}b{b}{d}": (lambda seed=7, c=c, b=b, d=d: paged_quantized(c, b, d, seed))
+                for c, b in ((1024, 32), (4096, 8), (4096, 32), (16384, 8), (16384, 32))
+                for d in ("i8", "fp8")},
              "P128": lambda seed=6: dsa_prefill(128, seed=seed),
              "P2048": lambda seed=6: dsa_prefill(2048, seed=seed),
              "P8192": lambda seed=6: dsa_prefill(8192, seed=seed)}
