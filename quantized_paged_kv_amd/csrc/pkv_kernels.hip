@@ -1228,8 +1228,7 @@ split_kernel(const SplitArgs a) {
 //     transpose reads.
 // Each row therefore crosses HBM and L2 once, V needs no registers while in
 // flight, and each wave keeps a 16 x (512 / W) accumulator.
-// Stage rows are padded so that the four token groups of a transposed V
-// read fall on disjoint LDS banks.
+// Stage rows are padded to keep LDS bank conflicts low.
 
 template <int CT, bool GATHER>
 struct LatCfg {
@@ -1243,7 +1242,12 @@ struct LatCfg {
   static constexpr int NT = 64 * W;              // threads per CTA
   static constexpr int VQ = VD / W;              // V channels per wave
   static constexpr int CPL = VQ / 16;            // 16-channel column tiles per wave
-  static constexpr int RS = KROW + 32 * EB;      // LDS stage row stride (bytes)
+  // LDS stage row stride (bytes).  One-byte codes: 592 = 148 dwords, which
+  // keeps the 16-byte row writes (16 rows x 64 bytes per instruction) free
+  // of conflicts on gfx950's 64 LDS banks and leaves the transposed V reads
+  // two-way conflicted at most (SQ_LDS_BANK_CONFLICT on the latent FP8
+  // workload: 2.6e5 against 8.5e5 with a 608-byte stride).
+  static constexpr int RS = KROW + (EB == 1 ? 16 : 64);
   static constexpr int ROUND = 16 * W;          // tokens per round
   static constexpr int MIN_WAVES = EB == 1 ? 2 : 1;
   static_assert(RS % 16 == 0, "stage rows hold 16-byte chunks");

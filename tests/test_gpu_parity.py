@@ -54,12 +54,20 @@ def test_split_overrides(name, S):
     assert_close_to_oracle(got, lse, ref, ref_lse, what=f"{name} S={S}")
 
 
-def test_partials_then_combine_equals_one_call():
-    inp, _ = named("C3")
-    announce("C3 partials + combine vs paged_decode_attention")
-    a, la, _ = run_gpu(inp)
-    b, lb, _ = run_gpu(inp, partials_then_combine=True)
+# paged_decode_attention and partials + split_combine give bit-identical
+# results, for every form of the merge: a wave per pair for up to 8 splits
+# (C5) or 16 splits with many pairs, and a CTA per pair (C2: 64 splits, C3:
+# 48, C4 at 24, C1 at 16).
+@pytest.mark.parametrize("name,S", [("C3", 0), ("C5", 0), ("C2", 0), ("C4", 24), ("C1", 16)])
+def test_partials_then_combine_equals_one_call(name, S):
+    inp, (ref, ref_lse) = named(name)
+    announce(f"{name} S={S} partials + combine vs paged_decode_attention")
+    geo = dict(splits_override=S, min_chunk=16) if S else {}
+    a, la, g = run_gpu(inp, **geo)
+    b, lb, _ = run_gpu(inp, partials_then_combine=True, **geo)
+    assert g.num_splits > 1
     assert np.array_equal(a, b) and np.array_equal(la, lb)
+    assert_close_to_oracle(a, la, ref, ref_lse, what=name)
 
 
 # ---------------------------------------------------------------------------
@@ -255,6 +263,10 @@ def test_hip_graph_replay_matches_eager_with_new_lengths():
         graph.replay()
         torch.cuda.synchronize()
         o_graph, l_graph = out.clone(), lse.clone()
+        for _ in range(3):  # further replays (each reuses the workspace counters)
+            graph.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(o_graph, out) and torch.equal(l_graph, lse)
         step()  # eager
         torch.cuda.synchronize()
         assert torch.equal(o_graph, out) and torch.equal(l_graph, lse)
