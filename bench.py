@@ -213,6 +213,172 @@ def bench_write(args, dev):
     return 0
 
 
+# ---- rocprofv3 summaries (profiles/) -----------------------------------------
+
+PMC_SQ = ("SQ_WAVES SQ_WAVE_CYCLES SQ_BUSY_CYCLES SQ_LEVEL_WAVES SQ_ACTIVE_INST_LDS "
+          "SQ_LDS_BANK_CONFLICT SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_MFMA")
+
+
+def _pmc_commands(w: str, tag: str) -> list:
+    """The rocprofv3 runs a counter summary is made from ($R = repository
+    root); they run committed files only."""
+    run = f"python3 $R/bench.py --workload {w} --eager --steps 20 --warmup 2 --no-cpu-baseline"
+    cmds = []
+    for name, pmc in (("FETCH_SIZE", "FETCH_SIZE"), ("WRITE_SIZE", "WRITE_SIZE"), ("SQ", PMC_SQ)):
+        cmds.append(f"cd /tmp && export TMPDIR=/tmp && timeout -s KILL 90 rocprofv3 --pmc {pmc} "
+                    f"--output-format csv -d $R/gpurun_out/{tag}/pmc_{name}_{w} -o p -- {run}")
+    for name in ("FETCH_SIZE", "WRITE_SIZE"):
+        cmds.append(f"cd /tmp && export TMPDIR=/tmp && timeout -s KILL 90 rocprofv3 --pmc {name} "
+                    f"--output-format csv -d $R/gpurun_out/{tag}/pmc_{name}_copy -o p -- "
+                    f"python3 $R/bench.py --copy-bytes 268435456")
+    return cmds
+
+
+def _read_counters(path: str) -> dict:
+    """{kernel name: {counter: mean value per dispatch}} from a rocprofv3
+    counter_collection.csv."""
+    import csv
+    import glob
+
+    files = glob.glob(os.path.join(path, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise FileNotFoundError(f"no counter_collection.csv under {path}")
+    sums, disp = {}, {}
+    for f in files:
+        for row in csv.DictReader(open(f)):
+            k = row["Kernel_Name"]
+            sums.setdefault(k, {}).setdefault(row["Counter_Name"], 0.0)
+            sums[k][row["Counter_Name"]] += float(row["Counter_Value"])
+            disp.setdefault(k, set()).add(row["Dispatch_Id"])
+    return {k: {c: v / len(disp[k]) for c, v in cs.items()} | {"_dispatches": len(disp[k])}
+            for k, cs in sums.items()}
+
+
+def _dispatch_resources(path: str, kernel_name: str):
+    """(grid size, workgroup size, VGPRs, LDS bytes) of the kernel's first
+    dispatch in a counter_collection.csv, or None."""
+    import csv
+    import glob
+
+    for f in glob.glob(os.path.join(path, "**", "*counter_collection.csv"), recursive=True):
+        for row in csv.DictReader(open(f)):
+            if row["Kernel_Name"] == kernel_name:
+                return (int(row["Grid_Size"]), int(row["Workgroup_Size"]),
+                        int(row["VGPR_Count"]) + int(row.get("Accum_VGPR_Count") or 0),
+                        int(row["LDS_Block_Size"]))
+    return None
+
+
+def _pick(counters: dict, fragment: str):
+    hits = [k for k in counters if fragment in k]
+    return (hits[0], counters[hits[0]]) if hits else (None, {})
+
+
+def summarize_counters(tag_dir: str, w: str) -> str:
+    """The counter summary of the attention kernels of workload w from the
+    rocprofv3 runs under tag_dir (see _pmc_commands)."""
+    import workloads
+
+    inp = workloads.workload(w)
+    p = inp.problem
+    kernel = "latent_kernel" if p.layout == "latent" else "split_kernel"
+    fetch = _read_counters(os.path.join(tag_dir, f"pmc_FETCH_SIZE_{w}"))
+    write = _read_counters(os.path.join(tag_dir, f"pmc_WRITE_SIZE_{w}"))
+    sq = _read_counters(os.path.join(tag_dir, f"pmc_SQ_{w}"))
+    cf = _read_counters(os.path.join(tag_dir, "pmc_FETCH_SIZE_copy"))
+    cw = _read_counters(os.path.join(tag_dir, "pmc_WRITE_SIZE_copy"))
+    copy_kib = 268435456 / 1024
+    _, cfv = _pick(cf, "copyBuffer")
+    _, cwv = _pick(cw, "copyBuffer")
+    fscale = copy_kib / cfv["FETCH_SIZE"]
+    wscale = copy_kib / cwv["WRITE_SIZE"]
+    kname, kf = _pick(fetch, f"pkv::{kernel}")
+    _, kw = _pick(write, f"pkv::{kernel}")
+    _, ks = _pick(sq, f"pkv::{kernel}")
+    algo = inp.effective_kv_bytes()
+    rd = kf["FETCH_SIZE"] * fscale * 1024
+    wr = kw["WRITE_SIZE"] * wscale * 1024
+    tag = os.path.basename(os.path.normpath(tag_dir))
+    lines = [f"# HBM traffic and SQ counters of {kernel} on workload {w} ({inp.name}),",
+             "# from rocprofv3 hardware counters, one run per counter set ($R = repository root).",
+             "# runs:"]
+    lines += [f"#   {c}" for c in _pmc_commands(w, tag)]
+    lines += ["# summary: python3 $R/bench.py --summarize-counters $R/gpurun_out/" + tag
+              + f" --workload {w}",
+              "# scale = KiB the 256 MiB copy really reads (writes) / KiB the counter reports for it;",
+              "# hbm bytes = counter KiB per dispatch x scale x 1024, averaged over the kernel's dispatches;",
+              "# SQ counters: mean per dispatch, summed over the chip as rocprofv3 reports them.",
+              f"kernel: {kname}",
+              f"kernel_source_sha256_16: {kernel_source_hash()}",
+              f"dispatches: {kf['_dispatches']}",
+              f"fetch_size_kib_per_dispatch: {kf['FETCH_SIZE']:.1f}",
+              f"write_size_kib_per_dispatch: {kw['WRITE_SIZE']:.1f}",
+              f"copy_fetch_size_kib_per_dispatch: {cfv['FETCH_SIZE']:.1f}",
+              f"copy_write_size_kib_per_dispatch: {cwv['WRITE_SIZE']:.1f}",
+              f"fetch_scale: {fscale:.4f}",
+              f"write_scale: {wscale:.4f}",
+              f"hbm_read_bytes_per_launch: {rd:.0f}",
+              f"hbm_write_bytes_per_launch: {wr:.0f}",
+              f"hbm_bytes_per_launch: {rd + wr:.0f}",
+              f"algorithmic_kv_bytes_per_launch: {algo}",
+              f"read_over_algorithmic: {rd / algo:.4f}"]
+    for c in PMC_SQ.split():
+        if c in ks:
+            lines.append(f"{c.lower()}_per_dispatch: {ks[c]:.4g}")
+    if ks.get("SQ_ACTIVE_INST_LDS"):
+        lines.append("lds_bank_conflict_cycles_per_lds_active_cycle: "
+                     f"{ks['SQ_LDS_BANK_CONFLICT'] / ks['SQ_ACTIVE_INST_LDS']:.3f}")
+    if ks.get("SQ_BUSY_CYCLES") and ks.get("SQ_LEVEL_WAVES"):
+        lines.append("sq_level_waves_per_busy_cycle: "
+                     f"{ks['SQ_LEVEL_WAVES'] / ks['SQ_BUSY_CYCLES']:.2f}")
+    # the dispatch's resources as rocprofv3 records them (LDS in its
+    # allocation granule; gfx950 has 160 KiB of LDS per CU)
+    occ = _dispatch_resources(os.path.join(tag_dir, f"pmc_SQ_{w}"), kname)
+    if occ:
+        grid, wg, vgpr, lds = occ
+        lines += [f"grid_ctas: {grid // wg}", f"threads_per_cta: {wg}",
+                  f"lds_bytes_per_cta: {lds}",
+                  f"lds_limit_ctas_per_cu: {(160 * 1024) // lds if lds else 'none'}",
+                  f"rocprof_vgpr_count: {vgpr}"]
+    cname, cfc = _pick(fetch, "pkv::combine")
+    if cname:
+        _, cwc = _pick(write, "pkv::combine")
+        lines += [f"combine_kernel: {cname}",
+                  f"combine_hbm_read_bytes_per_launch: {cfc['FETCH_SIZE'] * fscale * 1024:.0f}",
+                  f"combine_hbm_write_bytes_per_launch: {cwc['WRITE_SIZE'] * wscale * 1024:.0f}"]
+    return "\n".join(lines) + "\n"
+
+
+def summarize_trace(tag_dir: str, w: str, bench_log: str = "") -> str:
+    """The per-kernel duration statistics of a rocprofv3 --kernel-trace --stats
+    run of bench.py on workload w."""
+    import csv
+    import glob
+
+    files = glob.glob(os.path.join(tag_dir, f"kt_{w}", "**", "*kernel_stats.csv"), recursive=True)
+    if not files:
+        raise FileNotFoundError(f"no kernel_stats.csv under {tag_dir}/kt_{w}")
+    tag = os.path.basename(os.path.normpath(tag_dir))
+    lines = [f"# rocprofv3 kernel-trace statistics of bench.py on workload {w}",
+             "# command ($R = repository root):",
+             f"#   cd /tmp && export TMPDIR=/tmp && timeout -k 10 300 rocprofv3 --kernel-trace --stats "
+             f"--output-format csv -d $R/gpurun_out/{tag}/kt_{w} -o kt -- python3 $R/bench.py "
+             f"--workload {w} --no-cpu-baseline",
+             "# summary: python3 $R/bench.py --summarize-trace $R/gpurun_out/" + tag + f" --workload {w}",
+             f"kernel_source_sha256_16: {kernel_source_hash()}",
+             f"{'kernel':<72} {'calls':>6} {'avg_ns':>10} {'min_ns':>8} {'max_ns':>8}"]
+    for row in csv.DictReader(open(files[0])):
+        name = row["Name"]
+        short = name if len(name) <= 72 else name[:69] + "..."
+        lines.append(f"{short:<72} {row['Calls']:>6} {float(row['AverageNs']):>10.1f} "
+                     f"{float(row['MinNs']):>8.0f} {float(row['MaxNs']):>8.0f}")
+    if bench_log and os.path.exists(bench_log):
+        for l in open(bench_log):
+            if "] step" in l:
+                lines.append("# bench.py's own line in the traced run: " + l.strip())
+    return "\n".join(lines) + "\n"
+
+
 def workloads_names():
     import workloads
 
@@ -243,11 +409,24 @@ def main():
                          "cache writer (reshape_and_cache) on the workload's cache format")
     ap.add_argument("--write-tokens", type=int, default=16384,
                     help="new tokens per writer call (--op write)")
+    ap.add_argument("--summarize-counters", default="",
+                    help="print the counter summary (profiles/) of the workload's attention kernel "
+                         "from the rocprofv3 runs under this directory, and exit")
+    ap.add_argument("--summarize-trace", default="",
+                    help="print the kernel-trace summary of the workload's rocprofv3 "
+                         "--kernel-trace --stats run under this directory, and exit")
+    ap.add_argument("--trace-log", default="", help="bench.py log of the traced run (--summarize-trace)")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="only run 4 plain device-to-device copies of this many bytes and exit "
                          "(calibrates the HBM byte counters)")
     args = ap.parse_args()
 
+    if args.summarize_counters:
+        sys.stdout.write(summarize_counters(args.summarize_counters, args.workload))
+        return 0
+    if args.summarize_trace:
+        sys.stdout.write(summarize_trace(args.summarize_trace, args.workload, args.trace_log))
+        return 0
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this build has "
               "no multi-GPU path. Run with --gpus 1.", file=sys.stderr)
