@@ -1249,7 +1249,8 @@ struct LatCfg {
   // workload: 2.6e5 against 8.5e5 with a 608-byte stride).
   static constexpr int RS = KROW + (EB == 1 ? 16 : 64);
   static constexpr int ROUND = 16 * W;          // tokens per round
-  static constexpr int MIN_WAVES = EB == 1 ? 2 : 1;
+  // one CTA per CU: the folded query stays in registers (one-byte codes)
+  static constexpr int MIN_WAVES = 1;
   static_assert(RS % 16 == 0, "stage rows hold 16-byte chunks");
 };
 
@@ -1424,9 +1425,13 @@ latent_kernel(const SplitArgs a) {
   // else, which measured faster than waiting for T; two-byte codes (whose
   // tiles are twice as large) issue them into T once it is staged.
   constexpr bool kEarly = C::EB == 1;
+  // one-byte codes: Q' is read from LDS into registers once, not per tile
+  half8 qreg[C::EB == 1 ? C::NKS : 1];
   auto round = [&](LatK<C>& T, LatK<C>& Tn, int rd, auto lo) __attribute__((always_inline)) {
     constexpr bool LO = decltype(lo)::value;
     if constexpr (kEarly) issue_k(Tn, (rd + 2) * W + wave);
+    // keep the loads ahead of the waits for this round's data
+    __builtin_amdgcn_sched_barrier(0);
     // scores of this wave's tile
     f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -1442,8 +1447,8 @@ latent_kernel(const SplitArgs a) {
         const half4 c3 = codes4_to_half4<CT>(T.k[4 * s + 3]);
         const half8 k0 = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
         const half8 k1 = {c2[0], c2[1], c2[2], c2[3], c3[0], c3[1], c3[2], c3[3]};
-        sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(k0, __builtin_bit_cast(half8, s_q[(2 * s) * 64 + lane]), sacc, 0, 0, 0);
-        sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(k1, __builtin_bit_cast(half8, s_q[(2 * s + 1) * 64 + lane]), sacc, 0, 0, 0);
+        sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(k0, qreg[2 * s], sacc, 0, 0, 0);
+        sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(k1, qreg[2 * s + 1], sacc, 0, 0, 0);
       }
     }
     f32x4 scw;
@@ -1546,6 +1551,10 @@ latent_kernel(const SplitArgs a) {
   if (wave == 0) {
     const bool fold = fold_over_budget<CT, C::NKS>(a, s_err, nh, lane);
     if (lane == 0) s_flag[W] = fold ? 1 : 0;
+  }
+  if constexpr (C::EB == 1) {
+#pragma unroll
+    for (int s = 0; s < C::NKS; ++s) qreg[s] = __builtin_bit_cast(half8, s_q[s * 64 + lane]);
   }
   auto round_loop = [&](auto lo) __attribute__((always_inline)) {
     if constexpr (kEarly) {

@@ -27,7 +27,7 @@ def named(name):
 # the five workloads at full size, default geometry (the bench configuration)
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("name", ["C1", "C2", "C3", "C4", "C5"])
+@pytest.mark.parametrize("name", ["C1", "C2", "C3", "C4", "C5", "C2b8"])
 def test_workload_parity(name):
     inp, (ref, ref_lse) = named(name)
     announce(f"{name} default geometry")
@@ -431,3 +431,46 @@ def test_paged_page_shapes(name, S):
     geo = {} if S == 0 else dict(splits_override=S, min_chunk=16)
     got, lse, g = run_gpu(inp, **geo)
     assert_close_to_oracle(got, lse, ref, ref_lse, what=f"{name} S={g.num_splits}")
+
+
+# ---------------------------------------------------------------------------
+# long rows: a wave walks more than 64 tiles, so the per-wave window of
+# block ids (64 tiles per vector register) is refilled mid-row; and more rows
+# than the live-balanced decomposition takes (static mode), and exactly its
+# limit
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("cache,lay", [("fp8", "separate"), ("i8", "separate"),
+                                       ("fp8", "latent"), ("f16", "latent")])
+@pytest.mark.parametrize("S", [1, 3])
+def test_long_rows_refill_block_windows(cache, lay, S):
+    if lay == "separate":
+        heads, kvh, D, VD, ctx = 4, 1, 64, 64, 65536
+    else:
+        heads, kvh, D, VD, ctx = 16, 1, 576, 512, 16384
+    quant = "none" if cache == "f16" else "tensor"
+    p = Problem(rows=2, heads=heads, kv_heads=kvh, head_size=D, v_head_size=VD, block_size=16,
+                max_blocks_per_row=ctx // 16, num_pool_blocks=0, cache_dtype=cache,
+                k_quant=quant, v_quant=quant, layout=lay)
+    inp = workloads.make_inputs(p, 11, [ctx, ctx - 37], with_sink=True,
+                                softmax_scale=1.0 / np.sqrt(D))
+    ref, ref_lse = oracle.paged_decode(inp)
+    announce(f"long rows {cache} {lay} ctx {ctx} S={S}")
+    got, lse, g = run_gpu(inp, splits_override=S, min_chunk=16)
+    assert g.num_splits == S
+    assert_close_to_oracle(got, lse, ref, ref_lse, what=f"long {cache} {lay} S={S}")
+
+
+@pytest.mark.parametrize("rows,balance", [(1100, 0), (1024, 1), (1024, 2)])
+def test_many_rows(rows, balance):
+    rng = np.random.default_rng(rows)
+    lens = rng.integers(0, 97, size=rows)
+    lens[:3] = [0, 96, 1]
+    p = Problem(rows=rows, heads=8, kv_heads=2, head_size=64, v_head_size=64, block_size=16,
+                max_blocks_per_row=6, num_pool_blocks=0, cache_dtype="f16")
+    inp = workloads.make_inputs(p, 12, lens, with_sink=True, softmax_scale=0.125)
+    ref, ref_lse = oracle.paged_decode(inp)
+    announce(f"{rows} rows balance={balance}")
+    got, lse, g = run_gpu(inp, balance=balance)
+    assert (g.target_ctas > 0) == (balance == 1)
+    assert_close_to_oracle(got, lse, ref, ref_lse, what=f"{rows} rows balance={balance}")

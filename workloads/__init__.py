@@ -341,12 +341,16 @@ def c1(seed: int = 1) -> Inputs:
                        name="C1 tiny FP16 decode: 1 row, 4q/1kv, head 64, context 256, block 16")
 
 
-def c2(seed: int = 2) -> Inputs:
-    p = Problem(rows=1, heads=24, kv_heads=2, head_size=256, v_head_size=256, block_size=16,
+def c2(seed: int = 2, batch: int = 1) -> Inputs:
+    """C2; with ``batch`` > 1 the same shape for that many rows (each row its
+    own context of 4096 tokens and shuffled blocks), the batch sweep that
+    shows where the step stops being latency bound."""
+    p = Problem(rows=batch, heads=24, kv_heads=2, head_size=256, v_head_size=256, block_size=16,
                 max_blocks_per_row=256, num_pool_blocks=0, cache_dtype="i8",
                 k_quant="tensor", v_quant="tensor")
+    rows = "1 row" if batch == 1 else f"{batch} rows"
     return make_inputs(p, seed, 4096, softmax_scale=0.0625,
-                       name="C2 INT8 per-tensor decode: 1 row, 24q/2kv, head 256, context 4096, block 16")
+                       name=f"C2 INT8 per-tensor decode: {rows}, 24q/2kv, head 256, context 4096, block 16")
 
 
 def c3(seed: int = 3) -> Inputs:
@@ -411,6 +415,7 @@ def paged_quantized(ctx: int, batch: int, cache_dtype: str, seed: int = 7) -> In
 
 
 WORKLOADS = {"C1": c1, "C2": c2, "C3": c3, "C4": c4, "C5": c5,
+             **{f"C2b{b}": (lambda seed=2, b=b: c2(seed, b)) for b in (8, 32, 64)},
              **{f"X{c}b{b}{d}": (lambda seed=7, c=c, b=b, d=d: paged_quantized(c, b, d, seed))
                 for c, b in ((1024, 32), (4096, 8), (4096, 32), (16384, 8), (16384, 32))
                 for d in ("i8", "fp8")},
