@@ -1746,26 +1746,30 @@ combine_kernel(const CombineArgs a) {
 
 // ---- the combine for few splits -------------------------------------------
 //
-// For few splits (S <= 8, or S <= 16 with many pairs and VD <= 256): one
-// wave per (row, query head), four per CTA, so a step with many rows does
-// not launch one 512-thread CTA per pair.  The
-// (m, l) pairs are wave-uniform and come through scalar loads; every lane
-// owns VD / 64 consecutive channels, issues all of its partial loads first
-// and sums the weighted partials in split order (deterministic).  Same
-// arithmetic as combine_kernel, so S = 1 gives what the kernels' direct
-// output gives.
+// For few splits (S <= 8, or S <= 16 with many pairs and VD <= 256): PARTS
+// waves per (row, query head), each owning VD / PARTS channels (PARTS = 2
+// for 512 channels, so every lane loads one float4 per split and twice as
+// many CUs pull the partials), four waves per CTA, so a step with many rows
+// does not launch one 512-thread CTA per pair.  The (m, l) pairs are
+// wave-uniform and come through scalar loads; every lane owns VD / 64 /
+// PARTS consecutive channels, issues all of its partial loads first and sums
+// the weighted partials in split order (deterministic).  Same arithmetic as
+// combine_kernel, so S = 1 gives what the kernels' direct output gives.
 
-template <int VD, bool OUT_F32, int kSmallSplits>
+template <int VD, bool OUT_F32, int kSmallSplits, int PARTS>
 __global__ void __launch_bounds__(256) combine_small_kernel(const CombineArgs a) {
-  constexpr int CPL = VD / 64;  // channels per lane
+  constexpr int CPL = VD / 64 / PARTS;  // channels per lane
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int pair = blockIdx.x * 4 + wave;
+  const int item = blockIdx.x * 4 + wave;
+  const int pair = item / PARTS;
+  const int part = item - pair * PARTS;
   if (pair >= a.rows * a.heads) return;
   const int S = a.num_splits;
   const int h = pair % a.heads;
+  const int c0 = part * (VD / PARTS) + lane * CPL;  // first channel of this lane
 
-  const float* base = a.ws_acc + (size_t)pair * S * VD + lane * CPL;
+  const float* base = a.ws_acc + (size_t)pair * S * VD + c0;
   float v[kSmallSplits][CPL];
 #pragma unroll
   for (int k = 0; k < kSmallSplits; ++k) {
@@ -1818,13 +1822,13 @@ __global__ void __launch_bounds__(256) combine_small_kernel(const CombineArgs a)
     f = 1.0f / L;
     if (a.head_sink) f *= 1.0f / (1.0f + expf(a.head_sink[h] - lse));
   }
-  if (a.lse_out && lane == 0) a.lse_out[pair] = lse;
+  if (a.lse_out && lane == 0 && part == 0) a.lse_out[pair] = lse;
   if constexpr (OUT_F32) {
-    float* dst = reinterpret_cast<float*>(a.out) + (size_t)pair * VD + lane * CPL;
+    float* dst = reinterpret_cast<float*>(a.out) + (size_t)pair * VD + c0;
 #pragma unroll
     for (int j = 0; j < CPL; ++j) dst[j] = o[j] * f;
   } else {
-    half_t* dst = reinterpret_cast<half_t*>(a.out) + (size_t)pair * VD + lane * CPL;
+    half_t* dst = reinterpret_cast<half_t*>(a.out) + (size_t)pair * VD + c0;
 #pragma unroll
     for (int j = 0; j < CPL; ++j) dst[j] = (half_t)(o[j] * f);
   }
@@ -1909,12 +1913,12 @@ static hipError_t launch_combine_t(const CombineArgs& a, hipStream_t stream) {
   const int pairs = a.rows * a.heads;
   // measured on MI355X: the wave-per-pair combine wins up to 8 splits, and up
   // to 16 once there are enough pairs to fill the chip with its small CTAs
+  constexpr int PARTS = VD > 256 ? 2 : 1;  // waves per pair
+  const int ctas = (pairs * PARTS + 3) / 4;
   if (a.num_splits <= 8)
-    hipLaunchKernelGGL((combine_small_kernel<VD, F32, 8>), dim3((pairs + 3) / 4), dim3(256), 0,
-                       stream, a);
+    hipLaunchKernelGGL((combine_small_kernel<VD, F32, 8, PARTS>), dim3(ctas), dim3(256), 0, stream, a);
   else if (a.num_splits <= 16 && VD <= 256 && pairs >= 512)
-    hipLaunchKernelGGL((combine_small_kernel<VD, F32, 16>), dim3((pairs + 3) / 4), dim3(256), 0,
-                       stream, a);
+    hipLaunchKernelGGL((combine_small_kernel<VD, F32, 16, PARTS>), dim3(ctas), dim3(256), 0, stream, a);
   else
     hipLaunchKernelGGL((combine_kernel<VD, F32>), dim3(pairs), dim3(kCombineThreads), 0, stream, a);
   return hipGetLastError();
