@@ -401,6 +401,8 @@ def main():
     ap.add_argument("--splits", type=int, default=0, help="split-count override (0 = automatic)")
     ap.add_argument("--min-chunk", type=int, default=0, help="geometry min_chunk (0 = default)")
     ap.add_argument("--waves", type=int, default=0, help="geometry target waves (0 = default)")
+    ap.add_argument("--kv-heads-per-cta", type=int, default=0,
+                    help="geometry: KV heads per CTA (0 = default, 1, or 4)")
     ap.add_argument("--eager", action="store_true",
                     help="launch every step eagerly instead of from a HIP graph (for "
                          "per-dispatch hardware counters)")
@@ -462,7 +464,7 @@ def main():
     d = to_device(inp, dev)
     prob = pkv.make_problem(**d.problem_kwargs)
     geo = pkv.split_geometry(prob, splits_override=args.splits, min_chunk=args.min_chunk,
-                             waves=args.waves)
+                             waves=args.waves, kv_heads_per_cta=args.kv_heads_per_cta)
     ws = pkv.workspace_for(geo, dev)
 
     # cold-cache replicas of the caches (the block table, lengths, Q, scales are shared)
@@ -582,6 +584,7 @@ def main():
             "compute": "K/V codes converted to fp16 in registers; fp16 MFMA with fp32 "
                        "accumulation; fp32 softmax",
             "num_splits": geo.num_splits,
+            "kv_heads_per_cta": geo.kv_heads_per_cta,
             "cold_cache_replicas": R,
             "timing": ("K eager launches" if args.eager else "one HIP-graph replay of K steps")
                       + ", HIP events on the launch stream",

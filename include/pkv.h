@@ -139,6 +139,9 @@ typedef struct {
   int32_t waves;            /* target = waves * num_cus * ctas_per_cu CTAs */
   int32_t balance;          /* 0: auto (live-balanced for 16..1024 rows), 1: live-
                                balanced (up to 1024 rows), 2: static */
+  int32_t kv_heads_per_cta; /* 0: auto (4 when allowed, else 1); 1; 4: one CTA takes four
+                               neighbouring KV heads, one per wave (dense rows, SEPARATE
+                               layout, num_kv_heads a multiple of 4, group <= 16) */
 } pkv_geometry_opts;
 
 /* Launch geometry; produced by split_geometry, consumed unchanged. */
@@ -149,13 +152,19 @@ typedef struct {
   int32_t head_blocks;      /* ceil(group / 16): query heads go 16 per CTA */
   int32_t grid_x, grid_y, grid_z;  /* split-kernel grid (1-D: grid_y = grid_z = 1) */
   int32_t target_ctas;      /* active CTAs the live chunk size aims at (0: per-row rule) */
+  int32_t kv_heads_per_cta; /* 1, or 4 (the four-KV-head CTAs of split_geometry's opts) */
   uint64_t workspace_bytes; /* bytes of workspace the calls below need */
 } pkv_geometry;
 
 /*
  * split_geometry -- choose the split count S from static shapes only.
  *
- * units = num_rows * num_kv_heads * ceil(group / 16);
+ * units = num_rows * (num_kv_heads / kv_heads_per_cta) * ceil(group / 16), where
+ *         kv_heads_per_cta is 4 when the problem allows it (dense rows, SEPARATE
+ *         layout, a multiple of four KV heads, group <= 16: the cache keeps
+ *         the KV heads of a token side by side, and a CTA whose four waves
+ *         read four neighbouring heads of the same records streams faster
+ *         than four CTAs reading one head each) and opts do not ask for 1;
  * cap   = max_blocks_per_row * block_size (dense; with a sliding window W
  *         at most W + 15, the positions from the window start rounded down
  *         to a multiple of 16) or max_candidates (gathered);
@@ -193,8 +202,10 @@ typedef struct {
  * the smallest c with P at most a quarter of them, if the grid then still
  * holds a quarter of the resident CTAs (units * ceil(cap / c) * 4 >=
  * resident); else kept at 64 -- a latency-bound step gains from more,
- * shorter splits.  waves: 2 in the live-balanced mode when 2 P is
- * less than the KV bytes of min_chunk positions, else 1.
+ * shorter splits.  P and the KV bytes are those of a work unit (four KV
+ * heads in the four-head mode).  waves: 2 in the live-balanced mode with
+ * one KV head per CTA when 2 P is less than the KV bytes of min_chunk
+ * positions, else 1.
  * Returns PKV_EINVAL / PKV_EUNSUPPORTED as paged_decode_attention would, or
  * PKV_EHIP if the device query fails.  Does not touch device memory.
  */

@@ -36,13 +36,13 @@ class Problem(ctypes.Structure):
 class GeometryOpts(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "num_cus", "ctas_per_cu", "splits_override", "min_chunk", "max_splits", "waves",
-        "balance")]
+        "balance", "kv_heads_per_cta")]
 
 
 class Geometry(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "num_splits", "min_chunk", "threads", "head_blocks", "grid_x", "grid_y", "grid_z",
-        "target_ctas")] + [("workspace_bytes", ctypes.c_uint64)]
+        "target_ctas", "kv_heads_per_cta")] + [("workspace_bytes", ctypes.c_uint64)]
 
     def as_dict(self):
         return {n: getattr(self, n) for n, _ in self._fields_}
@@ -113,9 +113,9 @@ def make_problem(num_rows, num_heads, num_kv_heads, head_size, v_head_size, bloc
 
 
 def split_geometry(problem: Problem, num_cus=0, ctas_per_cu=0, splits_override=0, min_chunk=0,
-                   max_splits=0, waves=0, balance=0) -> Geometry:
+                   max_splits=0, waves=0, balance=0, kv_heads_per_cta=0) -> Geometry:
     opts = GeometryOpts(int(num_cus), int(ctas_per_cu), int(splits_override), int(min_chunk),
-                        int(max_splits), int(waves), int(balance))
+                        int(max_splits), int(waves), int(balance), int(kv_heads_per_cta))
     g = Geometry()
     _check(load().split_geometry(ctypes.byref(problem), ctypes.byref(opts), ctypes.byref(g)))
     return g

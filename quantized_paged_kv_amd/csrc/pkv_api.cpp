@@ -41,7 +41,22 @@ pkv::Variant variant_of(const pkv_problem& p) {
   v.latent = p.layout == PKV_LATENT;
   v.gathered = p.max_candidates > 0;
   v.ext = p.sliding_window > 0 || p.softcap > 0.0f;
+  v.kvp = 0;
   return v;
+}
+
+// Four KV heads per CTA (split_kvp_kernel): dense rows, separate caches, a
+// multiple of four KV heads and at most 16 query heads per KV head.
+bool kvp_allowed(const pkv_problem& p) {
+  const int group = p.num_heads / p.num_kv_heads;
+  return p.layout == PKV_SEPARATE && p.max_candidates == 0 &&
+         p.num_kv_heads % pkv::kKvHeadsPerCta == 0 && group <= 16;
+}
+
+// Work units per row: (KV head, 16-query-head block), or groups of four KV
+// heads in the four-head mode.
+int64_t units_row_of(const pkv_problem& p, int kv_per_cta) {
+  return (int64_t)(p.num_kv_heads / kv_per_cta) * ceil_div(p.num_heads / p.num_kv_heads, 16);
 }
 
 // Most positions one row can have: the candidate-list capacity (gathered
@@ -111,9 +126,8 @@ uint64_t workspace_bytes_for(const pkv_problem& p, int S) {
 // split).  Live-balanced mode: the work items are at most
 // target + rows * units (each row rounds its split count up by less than one
 // chunk), and never more than the static count.
-int64_t grid_ctas_for(const pkv_problem& p, int S, int target) {
-  const int64_t units = (int64_t)p.num_rows * p.num_kv_heads *
-                        ceil_div(p.num_heads / p.num_kv_heads, 16);
+int64_t grid_ctas_for(const pkv_problem& p, int S, int target, int kv_per_cta) {
+  const int64_t units = (int64_t)p.num_rows * units_row_of(p, kv_per_cta);
   const int64_t all = units * S;
   return target > 0 ? std::min<int64_t>(all, (int64_t)target + units) : all;
 }
@@ -128,7 +142,7 @@ std::unordered_map<int, DeviceInfo> g_dev;
 
 uint64_t variant_key(const pkv::Variant& v) {
   return ((uint64_t)v.cache_dtype << 40) | ((uint64_t)v.head_size << 24) |
-         ((uint64_t)v.v_head_size << 8) | (v.ext << 2) | (v.latent << 1) | v.gathered;
+         ((uint64_t)v.v_head_size << 8) | (v.kvp << 3) | (v.ext << 2) | (v.latent << 1) | v.gathered;
 }
 
 pkv_status device_numbers(const pkv::Variant& v, int* cus, int* occ) {
@@ -165,7 +179,9 @@ pkv_status check_geometry(const pkv_problem& p, const pkv_geometry* g) {
   if (g->min_chunk < 16 || g->min_chunk % 16)
     return fail(PKV_EINVAL, "geometry min_chunk %d is not a positive multiple of 16", g->min_chunk);
   if (g->head_blocks != ceil_div(group, 16) || g->threads != pkv::threads_of(variant_of(p)) ||
-      g->grid_x != grid_ctas_for(p, g->num_splits, g->target_ctas) || g->grid_y != 1 ||
+      (g->kv_heads_per_cta != 1 && g->kv_heads_per_cta != pkv::kKvHeadsPerCta) ||
+      (g->kv_heads_per_cta != 1 && !kvp_allowed(p)) ||
+      g->grid_x != grid_ctas_for(p, g->num_splits, g->target_ctas, g->kv_heads_per_cta) || g->grid_y != 1 ||
       g->grid_z != 1 || g->workspace_bytes != workspace_bytes_for(p, g->num_splits) ||
       g->target_ctas < 0 || (g->target_ctas > 0 && p.num_rows > kMaxBalancedRows))
     return fail(PKV_EINVAL, "geometry does not belong to this problem (call split_geometry)");
@@ -254,6 +270,8 @@ pkv::SplitArgs split_args(const pkv_problem& p, const pkv_geometry& g, const Ptr
   a.kv_heads = p.num_kv_heads;
   a.group = p.num_heads / p.num_kv_heads;
   a.head_blocks = g.head_blocks;
+  a.units_row = (int)units_row_of(p, g.kv_heads_per_cta);
+  a.kvp = g.kv_heads_per_cta == pkv::kKvHeadsPerCta;
   a.block_size = p.block_size;
   a.log2_block = __builtin_ctz((unsigned)p.block_size);
   a.max_blocks_per_row = p.max_blocks_per_row;
@@ -390,7 +408,20 @@ pkv_status split_geometry(const pkv_problem* problem, const pkv_geometry_opts* o
 
   const int group = p.num_heads / p.num_kv_heads;
   const int head_blocks = ceil_div(group, 16);
-  const int64_t units = std::max<int64_t>(1, (int64_t)p.num_rows * p.num_kv_heads * head_blocks);
+  // KV heads per CTA: four when the problem allows it (whole-record reads),
+  // unless the caller asks for one
+  if (o.kv_heads_per_cta != 0 && o.kv_heads_per_cta != 1 && o.kv_heads_per_cta != pkv::kKvHeadsPerCta)
+    return fail(PKV_EINVAL, "kv_heads_per_cta must be 0, 1 or %d", pkv::kKvHeadsPerCta);
+  if (o.kv_heads_per_cta == pkv::kKvHeadsPerCta && !kvp_allowed(p))
+    return fail(PKV_EUNSUPPORTED, "four KV heads per CTA need dense rows, the SEPARATE layout, a "
+                                  "multiple of four KV heads and at most 16 query heads per KV head");
+  // (automatic for head sizes up to 128: measured faster there; larger
+  // heads need more registers per wave than two waves per SIMD allow)
+  const int kv_per_cta = o.kv_heads_per_cta ? o.kv_heads_per_cta
+                         : (kvp_allowed(p) && p.head_size <= 128 ? pkv::kKvHeadsPerCta : 1);
+  pkv::Variant var = variant_of(p);
+  var.kvp = kv_per_cta == pkv::kKvHeadsPerCta;
+  const int64_t units = std::max<int64_t>(1, (int64_t)p.num_rows * units_row_of(p, kv_per_cta));
   const int64_t cap = positions_cap(p);
 
   // The device balances chunk sizes across rows from the live lengths when
@@ -401,7 +432,7 @@ pkv_status split_geometry(const pkv_problem* problem, const pkv_geometry_opts* o
   int cus = o.num_cus, occ = o.ctas_per_cu;
   if (cus == 0 || occ == 0) {
     int qc = 0, qo = 0;
-    st = device_numbers(variant_of(p), &qc, occ == 0 ? &qo : nullptr);
+    st = device_numbers(var, &qc, occ == 0 ? &qo : nullptr);
     if (st != PKV_OK) return st;
     if (cus == 0) cus = qc;
     if (occ == 0) occ = qo;
@@ -411,9 +442,12 @@ pkv_status split_geometry(const pkv_problem* problem, const pkv_geometry_opts* o
   // unless a split's partial (written once, read once by the combine) is at
   // least half the KV bytes of a min_chunk -- then halving the chunk costs
   // more traffic than it saves (latent rows: 16 heads x 512 FP32 per split).
-  const int64_t partial_bytes = (int64_t)(p.num_heads / p.num_kv_heads) * (p.v_head_size + 2) * 4;
-  const int64_t row_bytes = (int64_t)(p.layout == PKV_LATENT ? p.head_size
-                                                             : p.head_size + p.v_head_size) *
+  // (per work unit: its KV heads' query heads, and the KV bytes of one
+  // position of all its KV heads)
+  const int64_t partial_bytes =
+      (int64_t)kv_per_cta * (p.num_heads / p.num_kv_heads) * (p.v_head_size + 2) * 4;
+  const int64_t row_bytes = (int64_t)kv_per_cta *
+                            (p.layout == PKV_LATENT ? p.head_size : p.head_size + p.v_head_size) *
                             (p.cache_dtype == PKV_F16 ? 2 : 1);
   // Automatic chunk floor: 64 positions, raised to the power of two that
   // keeps a split's partial (written once, read back once by the combine) at
@@ -436,7 +470,10 @@ pkv_status split_geometry(const pkv_problem* problem, const pkv_geometry_opts* o
       min_chunk = (int)c4;
   }
   const bool cheap_partials = 2 * partial_bytes < row_bytes * min_chunk;
-  const int waves = waves_req ? waves_req : (balanced && cheap_partials ? 2 : 1);
+  // (four KV heads per CTA: one round; their CTAs already carry four
+  // units' partials, and a second round measured slower)
+  const int waves = waves_req ? waves_req
+                              : (balanced && cheap_partials && kv_per_cta == 1 ? 2 : 1);
   const int64_t target = (int64_t)waves * cus * occ;
   int S;
   if (o.splits_override > 0) {
@@ -463,7 +500,8 @@ pkv_status split_geometry(const pkv_problem* problem, const pkv_geometry_opts* o
   out->threads = pkv::threads_of(variant_of(p));
   out->head_blocks = head_blocks;
   out->target_ctas = balanced ? (int32_t)std::min<int64_t>(target, INT32_MAX) : 0;
-  const int64_t grid = grid_ctas_for(p, S, out->target_ctas);
+  out->kv_heads_per_cta = kv_per_cta;
+  const int64_t grid = grid_ctas_for(p, S, out->target_ctas, kv_per_cta);
   if (grid > INT32_MAX) return fail(PKV_EUNSUPPORTED, "too many CTAs (%lld)", (long long)grid);
   out->grid_x = (int32_t)grid;
   out->grid_y = 1;

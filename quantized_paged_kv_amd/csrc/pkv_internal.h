@@ -23,6 +23,8 @@ struct SplitArgs {
   float* ws_acc;                // [rows, heads, S, VD]
   float* ws_ml;                 // [rows, heads, S, 2]
   int rows, heads, kv_heads, group, head_blocks;
+  int units_row;                // work units per row: kv_heads * head_blocks, or kv_heads / 4
+  int kvp;                      // 1: four KV heads per CTA (split_kvp_kernel)
   int block_size, log2_block, max_blocks_per_row, num_pool_blocks, max_candidates;
   int num_splits, min_chunk;
   int target_ctas;              // > 0: live chunk from the total work of all rows
@@ -78,6 +80,7 @@ struct Variant {
   int latent;
   int gathered;
   int ext;          // a sliding window or a soft cap is set
+  int kvp;          // four KV heads per CTA (dense rows, separate caches)
 };
 
 constexpr int kWaves = 4;          // waves per split-kernel CTA
@@ -90,6 +93,7 @@ inline int threads_of(const Variant& v) {
 }
 constexpr int kMaxSplits = 64;     // the combine holds one split per lane
 constexpr int kMaxBalancedRows = 1024;  // live-balanced chunks up to this many rows
+constexpr int kKvHeadsPerCta = 4;       // KV heads of one CTA in the four-head mode
 
 // Launchers; return hipSuccess or the launch error.  `supported` reports
 // whether a variant was compiled.

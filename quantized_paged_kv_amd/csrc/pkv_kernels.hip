@@ -338,7 +338,7 @@ __device__ __forceinline__ void scaled_scores(const SplitArgs& a, const f32x4& a
 template <bool GATHER, bool EXT>
 __device__ __forceinline__ bool locate_balanced(const SplitArgs& a, int lane, Work& w) {
   const int S = a.num_splits;
-  const int units_row = a.kv_heads * a.head_blocks;
+  const int units_row = a.units_row;
   const int cap = a.max_blocks_per_row * a.block_size;
   const int c = blockIdx.x;
   constexpr int NR = kMaxBalancedRows / 64;
@@ -420,7 +420,7 @@ __device__ __forceinline__ bool locate_balanced(const SplitArgs& a, int lane, Wo
 // split < S) list; nothing is read.
 __device__ __forceinline__ void static_item(const SplitArgs& a, Work& w) {
   const int S = a.num_splits;
-  const int units_row = a.kv_heads * a.head_blocks;
+  const int units_row = a.units_row;
   const int c = blockIdx.x;
   w.r = c / (units_row * S);
   const int rem = c - w.r * units_row * S;
@@ -1213,6 +1213,325 @@ split_kernel(const SplitArgs a) {
   }
 }
 
+// ---- four KV heads per CTA (dense rows, separate K / V caches) -------------
+//
+// The cache keeps the rows of all KV heads of a token side by side
+// ([block, token, kv_head, dim]).  A CTA per KV head reads only its slice of
+// every token record, at its own pace; on MI355X a streaming probe reads
+// such per-head slices at 5.4-5.6 TB/s, but 6.3 TB/s when the four waves of
+// one CTA read four neighbouring slices of the same records together.  So
+// when a problem has a multiple of four KV heads (and at most 16 query
+// heads per KV head), one CTA takes KV heads 4u .. 4u + 3 of a row and
+// split: wave w takes KV head 4u + w and every tile of the split's range,
+// with split_kernel's per-tile code (gather, exact conversion, MFMA scores,
+// online softmax, PV).  Each wave holds the complete state of its query
+// heads, so the waves need no merge: every wave writes its own partials
+// straight from registers.
+
+template <int CT, int D, int VD, bool EXT>
+__global__ void __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(SplitCfg<CT, D, VD, false, false>::MIN_WAVES)))
+split_kvp_kernel(const SplitArgs a) {
+  using C = SplitCfg<CT, D, VD, false, false>;
+  constexpr int W = kWaves;  // KV heads per CTA
+  constexpr int NST = C::NST;
+  static_assert(C::CPL % 4 == 0, "float4 groups of channels per lane");
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int li = lane & 15;
+  const int lj = lane >> 4;
+  const int S = a.num_splits;
+  const int KVH = a.kv_heads;
+  const int group = a.group;
+
+  // ---- prologue (as split_kernel, for four KV heads)
+  const bool balanced = a.target_ctas > 0;
+  Work wk;
+  int raw_npos = 0;
+  if (balanced) {
+    if (!locate_balanced<false, EXT>(a, lane, wk)) return;  // padding CTA
+  } else {
+    static_item(a, wk);
+    raw_npos = uniform_load(a.seq_lens, wk.r);
+  }
+  // the unit: KV heads 4u .. 4u + 3 and their query heads (contiguous)
+  wk.g = W * wk.u;
+  wk.hb = 0;
+  wk.h0 = wk.g * group;
+  wk.nh = W * group;
+  const int r = wk.r;
+  const int g = wk.g + wave;     // this wave's KV head
+  const int hw0 = g * group;     // its first query head
+
+  __shared__ uint4 s_q[W][C::NKS * 64];
+  __shared__ float s_err[W][C::NKS * 64];
+  __shared__ int s_flag[2 * W];  // [w]: deep tail, [W + w]: folding, of wave w
+  __shared__ float s_vs[W][VD];
+  constexpr int QPT = (C::NKS * 64 + kThreads - 1) / kThreads;
+  uint4 qraw[W][QPT];
+  float4 ksc[W][QPT][2];
+  Scales sc[W];
+  const int32_t* bt_row = a.block_table + (size_t)r * a.max_blocks_per_row;
+  // every wave walks every tile: the block ids of the split's first 64 tiles
+  WaveBlocks wb{bt_row, wk.base + split_p0(a, wk), 0, 1, 0, 0};
+  wb.load(a, 0, lane);
+  auto unit_of = [&](int u4) __attribute__((always_inline)) {
+    Work w = wk;
+    w.g = wk.g + u4;
+    w.h0 = w.g * group;
+    w.nh = group;
+    return w;
+  };
+#pragma unroll
+  for (int u4 = 0; u4 < W; ++u4) {
+    q_issue<C::NKS, C::EB, D>(a, unit_of(u4), qraw[u4], ksc[u4]);
+    sc[u4] = load_scales<VD>(a, wk.g + u4);
+  }
+  finish_item<false, EXT>(a, wk, balanced, raw_npos, 0);
+  const int len = wk.len;
+  if constexpr (EXT)
+    if (!balanced && wk.base > 0) {
+      wb.p0 = wk.base + split_p0(a, wk);
+      wb.load(a, 0, lane);
+    }
+  const int skip = wk.lo - wk.base;
+  const int base = wk.base;
+  (void)len;
+
+  int p0, p1;
+  if (!split_range<VD>(a, wk, p0, p1)) return;
+  const int split = wk.split;
+  const int ntiles = (p1 - p0 + 15) >> 4;
+
+  const uint32_t tok_k = (uint32_t)KVH * C::KROW;
+  const uint32_t tok_v = (uint32_t)KVH * C::VROW;
+  const uint32_t koff = (uint32_t)li * tok_k + (uint32_t)g * C::KROW + 16u * lj;
+  const uint32_t voff = (uint32_t)(4 * lj) * tok_v + (uint32_t)g * C::VROW + (uint32_t)li * C::VSEG;
+
+  // loads of tile t (split_kernel's dense branch)
+  auto issue = [&](Tile<C>& T, int t) __attribute__((always_inline)) {
+    const int tp = p0 + 16 * t;
+    uint32_t vm = 0;
+    int blk = 0;
+    bool bv = false;
+    if (t < ntiles) {
+      blk = wb.of(a, t, lane);
+      bv = blk >= 0 && blk < a.num_pool_blocks;
+    }
+    const int64_t s0 = bv ? ((int64_t)blk << a.log2_block) + ((base + tp) & (a.block_size - 1)) : 0;
+    const uint32_t nv = bv ? (uint32_t)min(16, p1 - tp) : 0u;
+    const auto krs = make_rsrc(a.key_cache + s0 * tok_k, nv * tok_k);
+#pragma unroll
+    for (int s = 0; s < C::NKL; ++s) buffer_bytes<16>(krs, koff + 64 * s, 0, &T.k[4 * s]);
+    const auto vrs = make_rsrc(a.value_cache + s0 * tok_v, nv * tok_v);
+    if (EXT && tp < skip) {
+      const int sk = skip - tp;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int row = 4 * lj + q;
+        const uint32_t past = row < sk ? kPastDescriptor : 0u;
+        buffer_bytes<C::VSEG>(vrs, voff + (uint32_t)q * tok_v + past, 0, T.v[q]);
+        vm |= (row < (int)nv && row >= sk) ? (1u << q) : 0u;
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        buffer_bytes<C::VSEG>(vrs, voff + (uint32_t)q * tok_v, 0, T.v[q]);
+        vm |= (4 * lj + q < (int)nv) ? (1u << q) : 0u;
+      }
+    }
+    T.vmask = vm;
+  };
+
+  f32x4 acc[C::NCT];
+#pragma unroll
+  for (int ct = 0; ct < C::NCT; ++ct) acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_ref = kNegInf;
+  float l_part = 0.0f;
+  float smin = __builtin_inff();
+  const uint4* const sq = s_q[wave];
+
+  // split_kernel's tile consumer, on this wave's query block
+  auto consume = [&](const Tile<C>& T, auto lo) __attribute__((always_inline)) {
+    constexpr bool LO = decltype(lo)::value;
+    f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < C::NKL; ++s) {
+      if constexpr (C::EB == 2) {
+        const half8 kop = __builtin_bit_cast(
+            half8, uint4{T.k[4 * s], T.k[4 * s + 1], T.k[4 * s + 2], T.k[4 * s + 3]});
+        const half8 qop = __builtin_bit_cast(half8, sq[s * 64 + lane]);
+        sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop, qop, sacc, 0, 0, 0);
+      } else {
+        const half4 c0 = codes4_to_half4<CT>(T.k[4 * s + 0]);
+        const half4 c1 = codes4_to_half4<CT>(T.k[4 * s + 1]);
+        const half4 c2 = codes4_to_half4<CT>(T.k[4 * s + 2]);
+        const half4 c3 = codes4_to_half4<CT>(T.k[4 * s + 3]);
+        const half8 k0 = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
+        const half8 k1 = {c2[0], c2[1], c2[2], c2[3], c3[0], c3[1], c3[2], c3[3]};
+        const half8 q0 = __builtin_bit_cast(half8, sq[(2 * s) * 64 + lane]);
+        const half8 q1 = __builtin_bit_cast(half8, sq[(2 * s + 1) * 64 + lane]);
+        sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(k0, q0, sacc, 0, 0, 0);
+        sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(k1, q1, sacc, 0, 0, 0);
+      }
+    }
+    float x[4];
+    scaled_scores<EXT>(a, sacc, x);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const bool valid = (T.vmask >> q) & 1u;
+      x[q] = valid ? x[q] : kNegInf;
+      smin = fminf(smin, valid ? x[q] : __builtin_inff());
+    }
+    float mt = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+    mt = fmaxf(mt, __shfl_xor(mt, 16));
+    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    if (__any(mt > m_ref + kRescaleSlack)) {
+      const float mn = fmaxf(m_ref, mt);
+      const float alpha = (m_ref == kNegInf) ? 0.0f : __builtin_amdgcn_exp2f((m_ref - mn) * kLog2e);
+      l_part *= alpha;
+#pragma unroll
+      for (int ct = 0; ct < C::NCT; ++ct) acc[ct] *= alpha;
+      m_ref = mn;
+    }
+    const float mu = (m_ref == kNegInf) ? 0.0f : m_ref;
+    float p[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) p[q] = __builtin_amdgcn_exp2f((x[q] - mu) * kLog2e);
+    l_part += (p[0] + p[1]) + (p[2] + p[3]);
+    half4 pop, pol;
+    split_prob<LO>(p, pop, pol);
+    if constexpr (C::EB == 2) {
+#pragma unroll
+      for (int w = 0; w < C::NVW; ++w) {
+        const uint32_t r0 = T.v[0][w], r1 = T.v[1][w];
+        const uint32_t r2 = T.v[2][w], r3 = T.v[3][w];
+        const uint32_t a01 = perm(r1, r0, 0x05040100u), a23 = perm(r3, r2, 0x05040100u);
+        const uint32_t b01 = perm(r1, r0, 0x07060302u), b23 = perm(r3, r2, 0x07060302u);
+        const half4 va = __builtin_bit_cast(half4, uint2{a01, a23});
+        const half4 vb = __builtin_bit_cast(half4, uint2{b01, b23});
+        acc[2 * w] = __builtin_amdgcn_mfma_f32_16x16x16f16(va, pop, acc[2 * w], 0, 0, 0);
+        acc[2 * w + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(vb, pop, acc[2 * w + 1], 0, 0, 0);
+        if constexpr (LO) {
+          acc[2 * w] = __builtin_amdgcn_mfma_f32_16x16x16f16(va, pol, acc[2 * w], 0, 0, 0);
+          acc[2 * w + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(vb, pol, acc[2 * w + 1], 0, 0, 0);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int w = 0; w < C::NVW; ++w) {
+        const uint32_t r0 = T.v[0][w], r1 = T.v[1][w];
+        const uint32_t r2 = T.v[2][w], r3 = T.v[3][w];
+        const uint32_t t0 = perm(r1, r0, 0x05010400u), t1 = perm(r1, r0, 0x07030602u);
+        const uint32_t t2 = perm(r3, r2, 0x05010400u), t3 = perm(r3, r2, 0x07030602u);
+        const uint32_t o0 = perm(t2, t0, 0x05040100u), o1 = perm(t2, t0, 0x07060302u);
+        const uint32_t o2 = perm(t3, t1, 0x05040100u), o3 = perm(t3, t1, 0x07060302u);
+        const half4 h0 = codes4_to_half4<CT>(o0), h1 = codes4_to_half4<CT>(o1);
+        const half4 h2 = codes4_to_half4<CT>(o2), h3 = codes4_to_half4<CT>(o3);
+        acc[4 * w + 0] = __builtin_amdgcn_mfma_f32_16x16x16f16(h0, pop, acc[4 * w + 0], 0, 0, 0);
+        acc[4 * w + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(h1, pop, acc[4 * w + 1], 0, 0, 0);
+        acc[4 * w + 2] = __builtin_amdgcn_mfma_f32_16x16x16f16(h2, pop, acc[4 * w + 2], 0, 0, 0);
+        acc[4 * w + 3] = __builtin_amdgcn_mfma_f32_16x16x16f16(h3, pop, acc[4 * w + 3], 0, 0, 0);
+        if constexpr (LO) {
+          acc[4 * w + 0] = __builtin_amdgcn_mfma_f32_16x16x16f16(h0, pol, acc[4 * w + 0], 0, 0, 0);
+          acc[4 * w + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(h1, pol, acc[4 * w + 1], 0, 0, 0);
+          acc[4 * w + 2] = __builtin_amdgcn_mfma_f32_16x16x16f16(h2, pol, acc[4 * w + 2], 0, 0, 0);
+          acc[4 * w + 3] = __builtin_amdgcn_mfma_f32_16x16x16f16(h3, pol, acc[4 * w + 3], 0, 0, 0);
+        }
+      }
+    }
+  };
+
+  // ---- main loop: every wave walks all tiles; NST - 1 in flight
+  Tile<C> buf[NST];
+#pragma unroll
+  for (int i = 0; i < NST - 1; ++i) issue(buf[i], i);
+#pragma unroll
+  for (int u4 = 0; u4 < W; ++u4) {
+    q_stage<C::NKS, C::EB, D>(qraw[u4], ksc[u4], sc[u4].k_tensor, s_q[u4], s_err[u4]);
+    stage_scales<VD>(a, sc[u4], s_vs[u4]);
+  }
+  __syncthreads();
+  const bool fold = fold_over_budget<CT, C::NKS>(a, s_err[wave], group, lane);
+
+  auto tile_loop = [&](auto lo) __attribute__((always_inline)) {
+    for (int t = 0; t < ntiles; t += NST) {
+#pragma unroll
+      for (int st = 0; st < NST; ++st) {
+        const int tt = t + st;
+        if (tt >= ntiles) break;
+        issue(buf[(st + NST - 1) % NST], tt + NST - 1);
+        __builtin_amdgcn_sched_barrier(0);
+        consume(buf[st], lo);
+      }
+    }
+  };
+  tile_loop(std::integral_constant<bool, kResidualTile>{});
+  const bool deep = smin != __builtin_inff() && smin - m_ref < kTailLog;
+  l_part += __shfl_xor(l_part, 16);
+  l_part += __shfl_xor(l_part, 32);
+  {
+    const bool dw = __any(deep);
+    if (lane == 0) {
+      s_flag[wave] = dw ? 1 : 0;
+      s_flag[W + wave] = fold ? 1 : 0;
+    }
+  }
+  __syncthreads();
+  {
+    // robust numerics: a CTA-uniform decision over the four KV heads
+    bool fp32 = false;
+#pragma unroll
+    for (int w = 0; w < W; ++w) {
+      const bool armed = s_flag[w] != 0 &&
+                         value_bound<CT, VD>(a, sc[w], s_vs[w], lane) * (float)(p1 - p0) >= kTailArm;
+      fp32 |= s_flag[W + w] != 0 || armed;
+    }
+    if (fp32) {
+      // s_q is free: it holds the FP32 path's per-wave scratch; the per-tensor
+      // scales are the same for every KV head (sc[0]) and the per-channel
+      // value scales come from s_vs
+      static_assert(W * (VD + 2) * 4 <= (int)sizeof(s_q), "FP32-path scratch fits the query stage");
+#pragma unroll 1
+      for (int u4 = 0; u4 < W; ++u4)
+        exact_partial<CT, D, VD, false, false, W, EXT>(a, unit_of(u4), p0, p1, sc[0], s_vs[u4],
+                                                       reinterpret_cast<float*>(&s_q[0][0]));
+      return;
+    }
+  }
+
+  // ---- this wave's partials, straight from registers: lane (li, lj) holds
+  // channels (4 lj + q) CPL + ct of head li
+  if (li < group) {
+    const int h = hw0 + li;
+    const size_t pair = (size_t)r * a.heads + h;
+    const size_t pidx = pair * S + split;
+    Final fin{0.0f, kNegInf};
+    if (a.direct) {
+      fin = final_of(a, h, m_ref, l_part);
+      if (a.lse_out && lj == 0) a.lse_out[pair] = fin.lse;
+    } else if (lj == 0) {
+      reinterpret_cast<float2*>(a.ws_ml)[pidx] = make_float2(m_ref, l_part);
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+#pragma unroll
+      for (int c4 = 0; c4 < C::CPL; c4 += 4) {
+        const int ch = (4 * lj + q) * C::CPL + c4;
+        float4 o = make_float4(acc[c4][q], acc[c4 + 1][q], acc[c4 + 2][q], acc[c4 + 3][q]);
+        o.x *= a.v_mult * v_scale_of(a, sc[0], s_vs[wave], ch);
+        o.y *= a.v_mult * v_scale_of(a, sc[0], s_vs[wave], ch + 1);
+        o.z *= a.v_mult * v_scale_of(a, sc[0], s_vs[wave], ch + 2);
+        o.w *= a.v_mult * v_scale_of(a, sc[0], s_vs[wave], ch + 3);
+        if (a.direct)
+          store_final<VD>(a, pair, ch, o, fin.f);
+        else
+          *reinterpret_cast<float4*>(a.ws_acc + pidx * VD + ch) = o;
+      }
+    }
+  }
+}
+
 // ---- the latent (absorbed-MLA) kernel -------------------------------------
 //
 // One cache row per token supplies K (all 576 channels) and V (its first 512
@@ -1839,6 +2158,12 @@ __global__ void __launch_bounds__(256) combine_small_kernel(const CombineArgs a)
 template <int CT, int D, int VD, bool LAT, bool GA, bool EXT>
 static hipError_t launch_one(const SplitArgs& a, hipStream_t stream) {
   dim3 grid(a.grid_ctas);
+  if constexpr (!LAT && !GA) {
+    if (a.kvp) {
+      hipLaunchKernelGGL((split_kvp_kernel<CT, D, VD, EXT>), grid, dim3(kThreads), 0, stream, a);
+      return hipGetLastError();
+    }
+  }
   if constexpr (LAT)
     hipLaunchKernelGGL((latent_kernel<CT, GA, EXT>), grid, dim3(LatCfg<CT, GA>::NT), 0, stream, a);
   else
@@ -1847,7 +2172,12 @@ static hipError_t launch_one(const SplitArgs& a, hipStream_t stream) {
 }
 
 template <int CT, int D, int VD, bool LAT, bool GA, bool EXT>
-static hipError_t occupancy_one(int* n) {
+static hipError_t occupancy_one(int* n, bool kvp) {
+  if constexpr (!LAT && !GA) {
+    if (kvp)
+      return hipOccupancyMaxActiveBlocksPerMultiprocessor(n, split_kvp_kernel<CT, D, VD, EXT>,
+                                                           kThreads, 0);
+  }
   if constexpr (LAT)
     return hipOccupancyMaxActiveBlocksPerMultiprocessor(n, latent_kernel<CT, GA, EXT>,
                                                          LatCfg<CT, GA>::NT, 0);
@@ -1902,7 +2232,7 @@ hipError_t launch_split(const Variant& v, const SplitArgs& a, hipStream_t stream
 
 hipError_t split_occupancy(const Variant& v, int* ctas_per_cu) {
   hipError_t err = hipErrorInvalidValue;
-#define PKV_OCC(CT, D, VD, LAT, GA, EXT) err = occupancy_one<CT, D, VD, LAT, GA, EXT>(ctas_per_cu)
+#define PKV_OCC(CT, D, VD, LAT, GA, EXT) err = occupancy_one<CT, D, VD, LAT, GA, EXT>(ctas_per_cu, v.kvp != 0)
   PKV_FOR_VARIANT(v, PKV_OCC);
 #undef PKV_OCC
   return err;

@@ -60,7 +60,12 @@ def test_geometry_never_depends_on_live_data_and_sizes_workspace():
     S = g1.num_splits
     assert g1.workspace_bytes == 16 * 32 * S * (128 + 2) * 4
     assert (g1.grid_y, g1.grid_z) == (1, 1)
-    assert g1.grid_x == min(16 * 8 * S, g1.target_ctas + 16 * 8)
+    # 8 KV heads, group 4: four KV heads per CTA, so two units per row
+    assert g1.kv_heads_per_cta == 4
+    assert g1.grid_x == min(16 * 2 * S, g1.target_ctas + 16 * 2)
+    g3 = pkv.split_geometry(p, num_cus=256, ctas_per_cu=2, kv_heads_per_cta=1)
+    assert g3.kv_heads_per_cta == 1
+    assert g3.grid_x == min(16 * 8 * g3.num_splits, g3.target_ctas + 16 * 8)
     # more heads per KV head than one 16-wide tile: head blocks
     p2 = pkv.make_problem(2, 40, 2, 128, 128, 16, 64, 500)
     g = pkv.split_geometry(p2, num_cus=256, ctas_per_cu=2)

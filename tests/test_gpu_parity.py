@@ -474,3 +474,55 @@ def test_many_rows(rows, balance):
     got, lse, g = run_gpu(inp, balance=balance)
     assert (g.target_ctas > 0) == (balance == 1)
     assert_close_to_oracle(got, lse, ref, ref_lse, what=f"{rows} rows balance={balance}")
+
+
+# ---------------------------------------------------------------------------
+# four KV heads per CTA (chosen automatically with a multiple of four KV
+# heads, at most 16 query heads per KV head and head size <= 128): against
+# the oracle, next to one KV head per CTA
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("cache,D", [(c, D) for c in ("f16", "i8", "fp8") for D in (64, 128, 256)],
+                         ids=lambda v: str(v))
+@pytest.mark.parametrize("heads,kvh", [(32, 8), (64, 8), (12, 4)])
+def test_four_kv_heads_per_cta(cache, D, heads, kvh):
+    inp = _small(cache, D, D, "separate", False, seed=21, heads=heads, kvh=kvh)
+    ref, ref_lse = oracle.paged_decode(inp)
+    for S in (1, 5):
+        for kpc in (1, 4):
+            announce(f"{cache} D={D} {heads}q/{kvh}kv S={S} kv_heads_per_cta={kpc}")
+            got, lse, g = run_gpu(inp, splits_override=S, min_chunk=16, kv_heads_per_cta=kpc)
+            assert g.kv_heads_per_cta == kpc
+            assert_close_to_oracle(got, lse, ref, ref_lse, what=f"{cache} D={D} S={S} kpc={kpc}")
+
+
+def test_four_kv_heads_per_cta_is_the_default_where_allowed():
+    import quantized_paged_kv_amd as pkv
+    from workloads.device import problem_kwargs
+
+    for name, expect in (("C3", 4), ("X4096b8i8", 4), ("C2", 1), ("C4", 1), ("C5", 1)):
+        inp, _ = named(name)
+        g = pkv.split_geometry(pkv.make_problem(**problem_kwargs(inp.problem)))
+        assert g.kv_heads_per_cta == expect, name
+
+
+@pytest.mark.parametrize("case", ["fold", "tail"])
+def test_four_kv_heads_per_cta_fp32_path(case):
+    # every CTA takes the FP32 path: folding over budget (large queries), or
+    # a deep tail with a large value scale
+    if case == "fold":
+        inp = _small("i8", 128, 128, "separate", False, seed=13, quant="channel", heads=32, kvh=8)
+        inp.query[...] = (inp.query.astype(np.float32) * 200.0).astype(np.float16)
+        rel = 1e-4
+    else:
+        inp = _small("i8", 128, 128, "separate", False, seed=11, quant="tensor", heads=32, kvh=8,
+                     sink=False)
+        inp.query[...] = (inp.query.astype(np.float32) * 6.0).astype(np.float16)
+        inp.v_scale = (inp.v_scale * 2.0 ** 20).astype(np.float32)
+        rel = 1e-3
+    ref, ref_lse = oracle.paged_decode(inp)
+    for S in (1, 2):
+        announce(f"four KV heads per CTA, FP32 path ({case}), S={S}")
+        got, lse, g = run_gpu(inp, splits_override=S, min_chunk=16, out_dtype="f32",
+                              kv_heads_per_cta=4)
+        _near_exact(got, ref, lse, ref_lse, rel)
