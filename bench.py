@@ -269,6 +269,15 @@ def _dispatch_resources(path: str, kernel_name: str):
     return None
 
 
+def _attention_kernel(counters: dict, layout: str) -> str:
+    """The attention kernel's short name among the profiled kernels."""
+    names = ("latent_kernel",) if layout == "latent" else ("split_kvp_kernel", "split_kernel")
+    for n in names:
+        if any(f"pkv::{n}" in k for k in counters):
+            return n
+    raise KeyError(f"no attention kernel ({names}) among {list(counters)}")
+
+
 def _pick(counters: dict, fragment: str):
     hits = [k for k in counters if fragment in k]
     return (hits[0], counters[hits[0]]) if hits else (None, {})
@@ -281,8 +290,8 @@ def summarize_counters(tag_dir: str, w: str) -> str:
 
     inp = workloads.workload(w)
     p = inp.problem
-    kernel = "latent_kernel" if p.layout == "latent" else "split_kernel"
     fetch = _read_counters(os.path.join(tag_dir, f"pmc_FETCH_SIZE_{w}"))
+    kernel = _attention_kernel(fetch, p.layout)
     write = _read_counters(os.path.join(tag_dir, f"pmc_WRITE_SIZE_{w}"))
     sq = _read_counters(os.path.join(tag_dir, f"pmc_SQ_{w}"))
     cf = _read_counters(os.path.join(tag_dir, "pmc_FETCH_SIZE_copy"))
@@ -557,7 +566,8 @@ def main():
         dims = p.head_size + p.v_head_size
         flops = int(live_token_counts(inp).sum()) * p.heads * 2 * dims
         tflops = flops / (ms_split * 1e-3) / 1e12
-    kernel = "latent_kernel" if p.layout == "latent" else "split_kernel"
+    kernel = ("latent_kernel" if p.layout == "latent" else
+              "split_kvp_kernel" if geo.kv_heads_per_cta == 4 else "split_kernel")
     traffic = read_traffic(kernel, args.workload)
     log(f"step {ms_step * 1e3:.2f} us ({value:.0f} GB/s), split kernel {ms_split * 1e3:.2f} us "
         f"({achieved:.0f} GB/s)")
