@@ -85,11 +85,12 @@ struct Variant {
 
 constexpr int kWaves = 4;          // waves per split-kernel CTA
 constexpr int kThreads = 64 * kWaves;
-// waves per CTA of the latent kernel with one-byte codes (with FP16 codes it
-// uses kWaves)
+// waves per group and groups per CTA of the latent kernel with one-byte
+// codes (with FP16 codes it runs one group of kWaves)
 constexpr int kLatentWaves = 4;
+constexpr int kLatentGroups = 1;
 inline int threads_of(const Variant& v) {
-  return (v.latent && v.cache_dtype != PKV_F16) ? 64 * kLatentWaves : kThreads;
+  return (v.latent && v.cache_dtype != PKV_F16) ? 64 * kLatentWaves * kLatentGroups : kThreads;
 }
 constexpr int kMaxSplits = 64;     // the combine holds one split per lane
 constexpr int kMaxBalancedRows = 1024;  // live-balanced chunks up to this many rows

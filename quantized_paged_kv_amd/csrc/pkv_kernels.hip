@@ -1535,19 +1535,30 @@ split_kvp_kernel(const SplitArgs a) {
 // ---- the latent (absorbed-MLA) kernel -------------------------------------
 //
 // One cache row per token supplies K (all 576 channels) and V (its first 512
-// channels).  A CTA of W = 4 waves walks its position range in rounds of W
-// 16-token tiles.  In round rd wave w
+// channels).  A CTA holds G groups of W = 4 waves (G = 2 for one-byte codes,
+// so that every SIMD runs two waves and one wave's dependency stalls are
+// filled by the other's work) and walks its position range in rounds of
+// G W 16-token tiles; group j takes the j-th run of W tiles of a round.
+// In a round, wave w of a group
 //   * computes the scores S^T = K Q'^T of tile w from its K registers
-//     (fetched two rounds ahead) and publishes them in LDS,
+//     (fetched two rounds ahead) and publishes the tile's maximum per head
+//     in LDS,
 //   * copies the tile's raw codes into the round's LDS stage (64 rows),
-//   * runs, like every wave, the online softmax over all 16 W tokens (so all
-//     waves hold the same running maximum and sum), and
-//   * accumulates V channels [512 w / W, 512 (w + 1) / W) of all tokens of
-//     the round, reading the V^T operands from the stage with the LDS
-//     transpose reads.
+//   * takes the group's maximum over the W tile maxima (so the group's waves
+//     hold the same running reference maximum), turns its own tile's scores
+//     into probabilities and publishes them in LDS, and
+//   * accumulates V channels [512 w / W, 512 (w + 1) / W) of the group's
+//     tokens, reading the V^T operands from the group's stage with the LDS
+//     transpose reads and the probabilities of all W tiles.
+// Each wave evaluates the exponentials of its own tile only; the running
+// sums of a group's waves are added at the end.
 // Each row therefore crosses HBM and L2 once, V needs no registers while in
-// flight, and each wave keeps a 16 x (512 / W) accumulator.
+// flight, and each wave keeps a 16 x (512 / W) accumulator.  At the end the
+// groups' states (m, l, accumulator) are merged in LDS, in group order.
 // Stage rows are padded to keep LDS bank conflicts low.
+
+template <int N>
+using ic = std::integral_constant<int, N>;
 
 template <int CT, bool GATHER>
 struct LatCfg {
@@ -1557,8 +1568,10 @@ struct LatCfg {
   static constexpr int NKS = D / 32;
   static constexpr int NKL = KROW / 64;          // 16-byte K loads per lane per tile
   static constexpr int NKW = NKL * 4;
-  static constexpr int W = EB == 1 ? kLatentWaves : kWaves;  // waves per CTA
-  static constexpr int NT = 64 * W;              // threads per CTA
+  static constexpr int W = EB == 1 ? kLatentWaves : kWaves;  // waves per group
+  static constexpr int G = EB == 1 ? kLatentGroups : 1;      // groups per CTA
+  static constexpr int NW = W * G;               // waves per CTA
+  static constexpr int NT = 64 * NW;             // threads per CTA
   static constexpr int VQ = VD / W;              // V channels per wave
   static constexpr int CPL = VQ / 16;            // 16-channel column tiles per wave
   // LDS stage row stride (bytes).  One-byte codes: 592 = 148 dwords, which
@@ -1567,9 +1580,13 @@ struct LatCfg {
   // two-way conflicted at most (SQ_LDS_BANK_CONFLICT on the latent FP8
   // workload: 2.6e5 against 8.5e5 with a 608-byte stride).
   static constexpr int RS = KROW + (EB == 1 ? 16 : 64);
-  static constexpr int ROUND = 16 * W;          // tokens per round
-  // one CTA per CU: the folded query stays in registers (one-byte codes)
-  static constexpr int MIN_WAVES = 1;
+  static constexpr int ROUND = 16 * W;          // tokens per group and round
+  // one CTA per CU, G waves per SIMD
+  static constexpr int MIN_WAVES = G;
+  // one group: the folded query stays in registers (one-byte codes); two
+  // groups read it from LDS in every round (the registers go to the second
+  // wave per SIMD)
+  static constexpr bool QREG = EB == 1 && G == 1;
   static_assert(RS % 16 == 0, "stage rows hold 16-byte chunks");
 };
 
@@ -1603,10 +1620,13 @@ __attribute__((amdgpu_waves_per_eu(LatCfg<CT, GATHER>::MIN_WAVES)))
 latent_kernel(const SplitArgs a) {
   using C = LatCfg<CT, GATHER>;
   constexpr int W = C::W;
+  constexpr int NW = C::NW;
   constexpr int NT = C::NT;
   constexpr int D = C::D;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int grp = wave / W;         // group
+  const int wv = wave - grp * W;    // wave within the group
   const int li = lane & 15;
   const int lj = lane >> 4;
   const int S = a.num_splits;
@@ -1628,9 +1648,14 @@ latent_kernel(const SplitArgs a) {
 
   __shared__ uint4 s_q[C::NKS * 64];
   __shared__ float s_err[C::NKS * 64];            // folding error per Q' entry
-  __shared__ int s_flag[W + 1];                   // per wave: a deep-tail probability; [W]: folding
-  __shared__ f32x4 s_sc[W][64];                   // published scores of the round
-  __shared__ __attribute__((aligned(16))) uint8_t s_stage[C::ROUND * C::RS];
+  __shared__ int s_flag[NW + 1];                  // per wave: a deep-tail probability; [NW]: folding
+  static_assert(W == 4, "one float4 of tile maxima per head");
+  __shared__ f32x4 s_tmax[C::G][16];              // per group and head: the round's W tile maxima
+  __shared__ half4 s_p[NW][64];                   // per wave: FP16(16 p) of its tile
+  __shared__ half4 s_pl[kResidualTile ? NW : 1][64];  // and its residual
+  __shared__ float s_lw[NW][16];                  // per wave and head: its running sum
+  __shared__ __attribute__((aligned(16))) uint8_t s_stage[C::G * C::ROUND * C::RS];
+  __shared__ float s_ml[C::G][16];                // per group: reference maximum per head
   __shared__ float s_vs[C::VD];
   constexpr int QPT = (C::NKS * 64 + NT - 1) / NT;
   uint4 qraw[QPT];
@@ -1638,7 +1663,7 @@ latent_kernel(const SplitArgs a) {
   const int32_t* bt_row = a.block_table + (size_t)r * a.max_blocks_per_row;
   // block ids of this wave's first 64 tiles (static mode: before the length;
   // read again below when a sliding window moves the row's first token)
-  WaveBlocks wb{bt_row, wk.base + split_p0(a, wk), wave, W, 0, 0};
+  WaveBlocks wb{bt_row, wk.base + split_p0(a, wk), wave, NW, 0, 0};
   if constexpr (!GATHER) wb.load(a, 0, lane);
   q_issue<C::NKS, C::EB, D, QPT, NT>(a, wk, qraw, ksc);
   const Scales sc = load_scales<C::VD, NT>(a, g);
@@ -1657,12 +1682,13 @@ latent_kernel(const SplitArgs a) {
   if (!split_range<C::VD, NT>(a, wk, p0, p1)) return;
   const int split = wk.split;
   const int ntiles = (p1 - p0 + 15) >> 4;
-  const int nrounds = (ntiles + W - 1) / W;
+  const int nrounds = (ntiles + NW - 1) / NW;
 
   const uint32_t tok = (uint32_t)KVH * C::KROW;  // bytes per token slot
   const uint32_t koff = (uint32_t)li * tok + (uint32_t)g * C::KROW + 16u * lj;
 
-  auto issue_k = [&](LatK<C>& T, int t) __attribute__((always_inline)) {
+  auto issue_k = [&](LatK<C>& T, int t, auto s0c, auto s1c) __attribute__((always_inline)) {
+    constexpr int S0 = decltype(s0c)::value, S1 = decltype(s1c)::value;
     uint32_t m = 0;
     if constexpr (!GATHER) {
       int64_t s0 = 0;
@@ -1685,7 +1711,7 @@ latent_kernel(const SplitArgs a) {
         const int sk = skip - tp;
         const uint32_t past = li < sk ? kPastDescriptor : 0u;
 #pragma unroll
-        for (int s = 0; s < C::NKL; ++s) buffer_bytes<16>(rs, koff + 64 * s + past, 0, &T.k[4 * s]);
+        for (int s = S0; s < S1; ++s) buffer_bytes<16>(rs, koff + 64 * s + past, 0, &T.k[4 * s]);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int row = 4 * lj + q;
@@ -1693,7 +1719,7 @@ latent_kernel(const SplitArgs a) {
         }
       } else {
 #pragma unroll
-        for (int s = 0; s < C::NKL; ++s) buffer_bytes<16>(rs, koff + 64 * s, 0, &T.k[4 * s]);
+        for (int s = S0; s < S1; ++s) buffer_bytes<16>(rs, koff + 64 * s, 0, &T.k[4 * s]);
 #pragma unroll
         for (int q = 0; q < 4; ++q) m |= (4 * lj + q < (int)nv) ? (1u << q) : 0u;
       }
@@ -1709,7 +1735,7 @@ latent_kernel(const SplitArgs a) {
       const int64_t sl = v ? ((int64_t)blk << a.log2_block) + (c & (a.block_size - 1)) : 0;
       const uint8_t* krow = a.key_cache + ((size_t)sl * KVH + g) * C::KROW;
 #pragma unroll
-      for (int s = 0; s < C::NKL; ++s) load_bytes<16>(krow + 64 * s + 16 * lj, &T.k[4 * s]);
+      for (int s = S0; s < S1; ++s) load_bytes<16>(krow + 64 * s + 16 * lj, &T.k[4 * s]);
       const int vi = v ? 1 : 0;
 #pragma unroll
       for (int q = 0; q < 4; ++q) m |= __shfl(vi, 4 * lj + q) ? (1u << q) : 0u;
@@ -1725,8 +1751,9 @@ latent_kernel(const SplitArgs a) {
   float l_part = 0.0f;
   float smin = __builtin_inff();  // smallest valid score of this wave's tiles (lane's head)
 
-  // this lane's 16-byte K chunks of its tile row
-  uint8_t* const stage_k = s_stage + (size_t)(16 * wave + li) * C::RS + 16 * lj;
+  // this lane's 16-byte K chunks of its tile row in the group's stage
+  uint8_t* const stage_g = s_stage + (size_t)grp * C::ROUND * C::RS;
+  uint8_t* const stage_k = stage_g + (size_t)(16 * wv + li) * C::RS + 16 * lj;
   // the piece this lane contributes to a transposed V read (see lds_read_tr8
   // / lds_read_tr16): one-byte codes -- row k = li / 2 of k-group lj is token
   // 4 lj + (k & 3) of the first (k < 4) or second tile of a tile pair, bytes
@@ -1734,21 +1761,25 @@ latent_kernel(const SplitArgs a) {
   // k = li / 4 is token 4 lj + k of a tile, halves [4 (li & 3), +4).
   const uint8_t* stage_v;
   if constexpr (C::EB == 1)
-    stage_v = s_stage + (size_t)(16 * ((li >> 1) >> 2) + 4 * lj + ((li >> 1) & 3)) * C::RS +
-              (size_t)wave * C::VQ + 8 * (li & 1);
+    stage_v = stage_g + (size_t)(16 * ((li >> 1) >> 2) + 4 * lj + ((li >> 1) & 3)) * C::RS +
+              (size_t)wv * C::VQ + 8 * (li & 1);
   else
-    stage_v = s_stage + (size_t)(4 * lj + (li >> 2)) * C::RS + (size_t)(wave * C::VQ + 4 * (li & 3)) * 2;
+    stage_v = stage_g + (size_t)(4 * lj + (li >> 2)) * C::RS + (size_t)(wv * C::VQ + 4 * (li & 3)) * 2;
 
   // Round rd on the K tile in T.  One-byte codes: the loads of round rd + 2
-  // go into the third buffer Tn (free since round rd - 1) before anything
-  // else, which measured faster than waiting for T; two-byte codes (whose
-  // tiles are twice as large) issue them into T once it is staged.
+  // go into the third buffer Tn (free since round rd - 1), the first
+  // kFirstLoads of them before anything else and the rest after the first
+  // barrier, so that the four waves' load bursts do not stall their issue
+  // for the whole round (measured faster than one burst, and than waiting
+  // for T); two-byte codes (whose tiles are twice as large) issue them into
+  // T once it is staged.
   constexpr bool kEarly = C::EB == 1;
-  // one-byte codes: Q' is read from LDS into registers once, not per tile
-  half8 qreg[C::EB == 1 ? C::NKS : 1];
+  constexpr int kFirstLoads = (C::NKL + 1) / 2;
+  // one group, one-byte codes: Q' is read from LDS into registers once
+  half8 qreg[C::QREG ? C::NKS : 1];
   auto round = [&](LatK<C>& T, LatK<C>& Tn, int rd, auto lo) __attribute__((always_inline)) {
     constexpr bool LO = decltype(lo)::value;
-    if constexpr (kEarly) issue_k(Tn, (rd + 2) * W + wave);
+    if constexpr (kEarly) issue_k(Tn, (rd + 2) * NW + wave, ic<0>{}, ic<kFirstLoads>{});
     // keep the loads ahead of the waits for this round's data
     __builtin_amdgcn_sched_barrier(0);
     // scores of this wave's tile
@@ -1766,11 +1797,18 @@ latent_kernel(const SplitArgs a) {
         const half4 c3 = codes4_to_half4<CT>(T.k[4 * s + 3]);
         const half8 k0 = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
         const half8 k1 = {c2[0], c2[1], c2[2], c2[3], c3[0], c3[1], c3[2], c3[3]};
-        sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(k0, qreg[2 * s], sacc, 0, 0, 0);
-        sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(k1, qreg[2 * s + 1], sacc, 0, 0, 0);
+        if constexpr (C::QREG) {
+          sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(k0, qreg[2 * s], sacc, 0, 0, 0);
+          sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(k1, qreg[2 * s + 1], sacc, 0, 0, 0);
+        } else {
+          const half8 q0 = __builtin_bit_cast(half8, s_q[(2 * s) * 64 + lane]);
+          const half8 q1 = __builtin_bit_cast(half8, s_q[(2 * s + 1) * 64 + lane]);
+          sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(k0, q0, sacc, 0, 0, 0);
+          sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(k1, q1, sacc, 0, 0, 0);
+        }
       }
     }
-    f32x4 scw;
+    float scw[4];
     float xs[4];
     scaled_scores<EXT>(a, sacc, xs);
 #pragma unroll
@@ -1779,12 +1817,17 @@ latent_kernel(const SplitArgs a) {
       scw[q] = valid ? xs[q] : kNegInf;
       smin = fminf(smin, valid ? scw[q] : __builtin_inff());
     }
-    s_sc[wave][lane] = scw;
-    // every wave is past the previous round's V reads and has published its
-    // scores (one score buffer suffices: a wave reads the scores of round rd
-    // before the second barrier of round rd, and they are next written after
-    // it)
+    // the tile's maximum per head (lanes li, li + 16, li + 32, li + 48)
+    float tm = fmaxf(fmaxf(scw[0], scw[1]), fmaxf(scw[2], scw[3]));
+    tm = fmaxf(tm, __shfl_xor(tm, 16));
+    tm = fmaxf(tm, __shfl_xor(tm, 32));
+    if (lj == 0) reinterpret_cast<float*>(&s_tmax[grp][li])[wv] = tm;
+    // every wave is past the previous round's V and probability reads and
+    // has published its tile maximum (single buffers suffice: a wave reads
+    // the maxima, the stage and the probabilities of round rd before the
+    // first barrier of round rd + 1, and they are next written after it)
     __syncthreads();
+    if constexpr (kEarly) issue_k(Tn, (rd + 2) * NW + wave, ic<kFirstLoads>{}, ic<C::NKL>{});
     // invalid rows are stored as zeros, so the V operands need no mask
     // (dense rows: already zero from the buffer descriptor)
     const uint32_t keep = (GATHER && !T.row_ok) ? 0u : 0xffffffffu;
@@ -1792,18 +1835,11 @@ latent_kernel(const SplitArgs a) {
     for (int s = 0; s < C::NKL; ++s)
       *reinterpret_cast<uint4*>(stage_k + 64 * s) =
           uint4{T.k[4 * s] & keep, T.k[4 * s + 1] & keep, T.k[4 * s + 2] & keep, T.k[4 * s + 3] & keep};
-    if constexpr (!kEarly) issue_k(T, (rd + 2) * W + wave);
+    if constexpr (!kEarly) issue_k(T, (rd + 2) * NW + wave, ic<0>{}, ic<C::NKL>{});
     __builtin_amdgcn_sched_barrier(0);
 
-    f32x4 st[W];
-#pragma unroll
-    for (int j = 0; j < W; ++j) st[j] = s_sc[j][lane];
-    float mt = kNegInf;
-#pragma unroll
-    for (int j = 0; j < W; ++j)
-      mt = fmaxf(mt, fmaxf(fmaxf(st[j][0], st[j][1]), fmaxf(st[j][2], st[j][3])));
-    mt = fmaxf(mt, __shfl_xor(mt, 16));
-    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    const f32x4 tmx = s_tmax[grp][li];
+    const float mt = fmaxf(fmaxf(tmx[0], tmx[1]), fmaxf(tmx[2], tmx[3]));
     if (__any(mt > m_ref + kRescaleSlack)) {
       const float mn = fmaxf(m_ref, mt);
       const float alpha = (m_ref == kNegInf) ? 0.0f : __builtin_amdgcn_exp2f((m_ref - mn) * kLog2e);
@@ -1813,31 +1849,38 @@ latent_kernel(const SplitArgs a) {
       m_ref = mn;
     }
     const float mu = (m_ref == kNegInf) ? 0.0f : m_ref;
-    half4 pop[W], pol[W];  // FP16(16 p) and its residual
-#pragma unroll
-    for (int j = 0; j < W; ++j) {
+    {
       float p[4];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) p[q] = __builtin_amdgcn_exp2f((st[j][q] - mu) * kLog2e);
+      for (int q = 0; q < 4; ++q) p[q] = __builtin_amdgcn_exp2f((scw[q] - mu) * kLog2e);
       l_part += (p[0] + p[1]) + (p[2] + p[3]);
-      split_prob<LO>(p, pop[j], pol[j]);
+      half4 po, pr;  // FP16(16 p) and its residual
+      split_prob<LO>(p, po, pr);
+      s_p[wave][lane] = po;
+      if constexpr (LO) s_pl[wave][lane] = pr;
     }
-    // the stage holds all 64 rows of the round
+    // the stage and the probabilities hold all 64 rows of the round
     __syncthreads();
     if constexpr (C::EB == 1) {
       // O^T += V^T P^T over tile pairs with 16x16x32 MFMAs: k index 8 lj + e
       // is token 4 lj + (e & 3) of tile 2 m + (e >> 2), in both operands
 #pragma unroll
       for (int m = 0; m < W / 2; ++m) {
-        const half8 pb = {pop[2 * m][0], pop[2 * m][1], pop[2 * m][2], pop[2 * m][3],
-                          pop[2 * m + 1][0], pop[2 * m + 1][1], pop[2 * m + 1][2], pop[2 * m + 1][3]};
+        const half4 p0 = s_p[grp * W + 2 * m][lane], p1 = s_p[grp * W + 2 * m + 1][lane];
+        const half8 pb = {p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
         half8 pl = {};
-        if constexpr (LO)
-          pl = half8{pol[2 * m][0], pol[2 * m][1], pol[2 * m][2], pol[2 * m][3],
-                     pol[2 * m + 1][0], pol[2 * m + 1][1], pol[2 * m + 1][2], pol[2 * m + 1][3]};
+        if constexpr (LO) {
+          const half4 r0 = s_pl[grp * W + 2 * m][lane], r1 = s_pl[grp * W + 2 * m + 1][lane];
+          pl = half8{r0[0], r0[1], r0[2], r0[3], r1[0], r1[1], r1[2], r1[3]};
+        }
+        // all V^T reads of the tile pair go out before their conversions:
+        // one LDS round trip per pair instead of one per column tile
+        v2i32 raws[C::CPL];
+#pragma unroll
+        for (int ct = 0; ct < C::CPL; ++ct) raws[ct] = lds_read_tr8(stage_v + (size_t)(32 * m) * C::RS + 16 * ct);
 #pragma unroll
         for (int ct = 0; ct < C::CPL; ++ct) {
-          const v2i32 raw = lds_read_tr8(stage_v + (size_t)(32 * m) * C::RS + 16 * ct);
+          const v2i32 raw = raws[ct];
           const half4 lo = codes4_to_half4<CT>((uint32_t)raw.x);
           const half4 hi = codes4_to_half4<CT>((uint32_t)raw.y);
           const half8 va = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
@@ -1848,11 +1891,14 @@ latent_kernel(const SplitArgs a) {
     } else {
 #pragma unroll
       for (int j = 0; j < W; ++j) {
+        const half4 pj = s_p[grp * W + j][lane];
+        half4 rj = {};
+        if constexpr (LO) rj = s_pl[grp * W + j][lane];
 #pragma unroll
         for (int ct = 0; ct < C::CPL; ++ct) {
           const half4 va = lds_read_tr16(stage_v + (size_t)(16 * j) * C::RS + 32 * ct);
-          acc[ct] = __builtin_amdgcn_mfma_f32_16x16x16f16(va, pop[j], acc[ct], 0, 0, 0);
-          if constexpr (LO) acc[ct] = __builtin_amdgcn_mfma_f32_16x16x16f16(va, pol[j], acc[ct], 0, 0, 0);
+          acc[ct] = __builtin_amdgcn_mfma_f32_16x16x16f16(va, pj, acc[ct], 0, 0, 0);
+          if constexpr (LO) acc[ct] = __builtin_amdgcn_mfma_f32_16x16x16f16(va, rj, acc[ct], 0, 0, 0);
         }
       }
     }
@@ -1861,17 +1907,17 @@ latent_kernel(const SplitArgs a) {
   // two rounds of K in flight (deeper rings measured slower on MI355X: more
   // outstanding misses per CU only lengthen the latency)
   LatK<C> ka, kb, kc;
-  issue_k(ka, wave);
-  issue_k(kb, W + wave);
+  issue_k(ka, wave, ic<0>{}, ic<C::NKL>{});
+  issue_k(kb, NW + wave, ic<0>{}, ic<C::NKL>{});
   q_stage<C::NKS, C::EB, D, QPT, NT>(qraw, ksc, sc.k_tensor, s_q, s_err);
   stage_scales<C::VD, NT>(a, sc, s_vs);
   __syncthreads();
   // folding bound of the CTA's heads (read after the final barrier)
   if (wave == 0) {
     const bool fold = fold_over_budget<CT, C::NKS>(a, s_err, nh, lane);
-    if (lane == 0) s_flag[W] = fold ? 1 : 0;
+    if (lane == 0) s_flag[NW] = fold ? 1 : 0;
   }
-  if constexpr (C::EB == 1) {
+  if constexpr (C::QREG) {
 #pragma unroll
     for (int s = 0; s < C::NKS; ++s) qreg[s] = __builtin_bit_cast(half8, s_q[s * 64 + lane]);
   }
@@ -1893,9 +1939,25 @@ latent_kernel(const SplitArgs a) {
     }
   };
   round_loop(std::integral_constant<bool, kResidualTile>{});
+  // every wave of a group holds the group's running maximum and the sum over
+  // its own tiles: sum the lane groups, then the group's waves in order; the
+  // CTA's reference maximum is the largest of the groups'
+  l_part += __shfl_xor(l_part, 16);
+  l_part += __shfl_xor(l_part, 32);
+  if (lj == 0) s_lw[wave][li] = l_part;
+  if (C::G > 1 && wv == 0 && lane < 16) s_ml[grp][lane] = m_ref;
+  __syncthreads();
+  l_part = 0.0f;
+#pragma unroll
+  for (int j = 0; j < W; ++j) l_part += s_lw[grp * W + j][li];
+  float m_all = m_ref;
+  if constexpr (C::G > 1) {
+#pragma unroll
+    for (int j = 0; j < C::G; ++j) m_all = fmaxf(m_all, s_ml[j][li]);
+  }
   // a valid probability that fell below the FP16 tile's normal range: some
   // score more than ln 2^18 below the final reference maximum (conservative)
-  const bool deep = smin != __builtin_inff() && smin - m_ref < kTailLog;
+  const bool deep = smin != __builtin_inff() && smin - m_all < kTailLog;
 
   {
     const bool dw = __any(deep);
@@ -1907,19 +1969,45 @@ latent_kernel(const SplitArgs a) {
     // the tail-depth check fails (a CTA-uniform decision); the stage is free
     bool deep_any = false;
 #pragma unroll
-    for (int w = 0; w < W; ++w) deep_any |= s_flag[w] != 0;
+    for (int w = 0; w < NW; ++w) deep_any |= s_flag[w] != 0;
     const bool armed = deep_any && value_bound<CT, C::VD>(a, sc, s_vs, lane) * (float)(p1 - p0) >= kTailArm;
-    if (s_flag[W] != 0 || (deep_any && armed)) {
-      static_assert(W * (C::VD + 2) * 4 <= C::ROUND * C::RS, "FP32-path scratch fits the stage");
-      exact_partial<CT, D, C::VD, true, GATHER, W, EXT>(a, wk, p0, p1, sc, s_vs,
-                                                   reinterpret_cast<float*>(s_stage));
+    if (s_flag[NW] != 0 || (deep_any && armed)) {
+      static_assert(NW * (C::VD + 2) * 4 <= C::G * C::ROUND * C::RS, "FP32-path scratch fits the stage");
+      exact_partial<CT, D, C::VD, true, GATHER, NW, EXT>(a, wk, p0, p1, sc, s_vs,
+                                                    reinterpret_cast<float*>(s_stage));
       return;
     }
   }
 
-  // every wave holds the same running maximum and sum; sum the lane groups
-  l_part += __shfl_xor(l_part, 16);
-  l_part += __shfl_xor(l_part, 32);
+  if constexpr (C::G > 1) {
+    // groups 1 .. G-1 hand their accumulators to group 0 through the stage
+    // (free: every wave is past its last V read), which merges them in group
+    // order with the weights exp(m_j - m_all)
+    static_assert((C::G - 1) * W * C::CPL * 64 * 16 <= C::G * C::ROUND * C::RS, "accumulators fit the stage");
+    f32x4* const xacc = reinterpret_cast<f32x4*>(s_stage);
+    if (grp > 0) {
+#pragma unroll
+      for (int ct = 0; ct < C::CPL; ++ct) xacc[(((grp - 1) * W + wv) * C::CPL + ct) * 64 + lane] = acc[ct];
+    }
+    __syncthreads();
+    if (grp > 0) return;
+    const float f0 = (m_ref == kNegInf) ? 0.0f : __builtin_amdgcn_exp2f((m_ref - m_all) * kLog2e);
+    l_part *= f0;
+#pragma unroll
+    for (int ct = 0; ct < C::CPL; ++ct) acc[ct] *= f0;
+#pragma unroll
+    for (int j = 1; j < C::G; ++j) {
+      const float mj = s_ml[j][li];
+      const float fj = (mj == kNegInf) ? 0.0f : __builtin_amdgcn_exp2f((mj - m_all) * kLog2e);
+      float lj_sum = 0.0f;
+#pragma unroll
+      for (int w = 0; w < W; ++w) lj_sum += s_lw[j * W + w][li];
+      l_part += fj * lj_sum;
+#pragma unroll
+      for (int ct = 0; ct < C::CPL; ++ct) acc[ct] += fj * xacc[(((j - 1) * W + wv) * C::CPL + ct) * 64 + lane];
+    }
+    m_ref = m_all;
+  }
   if (li < nh) {
     const int h = h0 + li;
     const size_t pidx = ((size_t)r * a.heads + h) * S + split;
@@ -1935,7 +2023,7 @@ latent_kernel(const SplitArgs a) {
     // column tile ct holds channels 16 ct + 4 lj + q of this wave's range
 #pragma unroll
     for (int ct = 0; ct < C::CPL; ++ct) {
-      const int cbase = wave * C::VQ + 16 * ct + 4 * lj;
+      const int cbase = wv * C::VQ + 16 * ct + 4 * lj;
       float4 o;
       float* op = reinterpret_cast<float*>(&o);
 #pragma unroll
