@@ -1213,6 +1213,8 @@ split_kernel(const SplitArgs a) {
   }
 }
 
+constexpr int kKvpWavesPerSimd = 2;
+
 // ---- four KV heads per CTA (dense rows, separate K / V caches) -------------
 //
 // The cache keeps the rows of all KV heads of a token side by side
@@ -1227,14 +1229,26 @@ split_kernel(const SplitArgs a) {
 // online softmax, PV).  Each wave holds the complete state of its query
 // heads, so the waves need no merge: every wave writes its own partials
 // straight from registers.
+//
+// Several CTAs share a CU, and the sequencer issues the oldest wave first,
+// so with equal priorities the CTAs dispatched last to a CU starved: on the
+// C3 continuous-batching workload the third CTA of a CU waited 25-30 us
+// for its first data, and the kernel ended with a long tail of lone CTAs
+// reading with little in flight.  So every wave runs its prologue at the
+// highest priority and then lowers its priority as its remaining work
+// shrinks (2, 1, 0 for the thirds of its tiles): the CTAs of a CU progress
+// together and finish together.  Two tiles stay in flight per wave, two
+// waves per SIMD (measured better than one tile at three waves per SIMD
+// once the priorities are set).
 
 template <int CT, int D, int VD, bool EXT>
 __global__ void __launch_bounds__(kThreads)
-__attribute__((amdgpu_waves_per_eu(SplitCfg<CT, D, VD, false, false>::MIN_WAVES)))
+__attribute__((amdgpu_waves_per_eu(kKvpWavesPerSimd)))
 split_kvp_kernel(const SplitArgs a) {
+  __builtin_amdgcn_s_setprio(3);
   using C = SplitCfg<CT, D, VD, false, false>;
   constexpr int W = kWaves;  // KV heads per CTA
-  constexpr int NST = C::NST;
+  constexpr int NST = 3;     // tiles held per wave: one consumed, two in flight
   static_assert(C::CPL % 4 == 0, "float4 groups of channels per lane");
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1462,6 +1476,13 @@ split_kvp_kernel(const SplitArgs a) {
         if (tt >= ntiles) break;
         issue(buf[(st + NST - 1) % NST], tt + NST - 1);
         __builtin_amdgcn_sched_barrier(0);
+        {
+          // priority by the share of the wave's tiles still to come
+          const int pr = (3 * (ntiles - tt)) / (ntiles + 1);
+          if (pr >= 2) __builtin_amdgcn_s_setprio(2);
+          else if (pr == 1) __builtin_amdgcn_s_setprio(1);
+          else __builtin_amdgcn_s_setprio(0);
+        }
         consume(buf[st], lo);
       }
     }
