@@ -248,6 +248,37 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
                                            kBufferWord3);
 }
 
+// Direct-to-LDS loads (gfx950 `buffer_load_dwordx4 ... lds`): lane i's 16
+// bytes land at LDS address m0 + 16 i, nothing passes through registers,
+// and offsets past the descriptor's size land as zeros.  Written as inline
+// assembly because the compiler, seeing such a load, makes every later LDS
+// read wait for all outstanding vector loads (which would drain the
+// prefetch); the kernel therefore waits for them itself, with vmcnt counts
+// that follow its own issue order (wait_vmcnt).  The descriptor is the
+// same raw-buffer one as make_rsrc's, as four SGPRs.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ u32x4 rsrc_words(const void* base, uint32_t bytes) {
+  const uint64_t b = reinterpret_cast<uint64_t>(base);
+  return u32x4{(uint32_t)b, (uint32_t)(b >> 32) & 0xffffu, bytes, (uint32_t)kBufferWord3};
+}
+
+__device__ __forceinline__ void buffer_load_lds16(uint32_t lds, uint32_t voff, u32x4 rsrc) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :: "s"(lds), "v"(voff), "s"(rsrc) : "memory", "m0");
+}
+
+// wait until at most N vector memory operations of this wave are
+// outstanding (they complete in issue order)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)p;
+}
+
 // 16 / 8 / 4 bytes from a buffer; offsets past the descriptor's size read 0
 // without a memory request.
 template <int NB>
@@ -1608,6 +1639,15 @@ struct LatCfg {
   // groups read it from LDS in every round (the registers go to the second
   // wave per SIMD)
   static constexpr bool QREG = EB == 1 && G == 1;
+  // one-byte codes, dense rows, one group: K tiles go straight to an LDS
+  // ring of NSLOT rounds (no register holds K in flight, no stage copy);
+  // a tile is NKL 1 KB blocks (block s: lane i's 16 bytes = chunk
+  // (i >> 4) + 4 s of token i & 15), padded so that the two tiles of a
+  // pair start 32 banks apart for the transposed V reads
+  static constexpr bool DMA = EB == 1 && !GATHER && G == 1;
+  static constexpr int NSLOT = 4;
+  static constexpr int TB = NKL * 1024 + 128;     // bytes per tile in the ring
+  static constexpr int STAGE_BYTES = DMA ? NSLOT * W * TB : G * ROUND * RS;
   static_assert(RS % 16 == 0, "stage rows hold 16-byte chunks");
 };
 
@@ -1667,15 +1707,21 @@ latent_kernel(const SplitArgs a) {
   unit_heads(a, wk);
   const int r = wk.r, g = wk.g, h0 = wk.h0, nh = wk.nh;
 
-  __shared__ uint4 s_q[C::NKS * 64];
-  __shared__ float s_err[C::NKS * 64];            // folding error per Q' entry
+  // DMA ring: Q' and its folding errors live in the last slot until the
+  // prologue is over (that slot's first loads go out in round 1)
+  __shared__ uint4 s_q_own[C::DMA ? 1 : C::NKS * 64];
+  __shared__ float s_err_own[C::DMA ? 1 : C::NKS * 64];  // folding error per Q' entry
   __shared__ int s_flag[NW + 1];                  // per wave: a deep-tail probability; [NW]: folding
   static_assert(W == 4, "one float4 of tile maxima per head");
   __shared__ f32x4 s_tmax[C::G][16];              // per group and head: the round's W tile maxima
   __shared__ half4 s_p[NW][64];                   // per wave: FP16(16 p) of its tile
   __shared__ half4 s_pl[kResidualTile ? NW : 1][64];  // and its residual
   __shared__ float s_lw[NW][16];                  // per wave and head: its running sum
-  __shared__ __attribute__((aligned(16))) uint8_t s_stage[C::G * C::ROUND * C::RS];
+  __shared__ __attribute__((aligned(16))) uint8_t s_stage[C::STAGE_BYTES];
+  static_assert(!C::DMA || C::NKS * 64 * 20 <= W * C::TB, "Q' fits a ring slot");
+  uint4* const s_q = C::DMA ? reinterpret_cast<uint4*>(s_stage + (C::NSLOT - 1) * W * C::TB) : s_q_own;
+  float* const s_err = C::DMA ? reinterpret_cast<float*>(s_stage + (C::NSLOT - 1) * W * C::TB + C::NKS * 64 * 16)
+                              : s_err_own;
   __shared__ float s_ml[C::G][16];                // per group: reference maximum per head
   __shared__ float s_vs[C::VD];
   constexpr int QPT = (C::NKS * 64 + NT - 1) / NT;
@@ -1708,6 +1754,12 @@ latent_kernel(const SplitArgs a) {
   const uint32_t tok = (uint32_t)KVH * C::KROW;  // bytes per token slot
   const uint32_t koff = (uint32_t)li * tok + (uint32_t)g * C::KROW + 16u * lj;
 
+  // ring address of block s of tile t (round t / NW, this wave's tile)
+  const uint32_t ring = lds_addr(s_stage);
+  auto dma_dst = [&](int t, int s) __attribute__((always_inline)) {
+    const int slot = (t / NW) & (C::NSLOT - 1);
+    return (uint32_t)__builtin_amdgcn_readfirstlane(ring + (uint32_t)((slot * W + wv) * C::TB + 1024 * s));
+  };
   auto issue_k = [&](LatK<C>& T, int t, auto s0c, auto s1c) __attribute__((always_inline)) {
     constexpr int S0 = decltype(s0c)::value, S1 = decltype(s1c)::value;
     uint32_t m = 0;
@@ -1732,7 +1784,12 @@ latent_kernel(const SplitArgs a) {
         const int sk = skip - tp;
         const uint32_t past = li < sk ? kPastDescriptor : 0u;
 #pragma unroll
-        for (int s = S0; s < S1; ++s) buffer_bytes<16>(rs, koff + 64 * s + past, 0, &T.k[4 * s]);
+        for (int s = S0; s < S1; ++s) {
+          if constexpr (C::DMA)
+            buffer_load_lds16(dma_dst(t, s), koff + 64 * s + past, rsrc_words(a.key_cache + s0 * tok, nv * tok));
+          else
+            buffer_bytes<16>(rs, koff + 64 * s + past, 0, &T.k[4 * s]);
+        }
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int row = 4 * lj + q;
@@ -1740,7 +1797,12 @@ latent_kernel(const SplitArgs a) {
         }
       } else {
 #pragma unroll
-        for (int s = S0; s < S1; ++s) buffer_bytes<16>(rs, koff + 64 * s, 0, &T.k[4 * s]);
+        for (int s = S0; s < S1; ++s) {
+          if constexpr (C::DMA)
+            buffer_load_lds16(dma_dst(t, s), koff + 64 * s, rsrc_words(a.key_cache + s0 * tok, nv * tok));
+          else
+            buffer_bytes<16>(rs, koff + 64 * s, 0, &T.k[4 * s]);
+        }
 #pragma unroll
         for (int q = 0; q < 4; ++q) m |= (4 * lj + q < (int)nv) ? (1u << q) : 0u;
       }
@@ -1786,6 +1848,11 @@ latent_kernel(const SplitArgs a) {
               (size_t)wv * C::VQ + 8 * (li & 1);
   else
     stage_v = stage_g + (size_t)(4 * lj + (li >> 2)) * C::RS + (size_t)(wv * C::VQ + 4 * (li & 3)) * 2;
+  // the same piece in the DMA ring: row k = li / 2 is token 4 lj + (k & 3) of
+  // tile (k >> 2) of the pair; this wave's channel chunks 8 wv .. 8 wv + 7 are
+  // blocks 2 wv, 2 wv + 1 of the tile, lane slots token + 16 (chunk & 3)
+  const uint8_t* const ring_v = s_stage + (size_t)((li >> 1) >> 2) * C::TB + 2048 * wv +
+                                16 * (4 * lj + ((li >> 1) & 3)) + 8 * (li & 1);
 
   // Round rd on the K tile in T.  One-byte codes: the loads of round rd + 2
   // go into the third buffer Tn (free since round rd - 1), the first
@@ -1803,6 +1870,21 @@ latent_kernel(const SplitArgs a) {
     if constexpr (kEarly) issue_k(Tn, (rd + 2) * NW + wave, ic<0>{}, ic<kFirstLoads>{});
     // keep the loads ahead of the waits for this round's data
     __builtin_amdgcn_sched_barrier(0);
+    const int slot = rd & (C::NSLOT - 1);
+    if constexpr (C::DMA) {
+      // this round's tile has landed once only the next round's loads and
+      // the first part of round rd + 2's are outstanding
+      wait_vmcnt<C::NKL + kFirstLoads>();
+      const uint8_t* tile = s_stage + (size_t)(slot * W + wv) * C::TB + 16 * lane;
+#pragma unroll
+      for (int s = 0; s < C::NKL; ++s) {
+        const uint4 u = *reinterpret_cast<const uint4*>(tile + 1024 * s);
+        T.k[4 * s] = u.x;
+        T.k[4 * s + 1] = u.y;
+        T.k[4 * s + 2] = u.z;
+        T.k[4 * s + 3] = u.w;
+      }
+    }
     // scores of this wave's tile
     f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -1851,11 +1933,13 @@ latent_kernel(const SplitArgs a) {
     if constexpr (kEarly) issue_k(Tn, (rd + 2) * NW + wave, ic<kFirstLoads>{}, ic<C::NKL>{});
     // invalid rows are stored as zeros, so the V operands need no mask
     // (dense rows: already zero from the buffer descriptor)
-    const uint32_t keep = (GATHER && !T.row_ok) ? 0u : 0xffffffffu;
+    if constexpr (!C::DMA) {
+      const uint32_t keep = (GATHER && !T.row_ok) ? 0u : 0xffffffffu;
 #pragma unroll
-    for (int s = 0; s < C::NKL; ++s)
-      *reinterpret_cast<uint4*>(stage_k + 64 * s) =
-          uint4{T.k[4 * s] & keep, T.k[4 * s + 1] & keep, T.k[4 * s + 2] & keep, T.k[4 * s + 3] & keep};
+      for (int s = 0; s < C::NKL; ++s)
+        *reinterpret_cast<uint4*>(stage_k + 64 * s) =
+            uint4{T.k[4 * s] & keep, T.k[4 * s + 1] & keep, T.k[4 * s + 2] & keep, T.k[4 * s + 3] & keep};
+    }
     if constexpr (!kEarly) issue_k(T, (rd + 2) * NW + wave, ic<0>{}, ic<C::NKL>{});
     __builtin_amdgcn_sched_barrier(0);
 
@@ -1898,7 +1982,12 @@ latent_kernel(const SplitArgs a) {
         // one LDS round trip per pair instead of one per column tile
         v2i32 raws[C::CPL];
 #pragma unroll
-        for (int ct = 0; ct < C::CPL; ++ct) raws[ct] = lds_read_tr8(stage_v + (size_t)(32 * m) * C::RS + 16 * ct);
+        for (int ct = 0; ct < C::CPL; ++ct) {
+          if constexpr (C::DMA)
+            raws[ct] = lds_read_tr8(ring_v + (size_t)(slot * W + 2 * m) * C::TB + 1024 * (ct >> 2) + 256 * (ct & 3));
+          else
+            raws[ct] = lds_read_tr8(stage_v + (size_t)(32 * m) * C::RS + 16 * ct);
+        }
 #pragma unroll
         for (int ct = 0; ct < C::CPL; ++ct) {
           const v2i32 raw = raws[ct];
@@ -1960,6 +2049,9 @@ latent_kernel(const SplitArgs a) {
     }
   };
   round_loop(std::integral_constant<bool, kResidualTile>{});
+  // the ring's last loads (rounds past the end, zero-filled) land before
+  // the LDS is used again
+  if constexpr (C::DMA) wait_vmcnt<0>();
   // every wave of a group holds the group's running maximum and the sum over
   // its own tiles: sum the lane groups, then the group's waves in order; the
   // CTA's reference maximum is the largest of the groups'
