@@ -1587,27 +1587,29 @@ split_kvp_kernel(const SplitArgs a) {
 // ---- the latent (absorbed-MLA) kernel -------------------------------------
 //
 // One cache row per token supplies K (all 576 channels) and V (its first 512
-// channels).  A CTA holds G groups of W = 4 waves (G = 2 for one-byte codes,
-// so that every SIMD runs two waves and one wave's dependency stalls are
-// filled by the other's work) and walks its position range in rounds of
-// G W 16-token tiles; group j takes the j-th run of W tiles of a round.
-// In a round, wave w of a group
-//   * computes the scores S^T = K Q'^T of tile w from its K registers
-//     (fetched two rounds ahead) and publishes the tile's maximum per head
-//     in LDS,
-//   * copies the tile's raw codes into the round's LDS stage (64 rows),
+// channels).  A CTA holds G groups of W = 4 waves (built with G = 1: one
+// wave per SIMD; with G = 2 every SIMD would run two waves, each group
+// taking its own run of W tiles of a round) and walks its position range in
+// rounds of G W 16-token tiles.  Tiles are fetched two rounds ahead: with
+// one-byte codes on dense rows straight into an LDS ring of four rounds
+// (direct-to-LDS loads, see LatCfg::DMA), otherwise into registers.  In a
+// round, wave w of a group
+//   * computes the scores S^T = K Q'^T of tile w and publishes the tile's
+//     maximum per head in LDS,
+//   * (register path) copies the tile's raw codes into the round's LDS
+//     stage (64 rows),
 //   * takes the group's maximum over the W tile maxima (so the group's waves
 //     hold the same running reference maximum), turns its own tile's scores
 //     into probabilities and publishes them in LDS, and
 //   * accumulates V channels [512 w / W, 512 (w + 1) / W) of the group's
-//     tokens, reading the V^T operands from the group's stage with the LDS
-//     transpose reads and the probabilities of all W tiles.
+//     tokens, reading the V^T operands from the ring or the stage with the
+//     LDS transpose reads and the probabilities of all W tiles.
 // Each wave evaluates the exponentials of its own tile only; the running
 // sums of a group's waves are added at the end.
 // Each row therefore crosses HBM and L2 once, V needs no registers while in
-// flight, and each wave keeps a 16 x (512 / W) accumulator.  At the end the
-// groups' states (m, l, accumulator) are merged in LDS, in group order.
-// Stage rows are padded to keep LDS bank conflicts low.
+// flight, and each wave keeps a 16 x (512 / W) accumulator.  With G > 1 the
+// groups' states (m, l, accumulator) are merged in LDS at the end, in group
+// order.  Stage and ring rows are padded to keep LDS bank conflicts low.
 
 template <int N>
 using ic = std::integral_constant<int, N>;
