@@ -1640,13 +1640,13 @@ struct LatCfg {
   // one group: the folded query stays in registers (one-byte codes); two
   // groups read it from LDS in every round (the registers go to the second
   // wave per SIMD)
-  static constexpr bool QREG = EB == 1 && G == 1;
+  static constexpr bool QREG = EB == 1 && (G == 1 || !GATHER);
   // one-byte codes, dense rows, one group: K tiles go straight to an LDS
   // ring of NSLOT rounds (no register holds K in flight, no stage copy);
   // a tile is NKL 1 KB blocks (block s: lane i's 16 bytes = chunk
   // (i >> 4) + 4 s of token i & 15), padded so that the two tiles of a
   // pair start 32 banks apart for the transposed V reads
-  static constexpr bool DMA = EB == 1 && !GATHER && G == 1;
+  static constexpr bool DMA = EB == 1 && !GATHER && G <= 2;
   static constexpr int NSLOT = 4;
   static constexpr int TB = NKL * 1024 + 128;     // bytes per tile in the ring
   static constexpr int STAGE_BYTES = DMA ? NSLOT * W * TB : G * ROUND * RS;
@@ -1688,7 +1688,7 @@ latent_kernel(const SplitArgs a) {
   constexpr int D = C::D;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int grp = wave / W;         // group
+  const int grp = C::G == 1 ? 0 : wave / W;  // group
   const int wv = wave - grp * W;    // wave within the group
   const int li = lane & 15;
   const int lj = lane >> 4;
@@ -1759,7 +1759,7 @@ latent_kernel(const SplitArgs a) {
   // ring address of block s of tile t (round t / NW, this wave's tile)
   const uint32_t ring = lds_addr(s_stage);
   auto dma_dst = [&](int t, int s) __attribute__((always_inline)) {
-    const int slot = (t / NW) & (C::NSLOT - 1);
+    const int slot = ((t / NW) * C::G + grp) & (C::NSLOT - 1);
     return (uint32_t)__builtin_amdgcn_readfirstlane(ring + (uint32_t)((slot * W + wv) * C::TB + 1024 * s));
   };
   auto issue_k = [&](LatK<C>& T, int t, auto s0c, auto s1c) __attribute__((always_inline)) {
@@ -1864,19 +1864,24 @@ latent_kernel(const SplitArgs a) {
   // for T); two-byte codes (whose tiles are twice as large) issue them into
   // T once it is staged.
   constexpr bool kEarly = C::EB == 1;
-  constexpr int kFirstLoads = (C::NKL + 1) / 2;
+  // rounds of lead: two, except for two groups on the ring, whose four
+  // slots hold exactly the current and the next 128-token round, so the
+  // next one can only be loaded once every wave is past the previous
+  // round's V reads (after the first barrier)
+  constexpr int kAhead = (C::DMA && C::G > 1) ? 1 : 2;
+  constexpr int kFirstLoads = kAhead == 1 ? 0 : (C::NKL + 1) / 2;
   // one group, one-byte codes: Q' is read from LDS into registers once
   half8 qreg[C::QREG ? C::NKS : 1];
   auto round = [&](LatK<C>& T, LatK<C>& Tn, int rd, auto lo) __attribute__((always_inline)) {
     constexpr bool LO = decltype(lo)::value;
-    if constexpr (kEarly) issue_k(Tn, (rd + 2) * NW + wave, ic<0>{}, ic<kFirstLoads>{});
+    if constexpr (kEarly) issue_k(Tn, (rd + kAhead) * NW + wave, ic<0>{}, ic<kFirstLoads>{});
     // keep the loads ahead of the waits for this round's data
     __builtin_amdgcn_sched_barrier(0);
-    const int slot = rd & (C::NSLOT - 1);
+    const int slot = (rd * C::G + grp) & (C::NSLOT - 1);
     if constexpr (C::DMA) {
       // this round's tile has landed once only the next round's loads and
       // the first part of round rd + 2's are outstanding
-      wait_vmcnt<C::NKL + kFirstLoads>();
+      wait_vmcnt<(kAhead - 1) * C::NKL + kFirstLoads>();
       const uint8_t* tile = s_stage + (size_t)(slot * W + wv) * C::TB + 16 * lane;
 #pragma unroll
       for (int s = 0; s < C::NKL; ++s) {
@@ -1932,7 +1937,7 @@ latent_kernel(const SplitArgs a) {
     // the maxima, the stage and the probabilities of round rd before the
     // first barrier of round rd + 1, and they are next written after it)
     __syncthreads();
-    if constexpr (kEarly) issue_k(Tn, (rd + 2) * NW + wave, ic<kFirstLoads>{}, ic<C::NKL>{});
+    if constexpr (kEarly) issue_k(Tn, (rd + kAhead) * NW + wave, ic<kFirstLoads>{}, ic<C::NKL>{});
     // invalid rows are stored as zeros, so the V operands need no mask
     // (dense rows: already zero from the buffer descriptor)
     if constexpr (!C::DMA) {
@@ -2020,7 +2025,7 @@ latent_kernel(const SplitArgs a) {
   // outstanding misses per CU only lengthen the latency)
   LatK<C> ka, kb, kc;
   issue_k(ka, wave, ic<0>{}, ic<C::NKL>{});
-  issue_k(kb, NW + wave, ic<0>{}, ic<C::NKL>{});
+  if constexpr (kAhead == 2) issue_k(kb, NW + wave, ic<0>{}, ic<C::NKL>{});
   q_stage<C::NKS, C::EB, D, QPT, NT>(qraw, ksc, sc.k_tensor, s_q, s_err);
   stage_scales<C::VD, NT>(a, sc, s_vs);
   __syncthreads();
@@ -2034,7 +2039,15 @@ latent_kernel(const SplitArgs a) {
     for (int s = 0; s < C::NKS; ++s) qreg[s] = __builtin_bit_cast(half8, s_q[s * 64 + lane]);
   }
   auto round_loop = [&](auto lo) __attribute__((always_inline)) {
-    if constexpr (kEarly) {
+    if constexpr (kEarly && kAhead == 1) {
+      for (int rd = 0; rd < nrounds; rd += 3) {
+        round(ka, kb, rd, lo);
+        if (rd + 1 >= nrounds) break;
+        round(kb, kc, rd + 1, lo);
+        if (rd + 2 >= nrounds) break;
+        round(kc, ka, rd + 2, lo);
+      }
+    } else if constexpr (kEarly) {
       for (int rd = 0; rd < nrounds; rd += 3) {
         round(ka, kc, rd, lo);
         if (rd + 1 >= nrounds) break;
