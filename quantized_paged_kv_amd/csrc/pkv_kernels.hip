@@ -1710,7 +1710,7 @@ latent_kernel(const SplitArgs a) {
   const int r = wk.r, g = wk.g, h0 = wk.h0, nh = wk.nh;
 
   // DMA ring: Q' and its folding errors live in the last slot until the
-  // prologue is over (that slot's first loads go out in round 1)
+  // prologue is over (that slot's first loads go out in the second round)
   __shared__ uint4 s_q_own[C::DMA ? 1 : C::NKS * 64];
   __shared__ float s_err_own[C::DMA ? 1 : C::NKS * 64];  // folding error per Q' entry
   __shared__ int s_flag[NW + 1];                  // per wave: a deep-tail probability; [NW]: folding
