@@ -264,8 +264,9 @@ __device__ __forceinline__ u32x4 rsrc_words(const void* base, uint32_t bytes) {
 }
 
 __device__ __forceinline__ void buffer_load_lds16(uint32_t lds, uint32_t voff, u32x4 rsrc) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-               :: "s"(lds), "v"(voff), "s"(rsrc) : "memory", "m0");
+  // the LDS address goes in through m0 as an input operand, so the compiler
+  // sets m0 itself and knows what it holds
+  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" :: "v"(voff), "s"(rsrc), "{m0}"(lds) : "memory");
 }
 
 // wait until at most N vector memory operations of this wave are
