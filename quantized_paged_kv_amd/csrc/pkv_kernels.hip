@@ -1857,20 +1857,25 @@ latent_kernel(const SplitArgs a) {
   const uint8_t* const ring_v = s_stage + (size_t)((li >> 1) >> 2) * C::TB + 2048 * wv +
                                 16 * (4 * lj + ((li >> 1) & 3)) + 8 * (li & 1);
 
-  // Round rd on the K tile in T.  One-byte codes: the loads of round rd + 2
-  // go into the third buffer Tn (free since round rd - 1), the first
-  // kFirstLoads of them before anything else and the rest after the first
-  // barrier, so that the four waves' load bursts do not stall their issue
-  // for the whole round (measured faster than one burst, and than waiting
-  // for T); two-byte codes (whose tiles are twice as large) issue them into
-  // T once it is staged.
+  // Round rd on the K tile in T.  One-byte codes: the loads of round
+  // rd + kAhead go into the buffer Tn (for the mask; with the ring the data
+  // goes to its slot), the first kFirstLoads of them before anything else
+  // and the rest after the first barrier, so that the four waves' load
+  // bursts do not stall their issue for the whole round (measured faster
+  // than one burst, and than waiting for T); two-byte codes (whose tiles
+  // are twice as large) issue them into T once it is staged.
   constexpr bool kEarly = C::EB == 1;
-  // rounds of lead: two, except for two groups on the ring, whose four
-  // slots hold exactly the current and the next 128-token round, so the
-  // next one can only be loaded once every wave is past the previous
-  // round's V reads (after the first barrier)
-  constexpr int kAhead = (C::DMA && C::G > 1) ? 1 : 2;
-  constexpr int kFirstLoads = kAhead == 1 ? 0 : (C::NKL + 1) / 2;
+  // Rounds of lead.  Register path: two.  LDS ring: one -- on C5-shaped
+  // work a ring one round ahead measured faster than two (21.4-21.9 against
+  // 22.3-22.9 us) and three slower still (24.6): more outstanding loads per
+  // CU only lengthen their latency -- with three of the nine loads issued
+  // at the round start and six after the first barrier (all nine after it:
+  // 26.2 us; five or seven first: 21.8, 22.0).  Two groups on the ring hold
+  // exactly the current and the next 128-token round in the four slots, so
+  // there all nine loads wait for the first barrier (every wave past the
+  // previous round's V reads).
+  constexpr int kAhead = C::DMA ? 1 : 2;
+  constexpr int kFirstLoads = (C::DMA && C::G > 1) ? 0 : (C::DMA ? 3 : (C::NKL + 1) / 2);
   // one group, one-byte codes: Q' is read from LDS into registers once
   half8 qreg[C::QREG ? C::NKS : 1];
   auto round = [&](LatK<C>& T, LatK<C>& Tn, int rd, auto lo) __attribute__((always_inline)) {
@@ -2022,8 +2027,8 @@ latent_kernel(const SplitArgs a) {
     }
   };
 
-  // two rounds of K in flight (deeper rings measured slower on MI355X: more
-  // outstanding misses per CU only lengthen the latency)
+  // kAhead rounds of K in flight (deeper rings measured slower on MI355X:
+  // more outstanding misses per CU only lengthen the latency)
   LatK<C> ka, kb, kc;
   issue_k(ka, wave, ic<0>{}, ic<C::NKL>{});
   if constexpr (kAhead == 2) issue_k(kb, NW + wave, ic<0>{}, ic<C::NKL>{});
