@@ -224,9 +224,12 @@ struct SplitCfg {
   // Prefetch depth (tiles held in registers per wave: one consumed, the rest
   // in flight) and the register budget (waves per SIMD), chosen by
   // measurement on MI355X: for head sizes up to 128 three waves per SIMD
-  // with one tile in flight beat two waves with two tiles in flight.
+  // beat two; and one tile in flight (two for the smallest tiles) beat two
+  // (three): more outstanding loads per CU only lengthen their latency (the
+  // single-row INT8 head-256 step 7.35 -> 6.75 us, the gathered one 10.9
+  // -> 9.6, the 64-row one 59.3 -> 58.6).
   static constexpr int TILE_REGS = NKW + 4 * NVW;
-  static constexpr int NST = TILE_REGS <= 16 ? 4 : (VD <= 128 ? 2 : (TILE_REGS <= 40 ? 3 : 2));
+  static constexpr int NST = TILE_REGS <= 16 ? 3 : 2;
   static constexpr int MIN_WAVES =
       LATENT ? 1 : (TILE_REGS <= 32 && VD <= 128 && !GATHER ? 3 : (TILE_REGS <= 40 ? 2 : 1));
   static_assert(KROW % 64 == 0, "head_size * itemsize must be a multiple of 64");
