@@ -1271,8 +1271,8 @@ constexpr int kKvpWavesPerSimd = 2;
 // for its first data, and the kernel ended with a long tail of lone CTAs
 // reading with little in flight.  So every wave runs its prologue at the
 // highest priority and then lowers its priority as its remaining work
-// shrinks (2, 1, 0 for the thirds of its tiles): the CTAs of a CU progress
-// together and finish together.  Two tiles stay in flight per wave, two
+// shrinks (3, 2, 1, 0 for the quarters of its tiles): the CTAs of a CU
+// progress together and finish together.  Two tiles stay in flight per wave, two
 // waves per SIMD (measured better than one tile at three waves per SIMD
 // once the priorities are set).
 
@@ -1513,8 +1513,9 @@ split_kvp_kernel(const SplitArgs a) {
         __builtin_amdgcn_sched_barrier(0);
         {
           // priority by the share of the wave's tiles still to come
-          const int pr = (3 * (ntiles - tt)) / (ntiles + 1);
-          if (pr >= 2) __builtin_amdgcn_s_setprio(2);
+          const int pr = (4 * (ntiles - tt)) / (ntiles + 1);
+          if (pr >= 3) __builtin_amdgcn_s_setprio(3);
+          else if (pr == 2) __builtin_amdgcn_s_setprio(2);
           else if (pr == 1) __builtin_amdgcn_s_setprio(1);
           else __builtin_amdgcn_s_setprio(0);
         }
