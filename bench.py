@@ -2,22 +2,29 @@
 """Benchmark: one decode step = one paged_decode_attention call (split kernel +
 combine) over one batch of synthetic input, on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload C2]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload C3] [--also C5]
 
-Prints ONE JSON line.  ``value`` is the effective KV-cache bandwidth (bytes of
-K and V rows the step must read / time per step) in GB/s; ``ms_per_step`` is
-the time per step.  Inputs are resident in HBM before the timed region.  To
-measure HBM rather than the 256 MB Infinity Cache, the step cycles over R
-device replicas of the cache (R x bytes >= 1 GiB), and the K steps are
-replayed from one HIP graph, timed with HIP events on the launch stream.
+Prints ONE JSON line.  The default workload is the continuous-batching FP16
+step (16 rows of 512..8192 tokens, 32 query / 8 KV heads, head 128, ~290 MB of
+K and V per step), the largest configuration; the latent FP8 step (32 rows x
+4096 tokens) is timed the same way and reported in ``also``.  ``value`` is
+the effective KV-cache bandwidth (bytes of K and V rows the step must read /
+time per step) in GB/s; ``ms_per_step`` is the time per step.  Inputs are
+resident in HBM before the timed region.  To measure HBM rather than the
+256 MB Infinity Cache, step i reads replica i mod R of the caches (R x bytes
+>= 1 GiB, whatever K is) and every timed round starts after an untimed
+512 MiB read.  The K steps are replayed from one HIP graph and timed with
+HIP events on the launch stream; the reported time is the median of
+``--rounds`` (7) rounds after W eager warmup steps and one untimed replay,
+the protocol of the DSA page's H200 measurements.
 
 ``roofline`` describes the dominant kernel (the split kernel): algorithmic KV
 bytes per launch / its average duration (HIP events around a graph of K
-partial-only launches on the same stream), against the 8 TB/s HBM peak.
-``traffic`` is filled from the committed rocprofv3 counter summary
-(profiles/) when it was taken on the current kernel source, else null.
-``cpu_baseline`` times the FP64 oracle on the host cores on a bounded sample
-of the same workload.
+partial-only launches on the same stream, same rounds), against the 8 TB/s
+HBM peak.  ``traffic`` is filled from the committed rocprofv3 counter
+summary (profiles/) when it was taken on the current kernel source, else
+null.  ``cpu_baseline`` times the FP64 oracle on the host cores on a
+bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -67,12 +74,13 @@ def read_traffic(kernel: str, workload: str, src: str = KERNEL_SRC):
         return None
 
 
-def cpu_baseline(inp, budget_s: float = 12.0):
+def cpu_baseline(inp, budget_s: float = 15.0):
     """Time the FP64 oracle (as it stands) on the host cores on a bounded sample:
-    whole steps of the workload if one step fits the budget, else a subset of
-    its rows.  Returns the dict for the JSON line."""
-    import numpy as np
-
+    the median of 3 runs with one thread per host CPU (whole steps of the
+    workload if one step fits a quarter of the budget, else a subset of its
+    rows), plus one single-thread run on a smaller subset of rows.  Returns
+    the dict for the JSON line; `cores` is the number of threads the oracle
+    ran with, `host_cpus` what the host reports."""
     import oracle
     from workloads import live_token_counts
 
@@ -80,33 +88,48 @@ def cpu_baseline(inp, budget_s: float = 12.0):
     cores = os.cpu_count() or 1
     counts = live_token_counts(inp)
     row_bytes = (p.head_size if p.layout == "latent" else p.head_size + p.v_head_size) * p.cache_itemsize
+
+    def gbs(rows, dt, reps=1):
+        sel = counts if rows is None else counts[rows]
+        return int(sel.sum()) * p.kv_heads * row_bytes * reps / dt / 1e9
+
     # probe one row to size the sample
     t0 = time.perf_counter()
     oracle.paged_decode(inp, threads=cores, rows=[0])
     t_row = max(time.perf_counter() - t0, 1e-4)
-    rows_fit = max(1, int(budget_s / t_row))
+    run_s = budget_s / 4
+    rows_fit = max(1, int(run_s / t_row))
     if rows_fit >= p.rows:
-        reps = max(1, int(budget_s / (t_row * p.rows)))
+        reps = max(1, int(run_s / (t_row * p.rows)))
         rows = None
         nrows = p.rows
-        sample = f"{reps} full step(s) of the workload ({p.rows} rows)"
+        sample = f"{reps} full step(s) of the workload ({p.rows} rows) per run"
     else:
         reps = 1
         rows = list(range(min(p.rows, rows_fit)))
         nrows = len(rows)
-        sample = f"{nrows} of {p.rows} rows of one step"
-    units = nrows * p.kv_heads
-    used = min(cores, units)
+        sample = f"{nrows} of {p.rows} rows of one step per run"
+    used = min(cores, nrows * p.kv_heads)  # the oracle's threads take (row, KV head) units
+    runs = []
+    for _ in range(3):
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            oracle.paged_decode(inp, threads=cores, rows=rows)
+        runs.append(time.perf_counter() - t0)
+    dt = _median(runs)
+    # single thread: as many rows as fit a quarter of the budget
+    rows1 = list(range(max(1, min(p.rows, int(run_s / (t_row * used))))))
     t0 = time.perf_counter()
-    for _ in range(reps):
-        oracle.paged_decode(inp, threads=cores, rows=rows)
-    dt = time.perf_counter() - t0
-    sel = counts if rows is None else counts[rows]
-    kv_bytes = int(sel.sum()) * p.kv_heads * row_bytes * reps
-    return {"value": round(kv_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": used,
-            "kind": "oracle",
-            "sample": f"{sample}; FP64 C oracle, {used} threads over (row, KV head) units; "
-                      f"{dt:.1f} s wall; {dt / reps * 1e3 * p.rows / nrows:.1f} ms per full step"}
+    oracle.paged_decode(inp, threads=1, rows=rows1)
+    dt1 = time.perf_counter() - t0
+    return {"value": round(gbs(rows, dt, reps), 4), "unit": "GB/s", "cores": used,
+            "host_cpus": cores, "kind": "oracle",
+            "single_thread_value": round(gbs(rows1, dt1), 4),
+            "sample": f"{sample}; FP64 C oracle, {used} threads over (row, KV head) units "
+                      f"(host reports {cores} CPUs); median of 3 runs "
+                      f"({', '.join(f'{x:.2f}' for x in runs)} s), "
+                      f"{dt / reps * 1e3 * p.rows / nrows:.1f} ms per full step; single "
+                      f"thread on {len(rows1)} row(s): {dt1:.2f} s"}
 
 
 def bench_write(args, dev):
@@ -152,7 +175,7 @@ def bench_write(args, dev):
                      device=dev)
     vc = None if latent else torch.zeros((p.num_pool_blocks, p.block_size, p.kv_heads,
                                           p.v_head_size), dtype=cdt, device=dev)
-    R = max(1, min(args.steps, math.ceil(args.replica_bytes / max(algo, 1))))
+    R = max(1, math.ceil(args.replica_bytes / max(algo, 1)))
     keys = [key] + [key.clone() for _ in range(R - 1)]
     vals = [val] + ([val.clone() for _ in range(R - 1)] if val is not None else [None] * (R - 1))
     kcs = [kc] + [kc.clone() for _ in range(R - 1)]
@@ -185,12 +208,18 @@ def bench_write(args, dev):
         replay = g.replay
         replay()
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    replay()
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / K
+    flush = torch.ones(128 << 20, dtype=torch.int32, device=dev)
+    rounds = []
+    for _ in range(args.rounds):
+        flush.max()  # untimed: a 512 MiB read evicts the Infinity Cache
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        replay()
+        e1.record()
+        torch.cuda.synchronize()
+        rounds.append(e0.elapsed_time(e1) / K)
+    ms = _median(rounds)
     gbs = algo / (ms * 1e-3) / 1e9
     traffic = read_traffic("cache_write_kernel", f"{args.workload}_T{T}", WRITER_SRC)
     log(f"writer {ms * 1e3:.2f} us per call ({gbs:.0f} GB/s)")
@@ -203,8 +232,10 @@ def bench_write(args, dev):
                                f"format ({p.cache_dtype}, k {p.k_quant}, v {p.v_quant}, "
                                f"{p.layout})",
                    "cold_cache_replicas": R,
-                   "timing": ("K eager launches" if args.eager else
-                              "one HIP-graph replay of K calls") + ", HIP events"},
+                   "timing": f"median of {args.rounds} rounds; each round "
+                             + ("K eager launches" if args.eager else
+                                "one HIP-graph replay of K calls")
+                             + ", HIP events, after an untimed 512 MiB read"},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "kernel": "cache_write_kernel",
@@ -399,19 +430,24 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="C2", choices=sorted(workloads_names()),
+    ap.add_argument("--workload", default="C3", choices=sorted(workloads_names()),
                     help="C1..C5: the decode configurations; P<rows>: the dynamic-sparse "
                          "prefill shape (rows x 2048 gathered candidates, MFMA-bound); "
                          "X<ctx>b<batch><dtype>: the PagedAttention page's isolated decode "
                          "shapes (64q/8kv, head 64, block 256)")
     ap.add_argument("--replica-bytes", type=float, default=1.0 * (1 << 30),
                     help="cold-cache protocol: replicate the cache until this many bytes")
+    ap.add_argument("--rounds", type=int, default=7,
+                    help="timed rounds of K steps; the median round is reported")
+    ap.add_argument("--also", default="C5",
+                    help="comma-separated further workloads timed the same way and reported "
+                         "in the line's 'also' list ('' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--splits", type=int, default=0, help="split-count override (0 = automatic)")
     ap.add_argument("--min-chunk", type=int, default=0, help="geometry min_chunk (0 = default)")
     ap.add_argument("--waves", type=int, default=0, help="geometry target waves (0 = default)")
     ap.add_argument("--kv-heads-per-cta", type=int, default=0,
-                    help="geometry: KV heads per CTA (0 = default, 1, or 4)")
+                    help="geometry: KV heads per CTA (0 = default, 1, 4 or 8)")
     ap.add_argument("--eager", action="store_true",
                     help="launch every step eagerly instead of from a HIP graph (for "
                          "per-dispatch hardware counters)")
@@ -466,8 +502,36 @@ def main():
     if args.op == "write":
         return bench_write(args, dev)
 
-    log(f"generating {args.workload}")
-    inp = workloads.workload(args.workload)
+    line = decode_line(args, dev)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+def _median(xs):
+    ys = sorted(xs)
+    return ys[len(ys) // 2]
+
+
+def measure_decode(args, dev, workload: str, with_partials: bool = True) -> dict:
+    """Time the decode step (split kernel + combine) and the split kernel alone
+    on one workload with the cold-cache protocol:
+      * R = ceil(replica_bytes / cache bytes) device replicas of the caches
+        (independent of --steps), step i reads replica i mod R;
+      * K steps captured in one HIP graph, W eager warmup steps and one
+        untimed replay before timing;
+      * every timed round is preceded by an untimed read of a 512 MiB buffer
+        (twice the 256 MB Infinity Cache), so no round starts with the cache
+        holding the replicas it reads first;
+      * ms per step = median over --rounds rounds of (HIP events around one
+        replay on the launch stream) / K."""
+    import torch
+
+    import quantized_paged_kv_amd as pkv
+    import workloads
+    from workloads.device import to_device
+
+    log(f"generating {workload}")
+    inp = workloads.workload(workload)
     p = inp.problem
     kv_bytes = inp.effective_kv_bytes()
     d = to_device(inp, dev)
@@ -480,15 +544,19 @@ def main():
     cache_bytes = d.key_cache.numel() * d.key_cache.element_size()
     if d.value_cache is not None:
         cache_bytes += d.value_cache.numel() * d.value_cache.element_size()
-    R = max(1, min(args.steps, math.ceil(args.replica_bytes / max(cache_bytes, 1))))
-    log(f"{args.workload}: kv bytes/step {kv_bytes}, cache bytes {cache_bytes}, replicas {R}, "
-        f"splits {geo.num_splits}")
+    R = max(1, math.ceil(args.replica_bytes / max(cache_bytes, 1)))
+    log(f"{workload}: kv bytes/step {kv_bytes}, cache bytes {cache_bytes}, replicas {R} "
+        f"({R * cache_bytes} bytes), splits {geo.num_splits}")
     keys = [d.key_cache] + [d.key_cache.clone() for _ in range(R - 1)]
     vals = [d.value_cache] + ([d.value_cache.clone() for _ in range(R - 1)]
                               if d.value_cache is not None else [None] * (R - 1))
     odt = torch.float32 if d.problem_kwargs["out_dtype"] == "f32" else torch.float16
     out = torch.empty((p.rows, p.heads, p.v_head_size), dtype=odt, device=dev)
     lse = torch.empty((p.rows, p.heads), dtype=torch.float32, device=dev)
+    # a read of 512 MiB (twice the Infinity Cache) before every timed round
+    # evicts the replicas and leaves clean lines (a write would leave dirty
+    # lines whose write-back the first timed steps would pay for)
+    flush = torch.ones(128 << 20, dtype=torch.int32, device=dev)
 
     def step(i):
         pkv.paged_decode_attention(prob, geo, d.query, keys[i % R], vals[i % R], d.block_table,
@@ -530,48 +598,52 @@ def main():
 
     K = args.steps
     g_step = capture(step, K)
-    g_part = capture(partial, K)
+    g_part = capture(partial, K) if with_partials else None
     g_step.replay()  # untimed: first replay of the graph
-    g_part.replay()
+    if g_part is not None:
+        g_part.replay()
     torch.cuda.synchronize()
 
-    # timed region: exactly K steps
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record()
-    g_step.replay()
-    e1.record()
-    torch.cuda.synchronize()
-    ms_step = e0.elapsed_time(e1) / K
+    def timed_rounds(g):
+        per_step = []
+        for _ in range(args.rounds):
+            flush.max()  # untimed: evict the Infinity Cache
+            torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            g.replay()  # exactly K steps
+            e1.record()
+            torch.cuda.synchronize()
+            per_step.append(e0.elapsed_time(e1) / K)
+        return _median(per_step), per_step
 
-    # dominant kernel alone: K partial-only launches, same stream
-    f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    f0.record()
-    g_part.replay()
-    f1.record()
-    torch.cuda.synchronize()
-    ms_split = f0.elapsed_time(f1) / K
+    ms_step, rounds_step = timed_rounds(g_step)
+    ms_split, rounds_split = timed_rounds(g_part) if g_part is not None else (None, [])
+    kernel = ("latent_kernel" if p.layout == "latent" else
+              "split_kvp_kernel" if geo.kv_heads_per_cta > 1 else "split_kernel")
+    res = {"inp": inp, "geo": geo, "kv_bytes": kv_bytes, "R": R, "cache_bytes": cache_bytes,
+           "ms_step": ms_step, "rounds_step": rounds_step, "ms_split": ms_split,
+           "rounds_split": rounds_split, "kernel": kernel}
+    msg = f"{workload}: step {ms_step * 1e3:.2f} us ({kv_bytes / (ms_step * 1e-3) / 1e9:.0f} GB/s)"
+    if ms_split is not None:
+        msg += (f", split kernel {ms_split * 1e3:.2f} us "
+                f"({kv_bytes / (ms_split * 1e-3) / 1e9:.0f} GB/s)")
+    log(msg + f" [median of {args.rounds} rounds of {K} steps]")
+    del keys, vals, flush
+    torch.cuda.empty_cache()
+    return res
 
+
+def decode_line(args, dev) -> dict:
+    m = measure_decode(args, dev, args.workload)
+    inp, geo, p = m["inp"], m["geo"], m["inp"].problem
+    kv_bytes, ms_step, ms_split = m["kv_bytes"], m["ms_step"], m["ms_split"]
     value = kv_bytes / (ms_step * 1e-3) / 1e9
     achieved = kv_bytes / (ms_split * 1e-3) / 1e9
-    # prefill shapes gather cache-resident rows many times over: there the
-    # contractions bound the kernel (QK^T and PV, 2 (D + VD) flops per head
-    # and attended token; the GQA group is padded to the 16-wide MFMA tile,
-    # which is not counted)
-    prefill = args.workload.startswith("P")
-    flops = 0
-    if prefill:
-        from workloads import live_token_counts
-        dims = p.head_size + p.v_head_size
-        flops = int(live_token_counts(inp).sum()) * p.heads * 2 * dims
-        tflops = flops / (ms_split * 1e-3) / 1e12
-    kernel = ("latent_kernel" if p.layout == "latent" else
-              "split_kvp_kernel" if geo.kv_heads_per_cta == 4 else "split_kernel")
+    kernel = m["kernel"]
     traffic = read_traffic(kernel, args.workload)
-    log(f"step {ms_step * 1e3:.2f} us ({value:.0f} GB/s), split kernel {ms_split * 1e3:.2f} us "
-        f"({achieved:.0f} GB/s)")
-
+    K = args.steps
     line = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -595,9 +667,13 @@ def main():
                        "accumulation; fp32 softmax",
             "num_splits": geo.num_splits,
             "kv_heads_per_cta": geo.kv_heads_per_cta,
-            "cold_cache_replicas": R,
-            "timing": ("K eager launches" if args.eager else "one HIP-graph replay of K steps")
-                      + ", HIP events on the launch stream",
+            "cold_cache_replicas": m["R"],
+            "cold_cache_replica_bytes": m["R"] * m["cache_bytes"],
+            "timing": (f"median of {args.rounds} rounds; each round "
+                       + ("K eager launches" if args.eager else "one HIP-graph replay of K steps")
+                       + ", HIP events on the launch stream, after an untimed 512 MiB read "
+                         "that evicts the Infinity Cache"),
+            "us_per_step_rounds": [round(x * 1e3, 3) for x in m["rounds_step"]],
         },
         "roofline": {
             "bound": "hbm",
@@ -608,27 +684,47 @@ def main():
             "traffic": traffic,
             "kernel": f"{kernel} (paged_decode_partials)",
             "kernel_us": round(ms_split * 1e3, 3),
+            "kernel_us_rounds": [round(x * 1e3, 3) for x in m["rounds_split"]],
             "algorithmic_bytes_per_launch": kv_bytes,
         },
     }
-    if prefill:
-        line["roofline"] = {
-            "bound": "mfma",
-            "achieved": round(tflops, 2),
-            "peak": MFMA_F16_PEAK_TFLOPS,
-            "unit": "TFLOP/s",
-            "frac": round(tflops / MFMA_F16_PEAK_TFLOPS, 4),
-            "traffic": traffic,
-            "kernel": f"{kernel} (paged_decode_partials)",
-            "kernel_us": round(ms_split * 1e3, 3),
-            "algorithmic_flops_per_launch": flops,
-            "gathered_kv_bytes_per_launch": kv_bytes,
-        }
+    if args.workload.startswith("P"):
+        # prefill shapes gather cache-resident rows many times over (every row
+        # of a sequence attends its own candidates): the bytes that must come
+        # from HBM are the unique rows, the rest is served by the caches, and
+        # the kernel waits on its chain of dependent loads (candidate, block
+        # id, row); reported as gathered bytes per second with the MFMA
+        # utilisation beside it (QK^T and PV, 2 (D + VD) flops per head and
+        # attended token; the 12 -> 16 head padding and the residual tile are
+        # not counted)
+        from workloads import live_token_counts
+        dims = p.head_size + p.v_head_size
+        flops = int(live_token_counts(inp).sum()) * p.heads * 2 * dims
+        tflops = flops / (ms_split * 1e-3) / 1e12
+        line["roofline"]["bound"] = "latency"
+        line["roofline"]["note"] = ("gathered KV bytes per second; the bound is the chain of "
+                                    "dependent loads per gathered row, not HBM bandwidth")
+        line["roofline"]["mfma_tflops"] = round(tflops, 2)
+        line["roofline"]["mfma_frac_of_fp16_peak"] = round(tflops / MFMA_F16_PEAK_TFLOPS, 4)
+    also = [w for w in args.also.split(",") if w and w != args.workload]
+    if also:
+        line["also"] = []
+        for w in also:
+            a = measure_decode(args, dev, w)
+            v = a["kv_bytes"] / (a["ms_step"] * 1e-3) / 1e9
+            kv = a["kv_bytes"] / (a["ms_split"] * 1e-3) / 1e9
+            line["also"].append({
+                "workload": a["inp"].name, "us_per_step": round(a["ms_step"] * 1e3, 3),
+                "value": round(v, 2), "unit": "GB/s",
+                "pct_of_hbm_peak": round(100.0 * v / HBM_PEAK_GBS, 2),
+                "kernel": a["kernel"], "kernel_us": round(a["ms_split"] * 1e3, 3),
+                "kernel_frac_of_hbm_peak": round(kv / HBM_PEAK_GBS, 4),
+                "traffic": read_traffic(a["kernel"], w),
+                "num_splits": a["geo"].num_splits, "cold_cache_replicas": a["R"]})
     if not args.no_cpu_baseline:
         log("timing the oracle on the host cores")
         line["cpu_baseline"] = cpu_baseline(inp)
-    print(json.dumps(line), flush=True)
-    return 0
+    return line
 
 
 if __name__ == "__main__":

@@ -45,12 +45,14 @@ pkv::Variant variant_of(const pkv_problem& p) {
   return v;
 }
 
-// Four KV heads per CTA (split_kvp_kernel): dense rows, separate caches, a
-// multiple of four KV heads and at most 16 query heads per KV head.
-bool kvp_allowed(const pkv_problem& p) {
+// Several KV heads per CTA (split_kvp_kernel, kpc = 4 or 8): dense rows,
+// separate caches, a multiple of kpc KV heads and at most 16 query heads per
+// KV head.
+bool kvp_allowed(const pkv_problem& p, int kpc) {
   const int group = p.num_heads / p.num_kv_heads;
-  return p.layout == PKV_SEPARATE && p.max_candidates == 0 &&
-         p.num_kv_heads % pkv::kKvHeadsPerCta == 0 && group <= 16;
+  return (kpc == pkv::kKvHeadsPerCta || kpc == pkv::kKvHeadsPerCtaWide) &&
+         p.layout == PKV_SEPARATE && p.max_candidates == 0 && p.num_kv_heads % kpc == 0 &&
+         group <= 16;
 }
 
 // Work units per row: (KV head, 16-query-head block), or groups of four KV
@@ -178,9 +180,10 @@ pkv_status check_geometry(const pkv_problem& p, const pkv_geometry* g) {
     return fail(PKV_EINVAL, "geometry num_splits %d outside [1, %d]", g->num_splits, pkv::kMaxSplits);
   if (g->min_chunk < 16 || g->min_chunk % 16)
     return fail(PKV_EINVAL, "geometry min_chunk %d is not a positive multiple of 16", g->min_chunk);
-  if (g->head_blocks != ceil_div(group, 16) || g->threads != pkv::threads_of(variant_of(p)) ||
-      (g->kv_heads_per_cta != 1 && g->kv_heads_per_cta != pkv::kKvHeadsPerCta) ||
-      (g->kv_heads_per_cta != 1 && !kvp_allowed(p)) ||
+  pkv::Variant var = variant_of(p);
+  var.kvp = g->kv_heads_per_cta > 1 ? g->kv_heads_per_cta : 0;
+  if (g->head_blocks != ceil_div(group, 16) || g->threads != pkv::threads_of(var) ||
+      (g->kv_heads_per_cta != 1 && !kvp_allowed(p, g->kv_heads_per_cta)) ||
       g->grid_x != grid_ctas_for(p, g->num_splits, g->target_ctas, g->kv_heads_per_cta) || g->grid_y != 1 ||
       g->grid_z != 1 || g->workspace_bytes != workspace_bytes_for(p, g->num_splits) ||
       g->target_ctas < 0 || (g->target_ctas > 0 && p.num_rows > kMaxBalancedRows))
@@ -271,7 +274,7 @@ pkv::SplitArgs split_args(const pkv_problem& p, const pkv_geometry& g, const Ptr
   a.group = p.num_heads / p.num_kv_heads;
   a.head_blocks = g.head_blocks;
   a.units_row = (int)units_row_of(p, g.kv_heads_per_cta);
-  a.kvp = g.kv_heads_per_cta == pkv::kKvHeadsPerCta;
+  a.kvp = g.kv_heads_per_cta > 1 ? g.kv_heads_per_cta : 0;
   a.block_size = p.block_size;
   a.log2_block = __builtin_ctz((unsigned)p.block_size);
   a.max_blocks_per_row = p.max_blocks_per_row;
@@ -410,17 +413,20 @@ pkv_status split_geometry(const pkv_problem* problem, const pkv_geometry_opts* o
   const int head_blocks = ceil_div(group, 16);
   // KV heads per CTA: four when the problem allows it (whole-record reads),
   // unless the caller asks for one
-  if (o.kv_heads_per_cta != 0 && o.kv_heads_per_cta != 1 && o.kv_heads_per_cta != pkv::kKvHeadsPerCta)
-    return fail(PKV_EINVAL, "kv_heads_per_cta must be 0, 1 or %d", pkv::kKvHeadsPerCta);
-  if (o.kv_heads_per_cta == pkv::kKvHeadsPerCta && !kvp_allowed(p))
-    return fail(PKV_EUNSUPPORTED, "four KV heads per CTA need dense rows, the SEPARATE layout, a "
-                                  "multiple of four KV heads and at most 16 query heads per KV head");
+  if (o.kv_heads_per_cta != 0 && o.kv_heads_per_cta != 1 && o.kv_heads_per_cta != pkv::kKvHeadsPerCta &&
+      o.kv_heads_per_cta != pkv::kKvHeadsPerCtaWide)
+    return fail(PKV_EINVAL, "kv_heads_per_cta must be 0, 1, %d or %d", pkv::kKvHeadsPerCta,
+                pkv::kKvHeadsPerCtaWide);
+  if (o.kv_heads_per_cta > 1 && !kvp_allowed(p, o.kv_heads_per_cta))
+    return fail(PKV_EUNSUPPORTED, "%d KV heads per CTA need dense rows, the SEPARATE layout, a "
+                                  "multiple of %d KV heads and at most 16 query heads per KV head",
+                o.kv_heads_per_cta, o.kv_heads_per_cta);
   // (automatic for head sizes up to 128: measured faster there; larger
   // heads need more registers per wave than two waves per SIMD allow)
   const int kv_per_cta = o.kv_heads_per_cta ? o.kv_heads_per_cta
-                         : (kvp_allowed(p) && p.head_size <= 128 ? pkv::kKvHeadsPerCta : 1);
+                         : (kvp_allowed(p, pkv::kKvHeadsPerCta) && p.head_size <= 128 ? pkv::kKvHeadsPerCta : 1);
   pkv::Variant var = variant_of(p);
-  var.kvp = kv_per_cta == pkv::kKvHeadsPerCta;
+  var.kvp = kv_per_cta > 1 ? kv_per_cta : 0;
   const int64_t units = std::max<int64_t>(1, (int64_t)p.num_rows * units_row_of(p, kv_per_cta));
   const int64_t cap = positions_cap(p);
 
@@ -497,7 +503,7 @@ pkv_status split_geometry(const pkv_problem* problem, const pkv_geometry_opts* o
 
   out->num_splits = S;
   out->min_chunk = min_chunk;
-  out->threads = pkv::threads_of(variant_of(p));
+  out->threads = pkv::threads_of(var);
   out->head_blocks = head_blocks;
   out->target_ctas = balanced ? (int32_t)std::min<int64_t>(target, INT32_MAX) : 0;
   out->kv_heads_per_cta = kv_per_cta;

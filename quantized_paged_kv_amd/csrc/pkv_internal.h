@@ -24,7 +24,7 @@ struct SplitArgs {
   float* ws_ml;                 // [rows, heads, S, 2]
   int rows, heads, kv_heads, group, head_blocks;
   int units_row;                // work units per row: kv_heads * head_blocks, or kv_heads / 4
-  int kvp;                      // 1: four KV heads per CTA (split_kvp_kernel)
+  int kvp;                      // 4 or 8: that many KV heads per CTA (split_kvp_kernel); else 0
   int block_size, log2_block, max_blocks_per_row, num_pool_blocks, max_candidates;
   int num_splits, min_chunk;
   int target_ctas;              // > 0: live chunk from the total work of all rows
@@ -80,7 +80,7 @@ struct Variant {
   int latent;
   int gathered;
   int ext;          // a sliding window or a soft cap is set
-  int kvp;          // four KV heads per CTA (dense rows, separate caches)
+  int kvp;          // 4 or 8 KV heads per CTA (dense rows, separate caches); else 0
 };
 
 constexpr int kWaves = 4;          // waves per split-kernel CTA
@@ -90,11 +90,15 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kLatentWaves = 4;
 constexpr int kLatentGroups = 1;
 inline int threads_of(const Variant& v) {
+  if (v.kvp > 0) return 64 * v.kvp;  // one wave per KV head
   return (v.latent && v.cache_dtype != PKV_F16) ? 64 * kLatentWaves * kLatentGroups : kThreads;
 }
 constexpr int kMaxSplits = 64;     // the combine holds one split per lane
 constexpr int kMaxBalancedRows = 1024;  // live-balanced chunks up to this many rows
-constexpr int kKvHeadsPerCta = 4;       // KV heads of one CTA in the four-head mode
+// KV heads of one CTA in the multi-head mode (split_kvp_kernel): four, or
+// eight (every head of an eight-KV-head cache record)
+constexpr int kKvHeadsPerCta = 4;
+constexpr int kKvHeadsPerCtaWide = 8;
 
 // Launchers; return hipSuccess or the launch error.  `supported` reports
 // whether a variant was compiled.

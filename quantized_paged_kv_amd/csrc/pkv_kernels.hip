@@ -1276,14 +1276,15 @@ constexpr int kKvpWavesPerSimd = 2;
 // waves per SIMD (measured better than one tile at three waves per SIMD
 // once the priorities are set).
 
-template <int CT, int D, int VD, bool EXT>
-__global__ void __launch_bounds__(kThreads)
+template <int CT, int D, int VD, bool EXT, int KPC>
+__global__ void __launch_bounds__(64 * KPC)
 __attribute__((amdgpu_waves_per_eu(kKvpWavesPerSimd)))
 split_kvp_kernel(const SplitArgs a) {
   __builtin_amdgcn_s_setprio(3);
   using C = SplitCfg<CT, D, VD, false, false>;
-  constexpr int W = kWaves;  // KV heads per CTA
-  constexpr int NST = 3;     // tiles held per wave: one consumed, two in flight
+  constexpr int W = KPC;       // KV heads per CTA, one per wave
+  constexpr int NT = 64 * W;   // threads per CTA
+  constexpr int NST = 3;       // tiles held per wave: one consumed, two in flight
   static_assert(C::CPL % 4 == 0, "float4 groups of channels per lane");
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1316,7 +1317,7 @@ split_kvp_kernel(const SplitArgs a) {
   __shared__ float s_err[W][C::NKS * 64];
   __shared__ int s_flag[2 * W];  // [w]: deep tail, [W + w]: folding, of wave w
   __shared__ float s_vs[W][VD];
-  constexpr int QPT = (C::NKS * 64 + kThreads - 1) / kThreads;
+  constexpr int QPT = (C::NKS * 64 + NT - 1) / NT;
   uint4 qraw[W][QPT];
   float4 ksc[W][QPT][2];
   Scales sc[W];
@@ -1333,8 +1334,8 @@ split_kvp_kernel(const SplitArgs a) {
   };
 #pragma unroll
   for (int u4 = 0; u4 < W; ++u4) {
-    q_issue<C::NKS, C::EB, D>(a, unit_of(u4), qraw[u4], ksc[u4]);
-    sc[u4] = load_scales<VD>(a, wk.g + u4);
+    q_issue<C::NKS, C::EB, D, QPT, NT>(a, unit_of(u4), qraw[u4], ksc[u4]);
+    sc[u4] = load_scales<VD, NT>(a, wk.g + u4);
   }
   finish_item<false, EXT>(a, wk, balanced, raw_npos, 0);
   const int len = wk.len;
@@ -1348,7 +1349,7 @@ split_kvp_kernel(const SplitArgs a) {
   (void)len;
 
   int p0, p1;
-  if (!split_range<VD>(a, wk, p0, p1)) return;
+  if (!split_range<VD, NT>(a, wk, p0, p1)) return;
   const int split = wk.split;
   const int ntiles = (p1 - p0 + 15) >> 4;
 
@@ -1497,8 +1498,8 @@ split_kvp_kernel(const SplitArgs a) {
   for (int i = 0; i < NST - 1; ++i) issue(buf[i], i);
 #pragma unroll
   for (int u4 = 0; u4 < W; ++u4) {
-    q_stage<C::NKS, C::EB, D>(qraw[u4], ksc[u4], sc[u4].k_tensor, s_q[u4], s_err[u4]);
-    stage_scales<VD>(a, sc[u4], s_vs[u4]);
+    q_stage<C::NKS, C::EB, D, QPT, NT>(qraw[u4], ksc[u4], sc[u4].k_tensor, s_q[u4], s_err[u4]);
+    stage_scales<VD, NT>(a, sc[u4], s_vs[u4]);
   }
   __syncthreads();
   const bool fold = fold_over_budget<CT, C::NKS>(a, s_err[wave], group, lane);
@@ -2385,8 +2386,12 @@ template <int CT, int D, int VD, bool LAT, bool GA, bool EXT>
 static hipError_t launch_one(const SplitArgs& a, hipStream_t stream) {
   dim3 grid(a.grid_ctas);
   if constexpr (!LAT && !GA) {
-    if (a.kvp) {
-      hipLaunchKernelGGL((split_kvp_kernel<CT, D, VD, EXT>), grid, dim3(kThreads), 0, stream, a);
+    if (a.kvp == 4) {
+      hipLaunchKernelGGL((split_kvp_kernel<CT, D, VD, EXT, 4>), grid, dim3(256), 0, stream, a);
+      return hipGetLastError();
+    }
+    if (a.kvp == 8) {
+      hipLaunchKernelGGL((split_kvp_kernel<CT, D, VD, EXT, 8>), grid, dim3(512), 0, stream, a);
       return hipGetLastError();
     }
   }
@@ -2398,11 +2403,14 @@ static hipError_t launch_one(const SplitArgs& a, hipStream_t stream) {
 }
 
 template <int CT, int D, int VD, bool LAT, bool GA, bool EXT>
-static hipError_t occupancy_one(int* n, bool kvp) {
+static hipError_t occupancy_one(int* n, int kvp) {
   if constexpr (!LAT && !GA) {
-    if (kvp)
-      return hipOccupancyMaxActiveBlocksPerMultiprocessor(n, split_kvp_kernel<CT, D, VD, EXT>,
-                                                           kThreads, 0);
+    if (kvp == 4)
+      return hipOccupancyMaxActiveBlocksPerMultiprocessor(n, split_kvp_kernel<CT, D, VD, EXT, 4>,
+                                                           256, 0);
+    if (kvp == 8)
+      return hipOccupancyMaxActiveBlocksPerMultiprocessor(n, split_kvp_kernel<CT, D, VD, EXT, 8>,
+                                                           512, 0);
   }
   if constexpr (LAT)
     return hipOccupancyMaxActiveBlocksPerMultiprocessor(n, latent_kernel<CT, GA, EXT>,
@@ -2458,7 +2466,7 @@ hipError_t launch_split(const Variant& v, const SplitArgs& a, hipStream_t stream
 
 hipError_t split_occupancy(const Variant& v, int* ctas_per_cu) {
   hipError_t err = hipErrorInvalidValue;
-#define PKV_OCC(CT, D, VD, LAT, GA, EXT) err = occupancy_one<CT, D, VD, LAT, GA, EXT>(ctas_per_cu, v.kvp != 0)
+#define PKV_OCC(CT, D, VD, LAT, GA, EXT) err = occupancy_one<CT, D, VD, LAT, GA, EXT>(ctas_per_cu, v.kvp)
   PKV_FOR_VARIANT(v, PKV_OCC);
 #undef PKV_OCC
   return err;

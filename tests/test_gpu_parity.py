@@ -489,7 +489,7 @@ def test_four_kv_heads_per_cta(cache, D, heads, kvh):
     inp = _small(cache, D, D, "separate", False, seed=21, heads=heads, kvh=kvh)
     ref, ref_lse = oracle.paged_decode(inp)
     for S in (1, 5):
-        for kpc in (1, 4):
+        for kpc in [k for k in (1, 4, 8) if kvh % k == 0]:
             announce(f"{cache} D={D} {heads}q/{kvh}kv S={S} kv_heads_per_cta={kpc}")
             got, lse, g = run_gpu(inp, splits_override=S, min_chunk=16, kv_heads_per_cta=kpc)
             assert g.kv_heads_per_cta == kpc
