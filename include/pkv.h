@@ -275,6 +275,37 @@ pkv_status split_combine(const pkv_problem* problem, const pkv_geometry* geometr
                          void* out, float* lse_out, void* stream);
 
 /*
+ * paged_decode_attention_noalloc -- paged_decode_attention for callers that
+ * cannot allocate device memory (code under hipGraph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): the same operation, arguments and
+ * kernels, without the workspace argument.  The partials live in a device
+ * array of PKV_NOALLOC_WORKSPACE_BYTES (64 MiB) that the library holds on
+ * every GPU it runs on until the process ends; the call allocates, frees
+ * and memsets nothing.  The array's device address is resolved once per
+ * device (hipGetSymbolAddress) with that device current.
+ *
+ * Limit: a geometry whose workspace_bytes exceed PKV_NOALLOC_WORKSPACE_BYTES
+ * is rejected with PKV_EWORKSPACE before anything is enqueued (fewer rows or
+ * a smaller splits_override fit; e.g. 16 rows x 32 heads x 64 splits x 128
+ * channels need 17 MB).  The array keeps the last call's partials; no call
+ * needs it cleared.  All calls on one GPU share its one array, so calls that
+ * overlap in time on one GPU (two streams, or two host threads) race and
+ * must be ordered by the caller.  Results are bitwise those of
+ * paged_decode_attention with the same geometry.
+ */
+#define PKV_NOALLOC_WORKSPACE_BYTES (64u << 20)
+
+pkv_status paged_decode_attention_noalloc(const pkv_problem* problem,
+                                          const pkv_geometry* geometry, const void* query,
+                                          const void* key_cache, const void* value_cache,
+                                          const int32_t* block_table, const int32_t* seq_lens,
+                                          const int32_t* candidates,
+                                          const int32_t* num_candidates, const float* k_scale,
+                                          const float* v_scale, float softmax_scale,
+                                          const float* head_sink, void* out, float* lse_out,
+                                          void* stream);
+
+/*
  * reshape_and_cache -- quantise-on-write of new K/V rows into the paged cache
  * (ONNX Runtime PR #29912, "Summary of Changes": ReshapeAndCache writes each
  * new token at the slot its slot_mapping entry names, quantised with

@@ -8,6 +8,7 @@ import of any entry point raises; there is no fallback.
 Entry points (same names as the C ABI in include/pkv.h):
   split_geometry(problem, ...)                -> Geometry
   paged_decode_attention(problem, geometry, ...)
+  paged_decode_attention_noalloc(problem, geometry, ...)
   paged_decode_partials(problem, geometry, ...)
   split_combine(problem, geometry, ...)
 """
@@ -57,7 +58,11 @@ class PkvError(RuntimeError):
 _lib = None
 
 SYMBOLS = ("split_geometry", "paged_decode_attention", "paged_decode_partials", "split_combine",
-           "reshape_and_cache", "pkv_status_string", "pkv_last_error")
+           "paged_decode_attention_noalloc", "reshape_and_cache", "pkv_status_string",
+           "pkv_last_error")
+
+# bytes of partials the allocation-free entry point holds per device
+NOALLOC_WORKSPACE_BYTES = 64 << 20
 
 
 def load():
@@ -80,6 +85,10 @@ def load():
     lib.paged_decode_partials.restype = ctypes.c_int
     lib.paged_decode_partials.argtypes = ([ctypes.POINTER(Problem), ctypes.POINTER(Geometry)]
                                           + [P] * 9 + [ctypes.c_float, P, ctypes.c_size_t, P])
+    lib.paged_decode_attention_noalloc.restype = ctypes.c_int
+    lib.paged_decode_attention_noalloc.argtypes = ([ctypes.POINTER(Problem),
+                                                    ctypes.POINTER(Geometry)]
+                                                   + [P] * 9 + [ctypes.c_float] + [P] * 4)
     lib.split_combine.restype = ctypes.c_int
     lib.split_combine.argtypes = [ctypes.POINTER(Problem), ctypes.POINTER(Geometry), P,
                                   ctypes.c_size_t, P, P, P, P]
@@ -151,6 +160,20 @@ def paged_decode_attention(problem: Problem, geometry: Geometry, query, key_cach
         _ptr(value_cache), _ptr(block_table), _ptr(seq_lens), _ptr(candidates),
         _ptr(num_candidates), _ptr(k_scale), _ptr(v_scale), float(softmax_scale),
         _ptr(head_sink), _ptr(out), _ptr(lse_out), _ptr(workspace), int(wb), _stream(stream)))
+
+
+def paged_decode_attention_noalloc(problem: Problem, geometry: Geometry, query, key_cache,
+                                   value_cache, block_table, seq_lens, candidates,
+                                   num_candidates, k_scale, v_scale, softmax_scale: float,
+                                   head_sink, out, lse_out, stream=None):
+    """paged_decode_attention without a workspace argument: the partials go
+    to the library's per-device array (NOALLOC_WORKSPACE_BYTES); calls that
+    overlap on one GPU race."""
+    _check(load().paged_decode_attention_noalloc(
+        ctypes.byref(problem), ctypes.byref(geometry), _ptr(query), _ptr(key_cache),
+        _ptr(value_cache), _ptr(block_table), _ptr(seq_lens), _ptr(candidates),
+        _ptr(num_candidates), _ptr(k_scale), _ptr(v_scale), float(softmax_scale),
+        _ptr(head_sink), _ptr(out), _ptr(lse_out), _stream(stream)))
 
 
 def paged_decode_partials(problem: Problem, geometry: Geometry, query, key_cache, value_cache,

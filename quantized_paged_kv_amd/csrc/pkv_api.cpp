@@ -373,6 +373,39 @@ pkv_status hip_status(hipError_t e, const char* what) {
 
 }  // namespace
 
+// Workspace of paged_decode_attention_noalloc: a file-scope device array,
+// one copy per GPU, that holds the split partials (the memory the caller
+// passes as `workspace` to paged_decode_attention).  Host code never uses
+// its name as an address: the device address of the current GPU's copy comes
+// from hipGetSymbolAddress, once per device, and is cached.
+static __device__ __align__(256) uint8_t scratch[PKV_NOALLOC_WORKSPACE_BYTES];
+
+namespace {
+
+std::mutex g_scratch_mu;
+std::unordered_map<int, void*> g_scratch_ptr;
+
+// Device address of the current device's scratch copy (resolved once per
+// device, with that device current).
+pkv_status scratch_of_current_device(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(PKV_EHIP, "hipGetDevice failed");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  auto it = g_scratch_ptr.find(dev);
+  if (it == g_scratch_ptr.end()) {
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || ptr == nullptr)
+      return fail(PKV_EHIP, "hipGetSymbolAddress(scratch) failed on device %d: %s", dev,
+                  hipGetErrorString(e));
+    it = g_scratch_ptr.emplace(dev, ptr).first;
+  }
+  *out = it->second;
+  return PKV_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 const char* pkv_status_string(pkv_status s) {
@@ -598,6 +631,35 @@ pkv_status paged_decode_attention(const pkv_problem* problem, const pkv_geometry
   const pkv::CombineArgs c = combine_args(*problem, *geometry, workspace, head_sink, out, lse_out);
   return hip_status(pkv::launch_combine(problem->v_head_size, problem->out_dtype, c, s),
                     "combine kernel launch");
+}
+
+pkv_status paged_decode_attention_noalloc(const pkv_problem* problem,
+                                          const pkv_geometry* geometry, const void* query,
+                                          const void* key_cache, const void* value_cache,
+                                          const int32_t* block_table, const int32_t* seq_lens,
+                                          const int32_t* candidates,
+                                          const int32_t* num_candidates, const float* k_scale,
+                                          const float* v_scale, float softmax_scale,
+                                          const float* head_sink, void* out, float* lse_out,
+                                          void* stream) {
+  g_err[0] = 0;
+  pkv_status st = check_problem(problem);
+  if (st != PKV_OK) return st;
+  st = check_geometry(*problem, geometry);
+  if (st != PKV_OK) return st;
+  if (geometry->workspace_bytes > (uint64_t)PKV_NOALLOC_WORKSPACE_BYTES)
+    return fail(PKV_EWORKSPACE,
+                "the problem needs %llu bytes of workspace, more than the %llu bytes the "
+                "allocation-free entry point holds per device (fewer rows or splits fit)",
+                (unsigned long long)geometry->workspace_bytes,
+                (unsigned long long)PKV_NOALLOC_WORKSPACE_BYTES);
+  void* ws = nullptr;
+  st = scratch_of_current_device(&ws);
+  if (st != PKV_OK) return st;
+  return paged_decode_attention(problem, geometry, query, key_cache, value_cache, block_table,
+                                seq_lens, candidates, num_candidates, k_scale, v_scale,
+                                softmax_scale, head_sink, out, lse_out, ws,
+                                (size_t)PKV_NOALLOC_WORKSPACE_BYTES, stream);
 }
 
 pkv_status reshape_and_cache(const pkv_problem* problem, int32_t num_tokens, const void* key,

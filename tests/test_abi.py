@@ -301,3 +301,18 @@ def test_window_and_softcap_validation_and_geometry():
     wide = pkv.make_problem(1, 8, 2, 128, 128, 16, 512, 600, sliding_window=1 << 20)
     assert pkv.split_geometry(wide, num_cus=256, ctas_per_cu=2).as_dict() == \
         pkv.split_geometry(big, num_cus=256, ctas_per_cu=2).as_dict()
+
+
+def test_noalloc_entry_point_rejects_a_workspace_beyond_its_array():
+    """The allocation-free entry point holds NOALLOC_WORKSPACE_BYTES of
+    partials per device; a larger geometry is refused before anything is
+    enqueued (no device, no pointer is touched)."""
+    # 1024 rows x 16 heads x 8 splits x 514 floats x 4 B = 269 MB of partials
+    p = pkv.make_problem(1024, 16, 1, 576, 512, 64, 64, 70000, cache_dtype="fp8",
+                         k_quant="tensor", layout="latent")
+    g = pkv.split_geometry(p, num_cus=256, ctas_per_cu=1, splits_override=8)
+    assert g.workspace_bytes > pkv.NOALLOC_WORKSPACE_BYTES
+    with pytest.raises(pkv.PkvError) as e:
+        pkv.paged_decode_attention_noalloc(p, g, 16, 16, None, 16, 16, None, None, 16, None,
+                                           0.04, None, 16, None, stream=0)
+    assert e.value.status == 4 and "allocation-free" in str(e.value)
