@@ -277,6 +277,99 @@ def test_hip_graph_replay_matches_eager_with_new_lengths():
                                ref, ref_lse, what=f"replay {lens}")
 
 
+def _replay_with_lengths(inp, lens_list, what, **geo):
+    """Capture one decode step in a HIP graph, then for each length vector:
+    write it to the device, replay four times (bitwise equal to each other
+    and to an eager call) and compare with the oracle at those lengths."""
+    import torch
+
+    import quantized_paged_kv_amd as pkv
+    from workloads.device import to_device
+
+    d = to_device(inp, "cuda")
+    prob = pkv.make_problem(**d.problem_kwargs)
+    g = pkv.split_geometry(prob, **geo)
+    ws = pkv.workspace_for(g)
+    p = inp.problem
+    out = torch.zeros((p.rows, p.heads, p.v_head_size), dtype=torch.float16, device="cuda")
+    lse = torch.zeros((p.rows, p.heads), dtype=torch.float32, device="cuda")
+
+    def step():
+        pkv.paged_decode_attention(prob, g, d.query, d.key_cache, d.value_cache, d.block_table,
+                                   d.seq_lens, d.candidates, d.num_candidates, d.k_scale,
+                                   d.v_scale, d.softmax_scale, d.head_sink, out, lse, ws)
+
+    announce(f"{what}: graph capture (S={g.num_splits}, target_ctas={g.target_ctas}, "
+             f"kv_heads_per_cta={g.kv_heads_per_cta})")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()  # warm up on the side stream
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for lens in lens_list:
+        d.seq_lens.copy_(torch.tensor(lens, dtype=torch.int32))
+        announce(f"{what}: graph replay lens={list(lens)}")
+        graph.replay()
+        torch.cuda.synchronize()
+        o_graph, l_graph = out.clone(), lse.clone()
+        for _ in range(3):
+            graph.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(o_graph, out) and torch.equal(l_graph, lse)
+        step()  # eager
+        torch.cuda.synchronize()
+        assert torch.equal(o_graph, out) and torch.equal(l_graph, lse)
+        ref_inp = Inputs(**{**inp.__dict__, "seq_lens": np.array(lens, dtype=np.int32)})
+        ref, ref_lse = oracle.paged_decode(ref_inp)
+        assert_close_to_oracle(o_graph.double().cpu().numpy(), l_graph.double().cpu().numpy(),
+                               ref, ref_lse, what=f"{what} replay {list(lens)}")
+    return g
+
+
+def _replay_lens(rows, cap, seed):
+    """Length vectors for replays: random, rows going to 0 and to the full
+    capacity, and lengths around tile and block edges (and past capacity,
+    which is clamped)."""
+    rng = np.random.default_rng(seed)
+    edges = [0, 1, 15, 16, 17, 63, 64, 65, cap - 1, cap, cap + 9, 2, 31, 33, 100, cap // 2]
+    return [rng.integers(1, cap, size=rows, endpoint=True),
+            np.where(np.arange(rows) % 2 == 0, 0, cap),
+            np.array([edges[i % len(edges)] for i in range(rows)]),
+            np.full(rows, cap), np.zeros(rows, dtype=np.int64)]
+
+
+@pytest.mark.parametrize("kpc", [0, 8])
+def test_graph_replay_continuous_batching_shape(kpc):
+    """C3's shape at a smaller capacity: 16 rows (the live-balanced
+    decomposition, every CTA reading all lengths), 32 query / 8 KV heads,
+    head 128, FP16 with a head sink: several KV heads per CTA."""
+    cap = 512
+    p = Problem(rows=16, heads=32, kv_heads=8, head_size=128, v_head_size=128, block_size=16,
+                max_blocks_per_row=cap // 16, num_pool_blocks=0, cache_dtype="f16")
+    inp = workloads.make_inputs(p, 31, cap, with_sink=True, softmax_scale=1 / np.sqrt(128))
+    geo = {"kv_heads_per_cta": kpc} if kpc else {}
+    g = _replay_with_lengths(inp, _replay_lens(16, cap, 31), f"C3 shape kpc={kpc}", **geo)
+    assert g.target_ctas > 0 and g.kv_heads_per_cta == (kpc or 4) and g.num_splits > 1
+
+
+def test_graph_replay_latent_shape():
+    """C5's shape at a smaller capacity: 16 rows of the latent FP8 layout
+    (16 query heads over one 576-channel head, V = first 512 channels, block
+    64): the live-balanced decomposition on the latent kernel's
+    direct-to-LDS ring."""
+    cap = 1024
+    p = Problem(rows=16, heads=16, kv_heads=1, head_size=576, v_head_size=512, block_size=64,
+                max_blocks_per_row=cap // 64, num_pool_blocks=0, cache_dtype="fp8",
+                k_quant="tensor", v_quant="tensor", layout="latent")
+    inp = workloads.make_inputs(p, 32, cap, with_sink=True, softmax_scale=1 / 24)
+    g = _replay_with_lengths(inp, _replay_lens(16, cap, 32), "C5 shape")
+    assert g.target_ctas > 0 and g.num_splits > 1
+
+
 # ---------------------------------------------------------------------------
 # the pages' worked examples (FP32 output)
 # ---------------------------------------------------------------------------
@@ -308,10 +401,26 @@ def test_worked_examples_on_gpu(row):
                  softmax_scale=float(sscale), k_scale=np.array([1.0], np.float32),
                  v_scale=np.array([float(vscale)], np.float32),
                  candidates=np.array([[3, 11]], np.int32), num_candidates=np.array([2], np.int32))
-    announce(f"worked example {name}")
-    got, _, _ = run_gpu(inp, splits_override=1)
-    assert got[0, 0, 0] == pytest.approx(float(expected), rel=2e-3)
-    assert np.all(got[0, 0, 1:] == 0)
+    # Accuracy bound of the FP32 arithmetic on these rows: every probability
+    # enters the PV products with a relative error of at most about 2^-22
+    # (FP16 high + residual tiles) plus the FP32 exponential's, so the output
+    # error is at most 2^-21 of the magnitude of the summed terms,
+    # sum_t (p_t / l) |V_t| -- 2^-21 |O| (5e-7 relative) where nothing cancels,
+    # and 2^-21 * 4064 for the signed cancellation, whose exact result 0.496 is
+    # what remains of +-4064 (a single FP16 tile gives 0 there).
+    x = np.array([float(q0) * float(ka0) + float(q1) * float(ka1),
+                  float(q0) * float(kb0) + float(q1) * float(kb1)]) * float(sscale)
+    w = np.exp(x - x.max())
+    w /= w.sum()
+    mag = float(np.sum(w * np.abs(np.array([float(va), float(vb)]) * float(vscale))))
+    tol = 2.0 ** -21 * mag
+    for S in (1, 3):
+        announce(f"worked example {name} S={S}")
+        got, lse, _ = run_gpu(inp, splits_override=S, min_chunk=16)
+        assert abs(got[0, 0, 0] - float(expected)) <= tol, (got[0, 0, 0], float(expected), tol)
+        assert np.all(got[0, 0, 1:] == 0)
+        ref, ref_lse = oracle.paged_decode(inp)
+        assert abs(lse[0, 0] - ref_lse[0, 0]) <= 2.0 ** -21 * max(1.0, abs(ref_lse[0, 0]))
 
 
 # ---------------------------------------------------------------------------

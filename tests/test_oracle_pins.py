@@ -606,3 +606,181 @@ def test_softcap_bounds_and_limits():
     tight = Inputs(**{**inp.__dict__, "problem": replace(inp.problem, softcap=0.5)})
     o2, _ = oracle.paged_decode(tight)
     assert np.abs(o2 - o0).max() > 1e-3
+
+
+# ---------------------------------------------------------------------------
+# the quantise-on-write quotient and codes against exact rational arithmetic
+# (reading: the quotient x / scale is rounded once to FP32, then encoded)
+# ---------------------------------------------------------------------------
+
+from fractions import Fraction  # noqa: E402
+
+
+def _round_to_format(q: Fraction, mant_bits: int, emin: int, vmax: Fraction, sat: bool):
+    """Nearest value of a binary format to the rational q, ties to an even
+    significand: mant_bits fraction bits, smallest normal exponent emin
+    (subnormals below it), largest finite vmax; beyond it +-inf (sat=False,
+    past the halfway point to the next binade) or +-vmax (sat=True)."""
+    if q == 0:
+        return Fraction(0)
+    neg = q < 0
+    a = -q if neg else q
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    if Fraction(2) ** e > a:
+        e -= 1
+    quantum = Fraction(2) ** (max(e, emin) - mant_bits)
+    m = a / quantum
+    n = m.numerator // m.denominator
+    rem = m - n
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and n % 2 == 1):
+        n += 1
+    v = n * quantum
+    if v > vmax:
+        if sat:
+            v = vmax
+        else:
+            return Fraction(-1 if neg else 1) * 10 ** 60  # stands for infinity
+    return -v if neg else v
+
+
+def rn32(q):
+    return _round_to_format(q, 23, -126, Fraction(2 ** 24 - 1, 2 ** 23) * 2 ** 127, False)
+
+
+def rn16(q):
+    return _round_to_format(q, 10, -14, Fraction(65504), False)
+
+
+def rn_e4m3fn(q):
+    return _round_to_format(q, 3, -6, Fraction(448), True)
+
+
+def _frac_to_float(v: Fraction) -> float:
+    return math.copysign(math.inf, v) if abs(v) >= 10 ** 59 else float(v)
+
+
+def _expected_code(x16, s32, cache):
+    """The code of one element from the exact quotient: RN32(x / s), then
+    INT8: clip(round half even) / FP8: nearest e4m3fn, ties even, saturating
+    / FP16: RN16."""
+    q = rn32(Fraction(float(x16)) / Fraction(float(s32)))
+    if cache == "i8":
+        n = q.numerator // q.denominator
+        rem = q - n
+        if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and n % 2 == 1):
+            n += 1
+        return min(127, max(-128, n))
+    if cache == "fp8":
+        v = rn_e4m3fn(q)
+        mag = abs(v)
+        code = int(np.nonzero(cache_write._FP8_VALS == float(mag))[0][0])
+        return code | (0x80 if (v < 0 or (v == 0 and q < 0)) else 0)
+    v = _frac_to_float(rn16(q))
+    # a quotient that rounds to zero keeps its sign (IEEE)
+    return math.copysign(0.0, float(x16) / float(s32)) if v == 0 else v
+
+
+def _writer_samples(seed, n):
+    rng = np.random.default_rng(seed)
+    x = (rng.normal(0, 1, n) * np.exp2(rng.integers(-20, 12, n))).astype(np.float16)
+    x = x[np.isfinite(x)]
+    s = (rng.uniform(0.5, 1.0, len(x)) * np.exp2(rng.integers(-30, 20, len(x)))).astype(np.float32)
+    return x, s
+
+
+def test_rational_rounding_helpers_against_numpy_casts():
+    """The Fraction-based rounding agrees with IEEE casts of doubles on
+    values where those are single roundings (a double holds every product
+    and sum used here exactly)."""
+    rng = np.random.default_rng(3)
+    v = rng.normal(0, 1, 3000) * np.exp2(rng.integers(-160, 130, 3000))
+    for x in v:
+        assert _frac_to_float(rn32(Fraction(float(x)))) == float(np.float32(x))
+    w = rng.normal(0, 1, 3000) * np.exp2(rng.integers(-26, 17, 3000))
+    for x in w:
+        if abs(x) < 65520:
+            assert _frac_to_float(rn16(Fraction(float(x)))) == float(np.float16(x))
+
+
+@pytest.mark.parametrize("cache", ["i8", "fp8", "f16"])
+def test_writer_codes_from_the_exact_quotient(cache):
+    """quantize() equals the definition evaluated in exact rationals: the
+    quotient x / scale rounded once to FP32, then encoded.  Sampled inputs
+    over wide exponent ranges, plus quotients that are exact ties: of INT8
+    codes (k + 1/2), of FP8 values, of FP16 values, and FP32 ties in the
+    subnormal range (the only FP32 ties a FP16 / FP32 quotient can hit)."""
+    x, s = _writer_samples(11, 1500)
+    extra_x = [2.5, -3.5, 0.5, -0.5, 126.5, -127.5, 1.0625, 1.1875, 2.0 ** -7 * 3, 1 + 2 ** -11,
+               3 * 2 ** -24, -3 * 2 ** -24, 5 * 2 ** -24]
+    extra_s = [1.0, 1.0, 1.0, 1.0, 1.0, 1.0, 1.0, 1.0, 1.0, 1.0, 2.0 ** 126, 2.0 ** 126,
+               2.0 ** 126]
+    x = np.concatenate([x, np.array(extra_x, np.float16)])
+    s = np.concatenate([s, np.array(extra_s, np.float32)])
+    got = cache_write.quantize(x, s, cache)
+    for i in range(len(x)):
+        exp = _expected_code(x[i], s[i], cache)
+        if cache == "f16":
+            g = float(got[i])
+            assert g == exp or (math.isnan(g) and math.isnan(exp)), (x[i], s[i], g, exp)
+            assert math.copysign(1, g) == math.copysign(1, exp) or g != 0
+        elif cache == "fp8":
+            assert int(got[i]) == exp, (x[i], s[i], int(got[i]), exp)
+        else:
+            assert int(got[i]) == exp, (x[i], s[i], int(got[i]), exp)
+
+
+def test_writer_fp32_subnormal_quotient_ties():
+    """3 * 2^-24 (an FP16 subnormal) / 2^126 = 1.5 * 2^-149 lies halfway
+    between the two smallest FP32 subnormals; rounding half to even gives
+    2^-148, and 5 * 2^-24 / 2^126 = 2.5 * 2^-149 gives 2^-148 as well."""
+    for num in (3, 5):
+        q = rn32(Fraction(num * 2 ** -24) / Fraction(2 ** 126))
+        assert q == Fraction(2) ** -148
+        v = np.float16(num * 2 ** -24).astype(np.float32) / np.float32(2.0 ** 126)
+        assert float(v) == 2.0 ** -148
+
+
+def test_writer_fp16_branch_against_torch():
+    """The FP16-cache branch against torch's float32 division and half
+    cast (a library routine), over sampled inputs and every finite FP16
+    value under three scales."""
+    x, s = _writer_samples(12, 20000)
+    allx = workloads.every_fp16_value()
+    allx = allx[np.isfinite(allx)]
+    for xs, ss in ((x, s), (allx, np.float32(0.37)), (allx, np.float32(3.0e-5)),
+                   (allx, np.float32(7.5))):
+        ref = (torch.from_numpy(xs.astype(np.float32)) / torch.from_numpy(
+            np.broadcast_to(np.asarray(ss, np.float32), xs.shape).copy())).half().numpy()
+        got = cache_write.quantize(xs, ss, "f16")
+        assert np.array_equal(got.view(np.uint16), ref.view(np.uint16))
+
+
+def test_writer_fp16_double_rounding_is_the_stated_reading():
+    """Rounding the FP32 quotient to FP16 (the reading taken) is not always
+    rounding the exact quotient to FP16: when RN32(x / s) lands on an FP16
+    midpoint that the exact quotient misses, the two differ.  Find such
+    inputs and check that quantize() follows the FP32-first reading there."""
+    rng = np.random.default_rng(5)
+    found = 0
+    for _ in range(4000):
+        x = np.float16(rng.uniform(1, 2) * 2.0 ** int(rng.integers(-3, 4)))
+        # an FP16 midpoint T near x / s, and an FP32 scale s = RN32(x / T)
+        # nudged by a few ulps so that x / s straddles T by less than an FP32
+        # half-ulp
+        y = rn16(Fraction(float(x)) / Fraction(float(rng.uniform(0.7, 1.4))))
+        ulp16 = Fraction(2) ** (max(y.numerator.bit_length() - y.denominator.bit_length(), -14) - 10)
+        T = y + ulp16 / 2
+        s0 = np.float32(float(Fraction(float(x)) / T))
+        for k in range(-3, 4):
+            s = np.float32(s0 + k * np.spacing(s0))
+            q = Fraction(float(x)) / Fraction(float(s))
+            if rn32(q) == T and q != T:
+                exact = _frac_to_float(rn16(q))
+                twice = _frac_to_float(rn16(rn32(q)))
+                if exact != twice:
+                    found += 1
+                    got = float(cache_write.quantize(np.array([x]), s, "f16")[0])
+                    assert got == twice and got != exact
+        if found >= 3:
+            break
+    assert found >= 3
