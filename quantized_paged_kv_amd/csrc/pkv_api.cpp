@@ -85,8 +85,11 @@ pkv_status check_problem(const pkv_problem* p) {
     return fail(PKV_EUNSUPPORTED, "block_size (%d) must be a power of two >= 16", p->block_size);
   if (p->max_blocks_per_row <= 0) return fail(PKV_EINVAL, "max_blocks_per_row must be positive");
   if (p->num_pool_blocks <= 0) return fail(PKV_EINVAL, "num_pool_blocks must be positive");
-  if ((int64_t)p->max_blocks_per_row * p->block_size > INT32_MAX)
-    return fail(PKV_EINVAL, "capacity max_blocks_per_row * block_size overflows int32");
+  // positions are 32-bit on the device; at most 2^30 keeps every sum of two
+  // of them in range
+  if ((int64_t)p->max_blocks_per_row * p->block_size > (int64_t)1 << 30)
+    return fail(PKV_EINVAL, "capacity max_blocks_per_row * block_size exceeds 2^30 positions");
+  if (p->max_candidates > (1 << 30)) return fail(PKV_EINVAL, "max_candidates exceeds 2^30");
   if (p->max_candidates < 0) return fail(PKV_EINVAL, "max_candidates < 0");
   if (p->cache_dtype != PKV_F16 && p->cache_dtype != PKV_I8 && p->cache_dtype != PKV_FP8_E4M3FN)
     return fail(PKV_EINVAL, "cache_dtype must be PKV_F16, PKV_I8 or PKV_FP8_E4M3FN");
@@ -117,6 +120,12 @@ pkv_status check_problem(const pkv_problem* p) {
                 "64/64, 128/128, 256/256 SEPARATE; 576/512 LATENT)",
                 p->head_size, p->v_head_size, p->layout);
   return PKV_OK;
+}
+
+// The live-balanced decomposition: up to kMaxBalancedRows rows whose
+// positions cannot sum to 2^31.
+bool balance_fits(const pkv_problem& p) {
+  return p.num_rows <= kMaxBalancedRows && (int64_t)p.num_rows * positions_cap(p) <= INT32_MAX;
 }
 
 uint64_t workspace_bytes_for(const pkv_problem& p, int S) {
@@ -186,7 +195,7 @@ pkv_status check_geometry(const pkv_problem& p, const pkv_geometry* g) {
       (g->kv_heads_per_cta != 1 && !kvp_allowed(p, g->kv_heads_per_cta)) ||
       g->grid_x != grid_ctas_for(p, g->num_splits, g->target_ctas, g->kv_heads_per_cta) || g->grid_y != 1 ||
       g->grid_z != 1 || g->workspace_bytes != workspace_bytes_for(p, g->num_splits) ||
-      g->target_ctas < 0 || (g->target_ctas > 0 && p.num_rows > kMaxBalancedRows))
+      g->target_ctas < 0 || (g->target_ctas > 0 && !balance_fits(p)))
     return fail(PKV_EINVAL, "geometry does not belong to this problem (call split_geometry)");
   return PKV_OK;
 }
@@ -466,7 +475,9 @@ pkv_status split_geometry(const pkv_problem* problem, const pkv_geometry_opts* o
   // The device balances chunk sizes across rows from the live lengths when
   // the row count is modest (each CTA reads every row's length).
   if (o.balance < 0 || o.balance > 2) return fail(PKV_EINVAL, "balance must be 0, 1 or 2");
-  const bool balanced = p.num_rows <= kMaxBalancedRows &&
+  // (its CTAs sum the live positions of all rows in 32 bits: only when that
+  // sum cannot reach 2^31)
+  const bool balanced = balance_fits(p) &&
                         (o.balance == 1 || (o.balance == 0 && p.num_rows >= kMinBalancedRows));
   int cus = o.num_cus, occ = o.ctas_per_cu;
   if (cus == 0 || occ == 0) {

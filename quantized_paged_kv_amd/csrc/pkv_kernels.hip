@@ -384,6 +384,8 @@ __device__ __forceinline__ bool locate_balanced(const SplitArgs& a, int lane, Wo
     raw[i] = GATHER ? a.num_candidates[rr] : a.seq_lens[rr];
   }
   int np[NR];
+  // (the host uses this decomposition only when rows * capacity < 2^31, so
+  // the total fits 32 bits)
   int tot = 0;
 #pragma unroll
   for (int i = 0; i < NR; ++i) {
@@ -412,6 +414,7 @@ __device__ __forceinline__ bool locate_balanced(const SplitArgs& a, int lane, Wo
   for (int i = 0; i < NR; ++i) {
     if (64 * i >= a.rows) break;
     const int rr = lane + 64 * i;
+    // (capacities are at most 2^30 positions, so nothing here overflows)
     const int n = rr < a.rows ? min(S, max(1, (np[i] + cgl - 1) / cgl)) : 0;
     const int items = n * units_row;
     int incl = items;

@@ -316,3 +316,26 @@ def test_noalloc_entry_point_rejects_a_workspace_beyond_its_array():
         pkv.paged_decode_attention_noalloc(p, g, 16, 16, None, 16, 16, None, None, 16, None,
                                            0.04, None, 16, None, stream=0)
     assert e.value.status == 4 and "allocation-free" in str(e.value)
+
+
+def test_capacity_beyond_2p30_positions_is_rejected():
+    """Positions are 32-bit on the device; a capacity of at most 2^30 keeps
+    every sum of two of them in range (and 1024 rows' total in 64 bits)."""
+    ok = pkv.make_problem(1, 4, 1, 64, 64, 1 << 16, 1 << 14, 10)  # exactly 2^30
+    pkv.split_geometry(ok, num_cus=256, ctas_per_cu=2)
+    bad = pkv.make_problem(1, 4, 1, 64, 64, 1 << 16, (1 << 14) + 1, 10)
+    with pytest.raises(pkv.PkvError) as e:
+        pkv.split_geometry(bad, num_cus=256, ctas_per_cu=2)
+    assert e.value.status == 1 and "2^30" in str(e.value)
+
+
+def test_live_balanced_only_when_the_position_total_fits_32_bits():
+    """The live-balanced CTAs sum every row's positions in 32 bits, so the
+    geometry uses it only while rows * capacity < 2^31; beyond, the static
+    decomposition, even when asked for the balanced one."""
+    small = pkv.make_problem(1024, 8, 2, 64, 64, 16, (1 << 21) // 16, 10)  # 2^31 exactly
+    g = pkv.split_geometry(small, num_cus=256, ctas_per_cu=2, balance=1)
+    assert g.target_ctas == 0
+    fits = pkv.make_problem(1023, 8, 2, 64, 64, 16, (1 << 21) // 16, 10)
+    g = pkv.split_geometry(fits, num_cus=256, ctas_per_cu=2, balance=1)
+    assert g.target_ctas > 0
