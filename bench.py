@@ -551,8 +551,9 @@ def measure_decode(args, dev, workload: str, with_partials: bool = True) -> dict
     vals = [d.value_cache] + ([d.value_cache.clone() for _ in range(R - 1)]
                               if d.value_cache is not None else [None] * (R - 1))
     odt = torch.float32 if d.problem_kwargs["out_dtype"] == "f32" else torch.float16
-    out = torch.empty((p.rows, p.heads, p.v_head_size), dtype=odt, device=dev)
-    lse = torch.empty((p.rows, p.heads), dtype=torch.float32, device=dev)
+    qrows = p.rows * max(1, p.query_tokens)  # query rows: rows x tokens per row
+    out = torch.empty((qrows, p.heads, p.v_head_size), dtype=odt, device=dev)
+    lse = torch.empty((qrows, p.heads), dtype=torch.float32, device=dev)
     # a read of 512 MiB (twice the Infinity Cache) before every timed round
     # evicts the replicas and leaves clean lines (a write would leave dirty
     # lines whose write-back the first timed steps would pay for)

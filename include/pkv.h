@@ -44,6 +44,19 @@
  * [.., 1 row per token and KV head, head_size]; V^ is the first v_head_size
  * channels of the K row, with the K scales.
  *
+ * Several query tokens per row (query_tokens = T > 1; the multi-token decode
+ * of speculative and chunked steps, ONNX Runtime PR #33707 "Testing": 1, 3
+ * and 8 query rows of one sequence).  A row is then one sequence with T new
+ * query tokens that share its block-table row; seq_lens[r] counts all T of
+ * them, and token j (0 <= j < T) attends causally:
+ *   len_j  = max(0, len - (T - 1 - j)),  T_j = [0, len_j)
+ * query is [num_rows, T, num_heads, head_size], out [num_rows, T, num_heads,
+ * v_head_size], lse [num_rows, T, num_heads]; the result for token j is the
+ * definition above with len_j.  Every KV tile a CTA reads serves all T tokens
+ * of its query heads (the (token, head) pairs of a KV head fill the 16-wide
+ * MFMA tile: T * group <= 16 reads each tile once).  Dense rows, the
+ * SEPARATE layout, no sliding window, 1 <= T <= 16.
+ *
  * Memory layouts (all row-major, device memory unless stated):
  *   query        [num_rows, num_heads, head_size]              float16
  *   key_cache    [num_pool_blocks, block_size, num_kv_heads, head_size]
@@ -128,6 +141,7 @@ typedef struct {
   int32_t layout;          /* pkv_layout */
   int32_t sliding_window;  /* > 0: attend to the last sliding_window positions only; 0: all */
   float softcap;           /* > 0: logit soft cap c, x <- c tanh(x / c); 0: none */
+  int32_t query_tokens;    /* query tokens per row T (0 or 1: one); T > 1: see below */
 } pkv_problem;
 
 /* Optional knobs of split_geometry (pass NULL for all defaults; 0 = default). */

@@ -33,6 +33,10 @@ constexpr int kMinBalancedRows = 16;
 
 bool aligned(const void* p, size_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
 
+// Query tokens per row and head slots per KV head ((token, head) pairs).
+int qtok_of(const pkv_problem& p) { return p.query_tokens > 1 ? p.query_tokens : 1; }
+int vgroup_of(const pkv_problem& p) { return qtok_of(p) * (p.num_heads / p.num_kv_heads); }
+
 pkv::Variant variant_of(const pkv_problem& p) {
   pkv::Variant v;
   v.cache_dtype = p.cache_dtype;
@@ -42,6 +46,7 @@ pkv::Variant variant_of(const pkv_problem& p) {
   v.gathered = p.max_candidates > 0;
   v.ext = p.sliding_window > 0 || p.softcap > 0.0f;
   v.kvp = 0;
+  v.mt = qtok_of(p) > 1;
   return v;
 }
 
@@ -49,16 +54,15 @@ pkv::Variant variant_of(const pkv_problem& p) {
 // separate caches, a multiple of kpc KV heads and at most 16 query heads per
 // KV head.
 bool kvp_allowed(const pkv_problem& p, int kpc) {
-  const int group = p.num_heads / p.num_kv_heads;
   return (kpc == pkv::kKvHeadsPerCta || kpc == pkv::kKvHeadsPerCtaWide) &&
          p.layout == PKV_SEPARATE && p.max_candidates == 0 && p.num_kv_heads % kpc == 0 &&
-         group <= 16;
+         vgroup_of(p) <= 16;
 }
 
 // Work units per row: (KV head, 16-query-head block), or groups of four KV
 // heads in the four-head mode.
 int64_t units_row_of(const pkv_problem& p, int kv_per_cta) {
-  return (int64_t)(p.num_kv_heads / kv_per_cta) * ceil_div(p.num_heads / p.num_kv_heads, 16);
+  return (int64_t)(p.num_kv_heads / kv_per_cta) * ceil_div(vgroup_of(p), 16);
 }
 
 // Most positions one row can have: the candidate-list capacity (gathered
@@ -106,7 +110,17 @@ pkv_status check_problem(const pkv_problem* p) {
     if (p->layout == PKV_SEPARATE && p->v_quant == PKV_QUANT_NONE)
       return fail(PKV_EINVAL, "a quantised cache needs v_quant PER_TENSOR or PER_CHANNEL");
   }
-  if ((int64_t)p->num_rows * p->num_kv_heads * ceil_div(p->num_heads / p->num_kv_heads, 16) * 64 >
+  if (p->query_tokens < 0) return fail(PKV_EINVAL, "query_tokens < 0");
+  if (p->query_tokens > 1) {
+    if (p->query_tokens > 16)
+      return fail(PKV_EUNSUPPORTED, "query_tokens %d exceeds 16", p->query_tokens);
+    if (p->max_candidates > 0 || p->layout != PKV_SEPARATE || p->sliding_window > 0)
+      return fail(PKV_EUNSUPPORTED, "several query tokens per row need dense rows, the SEPARATE "
+                                    "layout and no sliding window");
+  }
+  if ((int64_t)p->num_rows * qtok_of(*p) * p->num_heads > INT32_MAX)
+    return fail(PKV_EUNSUPPORTED, "num_rows * query_tokens * num_heads is too large");
+  if ((int64_t)p->num_rows * p->num_kv_heads * ceil_div(vgroup_of(*p), 16) * 64 >
       INT32_MAX)
     return fail(PKV_EUNSUPPORTED, "num_rows * num_kv_heads * ceil(group / 16) is too large");
   if (p->sliding_window < 0) return fail(PKV_EINVAL, "sliding_window < 0");
@@ -129,7 +143,7 @@ bool balance_fits(const pkv_problem& p) {
 }
 
 uint64_t workspace_bytes_for(const pkv_problem& p, int S) {
-  const uint64_t pairs = (uint64_t)p.num_rows * p.num_heads;
+  const uint64_t pairs = (uint64_t)p.num_rows * qtok_of(p) * p.num_heads;
   return pairs * S * p.v_head_size * sizeof(float) + pairs * S * 2 * sizeof(float);
 }
 
@@ -184,14 +198,13 @@ pkv_status device_numbers(const pkv::Variant& v, int* cus, int* occ) {
 
 pkv_status check_geometry(const pkv_problem& p, const pkv_geometry* g) {
   if (!g) return fail(PKV_EINVAL, "geometry is NULL");
-  const int group = p.num_heads / p.num_kv_heads;
   if (g->num_splits < 1 || g->num_splits > pkv::kMaxSplits)
     return fail(PKV_EINVAL, "geometry num_splits %d outside [1, %d]", g->num_splits, pkv::kMaxSplits);
   if (g->min_chunk < 16 || g->min_chunk % 16)
     return fail(PKV_EINVAL, "geometry min_chunk %d is not a positive multiple of 16", g->min_chunk);
   pkv::Variant var = variant_of(p);
   var.kvp = g->kv_heads_per_cta > 1 ? g->kv_heads_per_cta : 0;
-  if (g->head_blocks != ceil_div(group, 16) || g->threads != pkv::threads_of(var) ||
+  if (g->head_blocks != ceil_div(vgroup_of(p), 16) || g->threads != pkv::threads_of(var) ||
       (g->kv_heads_per_cta != 1 && !kvp_allowed(p, g->kv_heads_per_cta)) ||
       g->grid_x != grid_ctas_for(p, g->num_splits, g->target_ctas, g->kv_heads_per_cta) || g->grid_y != 1 ||
       g->grid_z != 1 || g->workspace_bytes != workspace_bytes_for(p, g->num_splits) ||
@@ -264,7 +277,7 @@ pkv::SplitArgs split_args(const pkv_problem& p, const pkv_geometry& g, const Ptr
                           float softmax_scale, void* workspace) {
   pkv::SplitArgs a;
   std::memset(&a, 0, sizeof(a));
-  const uint64_t pairs = (uint64_t)p.num_rows * p.num_heads;
+  const uint64_t pairs = (uint64_t)p.num_rows * qtok_of(p) * p.num_heads;
   a.query = static_cast<const uint16_t*>(x.query);
   a.key_cache = static_cast<const uint8_t*>(x.key_cache);
   a.value_cache = static_cast<const uint8_t*>(x.value_cache);
@@ -281,6 +294,7 @@ pkv::SplitArgs split_args(const pkv_problem& p, const pkv_geometry& g, const Ptr
   a.heads = p.num_heads;
   a.kv_heads = p.num_kv_heads;
   a.group = p.num_heads / p.num_kv_heads;
+  a.qtok = qtok_of(p);
   a.head_blocks = g.head_blocks;
   a.units_row = (int)units_row_of(p, g.kv_heads_per_cta);
   a.kvp = g.kv_heads_per_cta > 1 ? g.kv_heads_per_cta : 0;
@@ -312,13 +326,13 @@ pkv::SplitArgs split_args(const pkv_problem& p, const pkv_geometry& g, const Ptr
 pkv::CombineArgs combine_args(const pkv_problem& p, const pkv_geometry& g, const void* ws,
                               const float* sink, void* out, float* lse) {
   pkv::CombineArgs c;
-  const uint64_t pairs = (uint64_t)p.num_rows * p.num_heads;
+  const uint64_t pairs = (uint64_t)p.num_rows * qtok_of(p) * p.num_heads;
   c.ws_acc = static_cast<const float*>(ws);
   c.ws_ml = c.ws_acc + pairs * g.num_splits * p.v_head_size;
   c.head_sink = sink;
   c.out = out;
   c.lse_out = lse;
-  c.rows = p.num_rows;
+  c.rows = p.num_rows * qtok_of(p);
   c.heads = p.num_heads;
   c.num_splits = g.num_splits;
   c.skip_empty = g.target_ctas > 0;
@@ -451,8 +465,7 @@ pkv_status split_geometry(const pkv_problem* problem, const pkv_geometry_opts* o
     return fail(PKV_EINVAL, "max_splits %d exceeds %d", max_splits, pkv::kMaxSplits);
   const int waves_req = o.waves;
 
-  const int group = p.num_heads / p.num_kv_heads;
-  const int head_blocks = ceil_div(group, 16);
+  const int head_blocks = ceil_div(vgroup_of(p), 16);
   // KV heads per CTA: four when the problem allows it (whole-record reads),
   // unless the caller asks for one
   if (o.kv_heads_per_cta != 0 && o.kv_heads_per_cta != 1 && o.kv_heads_per_cta != pkv::kKvHeadsPerCta &&
@@ -495,7 +508,7 @@ pkv_status split_geometry(const pkv_problem* problem, const pkv_geometry_opts* o
   // (per work unit: its KV heads' query heads, and the KV bytes of one
   // position of all its KV heads)
   const int64_t partial_bytes =
-      (int64_t)kv_per_cta * (p.num_heads / p.num_kv_heads) * (p.v_head_size + 2) * 4;
+      (int64_t)kv_per_cta * vgroup_of(p) * (p.v_head_size + 2) * 4;
   const int64_t row_bytes = (int64_t)kv_per_cta *
                             (p.layout == PKV_LATENT ? p.head_size : p.head_size + p.v_head_size) *
                             (p.cache_dtype == PKV_F16 ? 2 : 1);

@@ -23,6 +23,7 @@ struct SplitArgs {
   float* ws_acc;                // [rows, heads, S, VD]
   float* ws_ml;                 // [rows, heads, S, 2]
   int rows, heads, kv_heads, group, head_blocks;
+  int qtok;                     // query tokens per row (T >= 1; T > 1: head slots are (token, head))
   int units_row;                // work units per row: kv_heads * head_blocks, or kv_heads / 4
   int kvp;                      // 4 or 8: that many KV heads per CTA (split_kvp_kernel); else 0
   int block_size, log2_block, max_blocks_per_row, num_pool_blocks, max_candidates;
@@ -52,7 +53,7 @@ struct CombineArgs {
   const float* head_sink;       // [heads] or null
   void* out;                    // [rows, heads, VD]
   float* lse_out;               // [rows, heads] or null
-  int rows, heads, num_splits;
+  int rows, heads, num_splits;        // rows: query rows (rows x tokens per row)
   int skip_empty;               // read only splits with a nonzero weight
 };
 
@@ -81,6 +82,7 @@ struct Variant {
   int gathered;
   int ext;          // a sliding window or a soft cap is set
   int kvp;          // 4 or 8 KV heads per CTA (dense rows, separate caches); else 0
+  int mt;           // several query tokens per row (dense rows, separate caches)
 };
 
 constexpr int kWaves = 4;          // waves per split-kernel CTA

@@ -469,11 +469,49 @@ __device__ __forceinline__ void static_item(const SplitArgs& a, Work& w) {
   w.lo = w.base = 0;
 }
 
+// Several query tokens per row (MT, the multi-token decode of speculative
+// and chunked steps): the T tokens of a row share its block-table row and
+// attend causally, token j the positions [0, len - T + 1 + j).  The (token,
+// query head) pairs of one KV head are its "virtual heads" v = j * group + h
+// (T * group of them), taken 16 per head block like the query heads of one
+// token, so every KV tile a CTA reads serves all the tokens of its heads.
+template <bool MT = false>
 __device__ __forceinline__ void unit_heads(const SplitArgs& a, Work& w) {
   w.g = w.u / a.head_blocks;
   w.hb = w.u - w.g * a.head_blocks;
-  w.h0 = w.g * a.group + w.hb * 16;
-  w.nh = min(16, a.group - w.hb * 16);
+  if constexpr (MT) {
+    w.h0 = w.g * a.group;
+    w.nh = min(16, a.qtok * a.group - w.hb * 16);
+  } else {
+    w.h0 = w.g * a.group + w.hb * 16;
+    w.nh = min(16, a.group - w.hb * 16);
+  }
+}
+
+// Head slot e (0 <= e < w.nh) of a work unit: its (row, query token, head)
+// as the index of the query / output / lse row, the query head, and the
+// token.  One token per row: head h0 + e of row r.  Several: virtual head
+// hb * 16 + e of the unit's KV heads g, g + 1, ... (T * group each; units
+// of several KV heads have one head block).
+struct HeadSlot {
+  size_t pair;  // (row * T + token) * heads + head
+  int h;        // query head
+  int tok;      // query token of the row
+};
+
+template <bool MT = false>
+__device__ __forceinline__ HeadSlot head_slot(const SplitArgs& a, const Work& w, int e) {
+  if constexpr (!MT) {
+    return HeadSlot{(size_t)w.r * a.heads + w.h0 + e, w.h0 + e, 0};
+  } else {
+    const int vg = a.qtok * a.group;  // virtual heads per KV head
+    const int va = w.hb * 16 + e;
+    const int go = va / vg;           // KV head g + go
+    const int v = va - go * vg;
+    const int j = v / a.group;
+    const int h = (w.g + go) * a.group + (v - j * a.group);
+    return HeadSlot{((size_t)w.r * a.qtok + j) * a.heads + h, h, j};
+  }
 }
 
 // Clamped lengths from the raw values read in the prologue: raw_npos (static
@@ -584,7 +622,7 @@ struct WaveBlocks {
   }
 };
 
-template <int VD, int NT = kThreads>
+template <int VD, int NT = kThreads, bool MT = false>
 __device__ __forceinline__ bool split_range(const SplitArgs& a, const Work& w, int& p0, int& p1) {
   const int S = a.num_splits;
   int chunk;
@@ -596,23 +634,22 @@ __device__ __forceinline__ bool split_range(const SplitArgs& a, const Work& w, i
     p0 = static_p0(a, w.split);
   }
   p1 = min(w.npos, p0 + chunk);
-  const size_t pair0 = (size_t)w.r * a.heads + w.h0;
   float2* const ml = reinterpret_cast<float2*>(a.ws_ml);
   if (a.target_ctas > 0 && w.split == w.n_row - 1) {
     // the row's last split also publishes the splits n_row .. S-1, which have
     // no CTA in this mode
     for (int e = threadIdx.x; e < w.nh * (S - w.n_row); e += NT)
-      ml[(pair0 + e % w.nh) * S + w.n_row + e / w.nh] = make_float2(kNegInf, 0.0f);
+      ml[head_slot<MT>(a, w, e % w.nh).pair * S + w.n_row + e / w.nh] = make_float2(kNegInf, 0.0f);
   }
   if (p0 >= w.npos || (a.target_ctas > 0 && w.split >= w.n_row)) {
     if (a.direct) {
       // an empty row: O = 0, lse = -inf
       for (int e = threadIdx.x; e < w.nh * (VD / 4); e += NT)
-        store_final<VD>(a, pair0 + e / (VD / 4), 4 * (e % (VD / 4)), make_float4(0.f, 0.f, 0.f, 0.f),
-                        0.0f);
-      if (a.lse_out && threadIdx.x < w.nh) a.lse_out[pair0 + threadIdx.x] = kNegInf;
+        store_final<VD>(a, head_slot<MT>(a, w, e / (VD / 4)).pair, 4 * (e % (VD / 4)),
+                        make_float4(0.f, 0.f, 0.f, 0.f), 0.0f);
+      if (a.lse_out && threadIdx.x < w.nh) a.lse_out[head_slot<MT>(a, w, threadIdx.x).pair] = kNegInf;
     } else if (threadIdx.x < w.nh) {
-      ml[(pair0 + threadIdx.x) * S + w.split] = make_float2(kNegInf, 0.0f);
+      ml[head_slot<MT>(a, w, threadIdx.x).pair * S + w.split] = make_float2(kNegInf, 0.0f);
     }
     return false;
   }
@@ -629,7 +666,7 @@ __device__ __forceinline__ int q_channel(int ks, int lj) {
   else return 64 * (ks >> 1) + 16 * lj + 8 * (ks & 1);
 }
 
-template <int NKS, int EB, int D, int QPT, int NT = kThreads>
+template <int NKS, int EB, int D, int QPT, int NT = kThreads, bool MT = false>
 __device__ __forceinline__ void q_issue(const SplitArgs& a, const Work& w, uint4 (&qraw)[QPT],
                                         float4 (&ksc)[QPT][2]) {
 #pragma unroll
@@ -641,7 +678,7 @@ __device__ __forceinline__ void q_issue(const SplitArgs& a, const Work& w, uint4
       const int ks = e >> 6, el = e & 63, eli = el & 15, elj = el >> 4;
       const int d0 = q_channel<EB>(ks, elj);
       if (eli < w.nh)
-        qraw[i] = *reinterpret_cast<const uint4*>(a.query + ((size_t)w.r * a.heads + w.h0 + eli) * D + d0);
+        qraw[i] = *reinterpret_cast<const uint4*>(a.query + head_slot<MT>(a, w, eli).pair * D + d0);
       if (a.k_quant == PKV_QUANT_PER_CHANNEL) {
         const float4* kp = reinterpret_cast<const float4*>(a.k_scale + (size_t)w.g * D + d0);
         ksc[i][0] = kp[0];
@@ -719,7 +756,7 @@ __device__ __forceinline__ float v_scale_of(const SplitArgs& a, const Scales& sc
 // (natural-log units), and the FP32 accumulator is multiplied by the value
 // scale after the W wave states are merged in a fixed order.  `scratch`
 // holds W * (VD + 2) floats of LDS; every thread of the CTA calls this.
-template <int CT, int D, int VD, bool LATENT, bool GATHER, int W, bool EXT>
+template <int CT, int D, int VD, bool LATENT, bool GATHER, int W, bool EXT, bool MT = false>
 __device__ __forceinline__ void exact_partial(const SplitArgs& a, const Work& wk, int p0, int p1,
                                            const Scales& sc, const float* s_vs, float* scratch) {
   constexpr int NT = 64 * W;
@@ -736,7 +773,10 @@ __device__ __forceinline__ void exact_partial(const SplitArgs& a, const Work& wk
   const int32_t* bt_row = a.block_table + (size_t)wk.r * a.max_blocks_per_row;
   const uint8_t* vbase = LATENT ? a.key_cache : a.value_cache;
   for (int hh = 0; hh < wk.nh; ++hh) {
-    const int h = wk.h0 + hh;
+    const HeadSlot hs = head_slot<MT>(a, wk, hh);
+    const int h = hs.h;
+    // (several tokens per row: token j sees len - T + 1 + j positions)
+    const int tlen = MT ? wk.len - (a.qtok - 1 - hs.tok) : wk.len;
     float qf[KD];
 #pragma unroll
     for (int k = 0; k < KD; ++k) {
@@ -744,7 +784,7 @@ __device__ __forceinline__ void exact_partial(const SplitArgs& a, const Work& wk
       qf[k] = 0.0f;
       if (d < D) {
         const float ks = a.k_quant == PKV_QUANT_PER_CHANNEL ? a.k_scale[(size_t)g * D + d] : sc.k_tensor;
-        qf[k] = (float)reinterpret_cast<const half_t*>(a.query)[((size_t)wk.r * a.heads + h) * D + d] * ks;
+        qf[k] = (float)reinterpret_cast<const half_t*>(a.query)[hs.pair * D + d] * ks;
       }
     }
     float m = kNegInf, l = 0.0f;
@@ -754,7 +794,7 @@ __device__ __forceinline__ void exact_partial(const SplitArgs& a, const Work& wk
     for (int pos = p0 + wave; pos < p1; pos += W) {
       int t = wk.base + pos;
       if constexpr (GATHER) t = a.candidates[(size_t)wk.r * a.max_candidates + pos];
-      if (t < wk.lo || t >= wk.len) continue;
+      if (t < wk.lo || t >= tlen) continue;
       const int blk = bt_row[t >> a.log2_block];
       if (blk < 0 || blk >= a.num_pool_blocks) continue;
       const size_t slot = ((size_t)blk << a.log2_block) + (t & (a.block_size - 1));
@@ -804,10 +844,10 @@ __device__ __forceinline__ void exact_partial(const SplitArgs& a, const Work& wk
       f[w] = (mw == kNegInf) ? 0.0f : expf(mw - M);
       L += f[w] * scratch[w * (VD + 2) + VD + 1];
     }
-    const size_t pidx = ((size_t)wk.r * a.heads + h) * S + wk.split;
+    const size_t pidx = hs.pair * S + wk.split;
     if (a.direct) {
       const Final fin = final_of(a, h, M, L);
-      const size_t pair = (size_t)wk.r * a.heads + h;
+      const size_t pair = hs.pair;
       for (int c4 = threadIdx.x; c4 < VD / 4; c4 += NT) {
         float part[4];
 #pragma unroll
@@ -864,7 +904,7 @@ __device__ __forceinline__ float value_bound(const SplitArgs& a, const Scales& s
   return vm * code_bound<CT>();
 }
 
-template <int CT, int D, int VD, bool LATENT, bool GATHER, bool EXT>
+template <int CT, int D, int VD, bool LATENT, bool GATHER, bool EXT, bool MT>
 __global__ void __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(SplitCfg<CT, D, VD, LATENT, GATHER>::MIN_WAVES)))
 split_kernel(const SplitArgs a) {
@@ -892,8 +932,8 @@ split_kernel(const SplitArgs a) {
     raw_npos = GATHER ? uniform_load(a.num_candidates, wk.r) : uniform_load(a.seq_lens, wk.r);
   }
   if constexpr (GATHER) raw_len = uniform_load(a.seq_lens, wk.r);
-  unit_heads(a, wk);
-  const int r = wk.r, g = wk.g, h0 = wk.h0, nh = wk.nh;
+  unit_heads<MT>(a, wk);
+  const int r = wk.r, g = wk.g, nh = wk.nh;
 
   __shared__ uint4 s_q[C::NKS * 64];
   __shared__ float s_err[C::NKS * 64];  // folding error per Q' entry
@@ -907,7 +947,7 @@ split_kernel(const SplitArgs a) {
   // read again below when a sliding window moves the row's first token)
   WaveBlocks wb{bt_row, wk.base + split_p0(a, wk), wave, W, 0, 0};
   if constexpr (!GATHER) wb.load(a, 0, lane);
-  q_issue<C::NKS, C::EB, D>(a, wk, qraw, ksc);
+  q_issue<C::NKS, C::EB, D, QPT, kThreads, MT>(a, wk, qraw, ksc);
   const Scales sc = load_scales<VD>(a, g);
   finish_item<GATHER, EXT>(a, wk, balanced, raw_npos, raw_len);
   const int len = wk.len;
@@ -922,9 +962,13 @@ split_kernel(const SplitArgs a) {
   const int lo = wk.lo;
 
   int p0, p1;
-  if (!split_range<VD>(a, wk, p0, p1)) return;
+  if (!split_range<VD, kThreads, MT>(a, wk, p0, p1)) return;
   const int split = wk.split;
   const int ntiles = (p1 - p0 + 15) >> 4;
+  // several tokens per row: positions of this lane's head slot (its token
+  // sees T - 1 - j fewer than the row's last)
+  int lim = p1;
+  if constexpr (MT) lim = li < nh ? wk.npos - (a.qtok - 1 - head_slot<MT>(a, wk, li).tok) : p1;
 
   // Per-lane byte offsets inside a 16-token tile of one block (dense rows):
   // K: row of token li, 16-byte chunk lj (+64 s);  V: rows of tokens 4 lj + q
@@ -1018,7 +1062,7 @@ split_kernel(const SplitArgs a) {
 
   // Consume tile T: scores, online softmax, PV (lo: with the residual
   // probability tile).
-  auto consume = [&](const Tile<C>& T, auto lo) __attribute__((always_inline)) {
+  auto consume = [&](const Tile<C>& T, int tt, auto lo) __attribute__((always_inline)) {
     constexpr bool LO = decltype(lo)::value;
     // S^T = K Q'^T : lane holds scores of tokens 4 lj + q for head li
     f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
@@ -1046,7 +1090,9 @@ split_kernel(const SplitArgs a) {
     scaled_scores<EXT>(a, sacc, sc);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const bool valid = (T.vmask >> q) & 1u;
+      bool valid = (T.vmask >> q) & 1u;
+      if constexpr (MT) valid = valid && p0 + 16 * tt + 4 * lj + q < lim;
+      else (void)tt;
       sc[q] = valid ? sc[q] : kNegInf;
       smin = fminf(smin, valid ? sc[q] : __builtin_inff());
     }
@@ -1142,7 +1188,7 @@ split_kernel(const SplitArgs a) {
         issue(buf[(st + NST - 1) % NST], tt + (NST - 1) * W);
         // keep the loads ahead of the wait for this tile's data
         __builtin_amdgcn_sched_barrier(0);
-        consume(buf[st], lo);
+        consume(buf[st], tt, lo);
       }
     }
   };
@@ -1183,7 +1229,7 @@ split_kernel(const SplitArgs a) {
     for (int w = 0; w < W; ++w) deep_any |= s_flag[w] != 0;
     const bool armed = deep_any && value_bound<CT, VD>(a, sc, s_vs, lane) * (float)(p1 - p0) >= kTailArm;
     if (s_flag[W] != 0 || (deep_any && armed)) {
-      exact_partial<CT, D, VD, LATENT, GATHER, W, EXT>(a, wk, p0, p1, sc, s_vs, sm_acc);
+      exact_partial<CT, D, VD, LATENT, GATHER, W, EXT, MT>(a, wk, p0, p1, sc, s_vs, sm_acc);
       return;
     }
   }
@@ -1215,11 +1261,12 @@ split_kernel(const SplitArgs a) {
         const float mw = sm_m[w][hh];
         L += ((mw == kNegInf) ? 0.0f : __builtin_amdgcn_exp2f((mw - M) * kLog2e)) * sm_l[w][hh];
       }
-      const size_t pidx = ((size_t)r * a.heads + h0 + hh) * S + split;
-      const size_t pair = (size_t)r * a.heads + h0 + hh;
+      const HeadSlot hs = head_slot<MT>(a, wk, hh);
+      const size_t pidx = hs.pair * S + split;
+      const size_t pair = hs.pair;
       Final fin{0.0f, kNegInf};
       if (a.direct) {
-        fin = final_of(a, h0 + hh, M, L);
+        fin = final_of(a, hs.h, M, L);
         if (a.lse_out && cc == 0) a.lse_out[pair] = fin.lse;
       } else if (cc == 0) {
         reinterpret_cast<float2*>(a.ws_ml)[pidx] = make_float2(M, L);
@@ -1279,7 +1326,7 @@ constexpr int kKvpWavesPerSimd = 2;
 // waves per SIMD (measured better than one tile at three waves per SIMD
 // once the priorities are set).
 
-template <int CT, int D, int VD, bool EXT, int KPC>
+template <int CT, int D, int VD, bool EXT, int KPC, bool MT>
 __global__ void __launch_bounds__(64 * KPC)
 __attribute__((amdgpu_waves_per_eu(kKvpWavesPerSimd)))
 split_kvp_kernel(const SplitArgs a) {
@@ -1296,6 +1343,7 @@ split_kvp_kernel(const SplitArgs a) {
   const int S = a.num_splits;
   const int KVH = a.kv_heads;
   const int group = a.group;
+  const int vgroup = MT ? a.qtok * group : group;  // head slots per KV head
 
   // ---- prologue (as split_kernel, for four KV heads)
   const bool balanced = a.target_ctas > 0;
@@ -1311,10 +1359,9 @@ split_kvp_kernel(const SplitArgs a) {
   wk.g = W * wk.u;
   wk.hb = 0;
   wk.h0 = wk.g * group;
-  wk.nh = W * group;
+  wk.nh = W * vgroup;
   const int r = wk.r;
   const int g = wk.g + wave;     // this wave's KV head
-  const int hw0 = g * group;     // its first query head
 
   __shared__ uint4 s_q[W][C::NKS * 64];
   __shared__ float s_err[W][C::NKS * 64];
@@ -1332,12 +1379,12 @@ split_kvp_kernel(const SplitArgs a) {
     Work w = wk;
     w.g = wk.g + u4;
     w.h0 = w.g * group;
-    w.nh = group;
+    w.nh = vgroup;
     return w;
   };
 #pragma unroll
   for (int u4 = 0; u4 < W; ++u4) {
-    q_issue<C::NKS, C::EB, D, QPT, NT>(a, unit_of(u4), qraw[u4], ksc[u4]);
+    q_issue<C::NKS, C::EB, D, QPT, NT, MT>(a, unit_of(u4), qraw[u4], ksc[u4]);
     sc[u4] = load_scales<VD, NT>(a, wk.g + u4);
   }
   finish_item<false, EXT>(a, wk, balanced, raw_npos, 0);
@@ -1352,9 +1399,13 @@ split_kvp_kernel(const SplitArgs a) {
   (void)len;
 
   int p0, p1;
-  if (!split_range<VD, NT>(a, wk, p0, p1)) return;
+  if (!split_range<VD, NT, MT>(a, wk, p0, p1)) return;
   const int split = wk.split;
   const int ntiles = (p1 - p0 + 15) >> 4;
+  // several tokens per row: positions of this lane's head slot
+  int lim = p1;
+  if constexpr (MT)
+    lim = li < vgroup ? wk.npos - (a.qtok - 1 - head_slot<MT>(a, unit_of(wave), li).tok) : p1;
 
   const uint32_t tok_k = (uint32_t)KVH * C::KROW;
   const uint32_t tok_v = (uint32_t)KVH * C::VROW;
@@ -1405,7 +1456,7 @@ split_kvp_kernel(const SplitArgs a) {
   const uint4* const sq = s_q[wave];
 
   // split_kernel's tile consumer, on this wave's query block
-  auto consume = [&](const Tile<C>& T, auto lo) __attribute__((always_inline)) {
+  auto consume = [&](const Tile<C>& T, int tt, auto lo) __attribute__((always_inline)) {
     constexpr bool LO = decltype(lo)::value;
     f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -1432,7 +1483,9 @@ split_kvp_kernel(const SplitArgs a) {
     scaled_scores<EXT>(a, sacc, x);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const bool valid = (T.vmask >> q) & 1u;
+      bool valid = (T.vmask >> q) & 1u;
+      if constexpr (MT) valid = valid && p0 + 16 * tt + 4 * lj + q < lim;
+      else (void)tt;
       x[q] = valid ? x[q] : kNegInf;
       smin = fminf(smin, valid ? x[q] : __builtin_inff());
     }
@@ -1505,7 +1558,7 @@ split_kvp_kernel(const SplitArgs a) {
     stage_scales<VD, NT>(a, sc[u4], s_vs[u4]);
   }
   __syncthreads();
-  const bool fold = fold_over_budget<CT, C::NKS>(a, s_err[wave], group, lane);
+  const bool fold = fold_over_budget<CT, C::NKS>(a, s_err[wave], vgroup, lane);
 
   auto tile_loop = [&](auto lo) __attribute__((always_inline)) {
     for (int t = 0; t < ntiles; t += NST) {
@@ -1523,7 +1576,7 @@ split_kvp_kernel(const SplitArgs a) {
           else if (pr == 1) __builtin_amdgcn_s_setprio(1);
           else __builtin_amdgcn_s_setprio(0);
         }
-        consume(buf[st], lo);
+        consume(buf[st], tt, lo);
       }
     }
   };
@@ -1555,17 +1608,18 @@ split_kvp_kernel(const SplitArgs a) {
       static_assert(W * (VD + 2) * 4 <= (int)sizeof(s_q), "FP32-path scratch fits the query stage");
 #pragma unroll 1
       for (int u4 = 0; u4 < W; ++u4)
-        exact_partial<CT, D, VD, false, false, W, EXT>(a, unit_of(u4), p0, p1, sc[0], s_vs[u4],
-                                                       reinterpret_cast<float*>(&s_q[0][0]));
+        exact_partial<CT, D, VD, false, false, W, EXT, MT>(a, unit_of(u4), p0, p1, sc[0], s_vs[u4],
+                                                           reinterpret_cast<float*>(&s_q[0][0]));
       return;
     }
   }
 
   // ---- this wave's partials, straight from registers: lane (li, lj) holds
   // channels (4 lj + q) CPL + ct of head li
-  if (li < group) {
-    const int h = hw0 + li;
-    const size_t pair = (size_t)r * a.heads + h;
+  if (li < vgroup) {
+    const HeadSlot hs = head_slot<MT>(a, unit_of(wave), li);
+    const int h = hs.h;
+    const size_t pair = hs.pair;
     const size_t pidx = pair * S + split;
     Final fin{0.0f, kNegInf};
     if (a.direct) {
@@ -2385,50 +2439,60 @@ __global__ void __launch_bounds__(256) combine_small_kernel(const CombineArgs a)
 
 // ---- dispatch ---------------------------------------------------------------
 
-template <int CT, int D, int VD, bool LAT, bool GA, bool EXT>
+template <int CT, int D, int VD, bool LAT, bool GA, bool EXT, bool MT>
 static hipError_t launch_one(const SplitArgs& a, hipStream_t stream) {
   dim3 grid(a.grid_ctas);
-  if constexpr (!LAT && !GA) {
-    if (a.kvp == 4) {
-      hipLaunchKernelGGL((split_kvp_kernel<CT, D, VD, EXT, 4>), grid, dim3(256), 0, stream, a);
-      return hipGetLastError();
+  if constexpr (MT && (LAT || GA)) {
+    return hipErrorInvalidValue;  // several tokens per row: dense rows, separate caches
+  } else {
+    if constexpr (!LAT && !GA) {
+      if (a.kvp == 4) {
+        hipLaunchKernelGGL((split_kvp_kernel<CT, D, VD, EXT, 4, MT>), grid, dim3(256), 0, stream, a);
+        return hipGetLastError();
+      }
+      if (a.kvp == 8) {
+        hipLaunchKernelGGL((split_kvp_kernel<CT, D, VD, EXT, 8, MT>), grid, dim3(512), 0, stream, a);
+        return hipGetLastError();
+      }
     }
-    if (a.kvp == 8) {
-      hipLaunchKernelGGL((split_kvp_kernel<CT, D, VD, EXT, 8>), grid, dim3(512), 0, stream, a);
-      return hipGetLastError();
-    }
+    if constexpr (LAT)
+      hipLaunchKernelGGL((latent_kernel<CT, GA, EXT>), grid, dim3(LatCfg<CT, GA>::NT), 0, stream, a);
+    else
+      hipLaunchKernelGGL((split_kernel<CT, D, VD, LAT, GA, EXT, MT>), grid, dim3(kThreads), 0, stream, a);
+    return hipGetLastError();
   }
-  if constexpr (LAT)
-    hipLaunchKernelGGL((latent_kernel<CT, GA, EXT>), grid, dim3(LatCfg<CT, GA>::NT), 0, stream, a);
-  else
-    hipLaunchKernelGGL((split_kernel<CT, D, VD, LAT, GA, EXT>), grid, dim3(kThreads), 0, stream, a);
-  return hipGetLastError();
 }
 
-template <int CT, int D, int VD, bool LAT, bool GA, bool EXT>
+template <int CT, int D, int VD, bool LAT, bool GA, bool EXT, bool MT>
 static hipError_t occupancy_one(int* n, int kvp) {
-  if constexpr (!LAT && !GA) {
-    if (kvp == 4)
-      return hipOccupancyMaxActiveBlocksPerMultiprocessor(n, split_kvp_kernel<CT, D, VD, EXT, 4>,
-                                                           256, 0);
-    if (kvp == 8)
-      return hipOccupancyMaxActiveBlocksPerMultiprocessor(n, split_kvp_kernel<CT, D, VD, EXT, 8>,
-                                                           512, 0);
+  if constexpr (MT && (LAT || GA)) {
+    return hipErrorInvalidValue;
+  } else {
+    if constexpr (!LAT && !GA) {
+      if (kvp == 4)
+        return hipOccupancyMaxActiveBlocksPerMultiprocessor(n, split_kvp_kernel<CT, D, VD, EXT, 4, MT>,
+                                                             256, 0);
+      if (kvp == 8)
+        return hipOccupancyMaxActiveBlocksPerMultiprocessor(n, split_kvp_kernel<CT, D, VD, EXT, 8, MT>,
+                                                             512, 0);
+    }
+    if constexpr (LAT)
+      return hipOccupancyMaxActiveBlocksPerMultiprocessor(n, latent_kernel<CT, GA, EXT>,
+                                                           LatCfg<CT, GA>::NT, 0);
+    else
+      return hipOccupancyMaxActiveBlocksPerMultiprocessor(n, split_kernel<CT, D, VD, LAT, GA, EXT, MT>,
+                                                           kThreads, 0);
   }
-  if constexpr (LAT)
-    return hipOccupancyMaxActiveBlocksPerMultiprocessor(n, latent_kernel<CT, GA, EXT>,
-                                                         LatCfg<CT, GA>::NT, 0);
-  else
-    return hipOccupancyMaxActiveBlocksPerMultiprocessor(n, split_kernel<CT, D, VD, LAT, GA, EXT>,
-                                                         kThreads, 0);
 }
 
-// Calls F<CT, D, VD, LAT, GA, EXT>(args...) for the compiled variant;
-// returns hipErrorInvalidValue for a variant that is not compiled.
+// Calls F<CT, D, VD, LAT, GA, EXT, MT>(args...) for the compiled variant;
+// returns hipErrorInvalidValue for a variant that is not compiled.  Several
+// query tokens per row (MT) are compiled for dense rows of separate caches.
 #define PKV_FOR_VARIANT(v, CALL)                                                   \
   do {                                                                             \
     const int hs = (v).head_size, vhs = (v).v_head_size;                           \
     const bool lat = (v).latent != 0, ga = (v).gathered != 0, ext = (v).ext != 0;  \
+    const bool mt = (v).mt != 0;                                                   \
     switch ((v).cache_dtype) {                                                     \
       case PKV_F16: PKV_SHAPES(PKV_F16, CALL); break;                              \
       case PKV_I8: PKV_SHAPES(PKV_I8, CALL); break;                                \
@@ -2437,8 +2501,14 @@ static hipError_t occupancy_one(int* n, int kvp) {
     }                                                                              \
   } while (0)
 
+#define PKV_MT(CT, D, VD, LAT, GA, EXT, CALL)                                      \
+  do {                                                                             \
+    if (!mt) { CALL(CT, D, VD, LAT, GA, EXT, false); }                             \
+    else if (!LAT && !GA) { CALL(CT, D, VD, LAT, GA, EXT, true); }                 \
+  } while (0)
+
 #define PKV_EXT(CT, D, VD, LAT, GA, CALL) \
-  do { if (ext) { CALL(CT, D, VD, LAT, GA, true); } else { CALL(CT, D, VD, LAT, GA, false); } } while (0)
+  do { if (ext) { PKV_MT(CT, D, VD, LAT, GA, true, CALL); } else { PKV_MT(CT, D, VD, LAT, GA, false, CALL); } } while (0)
 
 #define PKV_GATHER(CT, D, VD, LAT, CALL) \
   do { if (ga) { PKV_EXT(CT, D, VD, LAT, true, CALL); } else { PKV_EXT(CT, D, VD, LAT, false, CALL); } } while (0)
@@ -2453,7 +2523,7 @@ static hipError_t occupancy_one(int* n, int kvp) {
 
 bool variant_supported(const Variant& v) {
   bool ok = false;
-#define PKV_MARK(CT, D, VD, LAT, GA, EXT) ok = true
+#define PKV_MARK(CT, D, VD, LAT, GA, EXT, MT) ok = true
   PKV_FOR_VARIANT(v, PKV_MARK);
 #undef PKV_MARK
   return ok;
@@ -2461,7 +2531,7 @@ bool variant_supported(const Variant& v) {
 
 hipError_t launch_split(const Variant& v, const SplitArgs& a, hipStream_t stream) {
   hipError_t err = hipErrorInvalidValue;
-#define PKV_LAUNCH(CT, D, VD, LAT, GA, EXT) err = launch_one<CT, D, VD, LAT, GA, EXT>(a, stream)
+#define PKV_LAUNCH(CT, D, VD, LAT, GA, EXT, MT) err = launch_one<CT, D, VD, LAT, GA, EXT, MT>(a, stream)
   PKV_FOR_VARIANT(v, PKV_LAUNCH);
 #undef PKV_LAUNCH
   return err;
@@ -2469,7 +2539,7 @@ hipError_t launch_split(const Variant& v, const SplitArgs& a, hipStream_t stream
 
 hipError_t split_occupancy(const Variant& v, int* ctas_per_cu) {
   hipError_t err = hipErrorInvalidValue;
-#define PKV_OCC(CT, D, VD, LAT, GA, EXT) err = occupancy_one<CT, D, VD, LAT, GA, EXT>(ctas_per_cu, v.kvp)
+#define PKV_OCC(CT, D, VD, LAT, GA, EXT, MT) err = occupancy_one<CT, D, VD, LAT, GA, EXT, MT>(ctas_per_cu, v.kvp)
   PKV_FOR_VARIANT(v, PKV_OCC);
 #undef PKV_OCC
   return err;

@@ -30,9 +30,10 @@ def run_gpu(inp, out_dtype=None, geometry=None, partials_then_combine=False, **g
     g = geometry if geometry is not None else pkv.split_geometry(prob, **geo)
     ws = pkv.workspace_for(g)
     p = inp.problem
+    qrows = p.rows * max(1, p.query_tokens)  # query rows: rows x query tokens per row
     odt = torch.float32 if d.problem_kwargs["out_dtype"] == "f32" else torch.float16
-    out = torch.full((p.rows, p.heads, p.v_head_size), float("nan"), dtype=odt, device="cuda")
-    lse = torch.full((p.rows, p.heads), float("nan"), dtype=torch.float32, device="cuda")
+    out = torch.full((qrows, p.heads, p.v_head_size), float("nan"), dtype=odt, device="cuda")
+    lse = torch.full((qrows, p.heads), float("nan"), dtype=torch.float32, device="cuda")
     if partials_then_combine:
         pkv.paged_decode_partials(prob, g, d.query, d.key_cache, d.value_cache, d.block_table,
                                   d.seq_lens, d.candidates, d.num_candidates, d.k_scale,

@@ -339,3 +339,60 @@ def test_live_balanced_only_when_the_position_total_fits_32_bits():
     fits = pkv.make_problem(1023, 8, 2, 64, 64, 16, (1 << 21) // 16, 10)
     g = pkv.split_geometry(fits, num_cus=256, ctas_per_cu=2, balance=1)
     assert g.target_ctas > 0
+
+
+def test_query_tokens_geometry_and_limits():
+    """Several query tokens per row: the (token, head) pairs of a KV head are
+    taken 16 per head block, the workspace holds a partial per query row, and
+    only dense rows of the separate layout without a sliding window take
+    them."""
+    p = pkv.make_problem(16, 32, 8, 128, 128, 16, 512, 5000, query_tokens=4)
+    g = pkv.split_geometry(p, num_cus=256, ctas_per_cu=2)
+    assert g.head_blocks == 1 and g.kv_heads_per_cta == 4  # 4 tokens x 4 heads = 16
+    assert g.workspace_bytes == 16 * 4 * 32 * g.num_splits * (128 + 2) * 4
+    p8 = pkv.make_problem(16, 32, 8, 128, 128, 16, 512, 5000, query_tokens=8)
+    g8 = pkv.split_geometry(p8, num_cus=256, ctas_per_cu=2)
+    assert g8.head_blocks == 2 and g8.kv_heads_per_cta == 1
+    for kw, st in ((dict(max_candidates=64), 2), (dict(layout="latent", cache_dtype="fp8",
+                                                        k_quant="tensor"), 2),
+                   (dict(sliding_window=32), 2), (dict(query_tokens=17), 2),
+                   (dict(query_tokens=-1), 1)):
+        args = {"query_tokens": 3, **kw}
+        hs, vhs = (576, 512) if kw.get("layout") == "latent" else (128, 128)
+        kvh = 1 if kw.get("layout") == "latent" else 8
+        q = pkv.make_problem(4, 16 if kvh == 1 else 32, kvh, hs, vhs, 16, 32, 500, **args)
+        with pytest.raises(pkv.PkvError) as e:
+            pkv.split_geometry(q, num_cus=256, ctas_per_cu=2)
+        assert e.value.status == st, kw
+
+
+def test_binding_rejects_tensors_smaller_than_the_problem():
+    """The C ABI takes raw pointers; the binding checks every tensor's extent
+    against the problem before calling it (a multi-token output must hold
+    rows x tokens x heads rows), and rejects host tensors."""
+    import torch
+
+    p = pkv.make_problem(4, 8, 2, 64, 64, 16, 4, 32, query_tokens=3)
+    g = pkv.split_geometry(p, num_cus=256, ctas_per_cu=2, splits_override=2, min_chunk=16)
+    class DeviceStub:  # what the check reads of a device tensor
+        is_cuda = True
+
+        def __init__(self, n, size):
+            self.n, self.size = n, size
+
+        def numel(self):
+            return self.n
+
+        def element_size(self):
+            return self.size
+
+        def is_contiguous(self):
+            return True
+
+    pkv._check_extents(p, out=DeviceStub(4 * 3 * 8 * 64, 2), lse_out=DeviceStub(4 * 3 * 8, 4))
+    with pytest.raises(ValueError, match="out holds 4096 bytes; the problem needs 12288"):
+        pkv._check_extents(p, out=DeviceStub(4 * 8 * 64, 2))  # 4 rows, not 4 x 3
+    with pytest.raises(ValueError, match="lse_out"):
+        pkv._check_extents(p, lse_out=DeviceStub(4 * 8, 4))
+    with pytest.raises(ValueError, match="device"):
+        pkv._check_extents(p, query=torch.empty((12, 8, 64), dtype=torch.float16))

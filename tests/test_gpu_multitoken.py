@@ -1,0 +1,78 @@
+"""Several query tokens per row (the multi-token decode of speculative and
+chunked steps; the DSA page's decode tests sweep 1, 3 and 8 query rows of
+one sequence).  The T tokens of a row share its block-table row and attend
+causally (token j: len - T + 1 + j positions); the kernels put the (token,
+head) pairs of a KV head into the 16-wide MFMA columns, so a KV tile is read
+once for all of them.  The oracle evaluates the same step as T * rows
+separate rows (workloads.expand_query_tokens); the tolerance is the usual
+one."""
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from workloads import Problem
+from tests.gpu_util import announce, assert_close_to_oracle, run_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+def _mt(cache, D, heads, kvh, T, seed=50, rows=6, B=16, mbpr=12):
+    quant = "none" if cache == "f16" else ("channel" if seed % 2 else "tensor")
+    cap = mbpr * B
+    lens = [0, 1, T, cap - 3, cap + 40, 77][:rows]
+    p = Problem(rows=rows, heads=heads, kv_heads=kvh, head_size=D, v_head_size=D, block_size=B,
+                max_blocks_per_row=mbpr, num_pool_blocks=0, cache_dtype=cache, k_quant=quant,
+                v_quant=quant, query_tokens=T)
+    return workloads.make_inputs(p, seed + T, lens, with_sink=True, softmax_scale=1.0 / np.sqrt(D))
+
+
+CASES = [("f16", 128, 32, 8, T) for T in (1, 2, 3, 4, 8)] + [
+    ("i8", 256, 24, 2, 3), ("fp8", 64, 64, 8, 2), ("i8", 128, 8, 4, 8), ("fp8", 128, 16, 4, 4)]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "-".join(map(str, c)))
+def test_multitoken_rows_against_the_oracle(case):
+    cache, D, heads, kvh, T = case
+    inp = _mt(cache, D, heads, kvh, T, seed=51 + (1 if cache == "i8" else 0))
+    ref, ref_lse = oracle.paged_decode(workloads.expand_query_tokens(inp))
+    vgroup = T * heads // kvh
+    for S in (1, 5):
+        for kpc in [k for k in (1, 4) if k == 1 or (kvh % k == 0 and vgroup <= 16)]:
+            announce(f"multi-token {case} S={S} kv_heads_per_cta={kpc}")
+            got, lse, g = run_gpu(inp, splits_override=S, min_chunk=16, kv_heads_per_cta=kpc)
+            assert g.head_blocks == -(-vgroup // 16)
+            assert_close_to_oracle(got, lse, ref, ref_lse, what=f"{case} S={S} kpc={kpc}")
+            # a token with nothing to attend (len - T + 1 + j <= 0) is empty
+            empty = np.isneginf(ref_lse)
+            assert np.all(got[empty] == 0)
+
+
+@pytest.mark.parametrize("name", ["C3t4", "C3t8"])
+def test_multitoken_continuous_batching_full_size(name):
+    """C3's 16 sequences with 4 (one MFMA tile of (token, head) pairs per KV
+    head, the four-KV-head kernel) or 8 query tokens (two head blocks) each,
+    default geometry, against the oracle on all their query rows."""
+    inp = workloads.workload(name)
+    ref, ref_lse = oracle.paged_decode(workloads.expand_query_tokens(inp))
+    announce(f"{name} default geometry")
+    got, lse, g = run_gpu(inp)
+    mx, mn = assert_close_to_oracle(got, lse, ref, ref_lse, what=name)
+    announce(f"{name}: S={g.num_splits} kv_heads_per_cta={g.kv_heads_per_cta} "
+             f"head_blocks={g.head_blocks} max_abs={mx:.2e} mean_abs={mn:.2e}")
+
+
+def test_multitoken_fp32_path():
+    """A CTA over budget (large queries: the FP32 path) with several tokens
+    per row evaluates each (token, head) pair with its own length."""
+    inp = _mt("i8", 128, 32, 8, 3, seed=13)
+    inp.query[...] = (inp.query.astype(np.float32) * 200.0).astype(np.float16)
+    ref, ref_lse = oracle.paged_decode(workloads.expand_query_tokens(inp))
+    for kpc in (1, 4):
+        announce(f"multi-token FP32 path kv_heads_per_cta={kpc}")
+        got, lse, _ = run_gpu(inp, splits_override=2, min_chunk=16, out_dtype="f32",
+                              kv_heads_per_cta=kpc)
+        scale = np.abs(ref).max()
+        assert np.abs(got - ref).max() <= 1e-4 * scale
+        fin = np.isfinite(ref_lse)
+        np.testing.assert_allclose(lse[fin], ref_lse[fin], rtol=1e-5, atol=1e-4)

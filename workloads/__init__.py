@@ -74,6 +74,7 @@ class Problem:
     out_dtype: str = "f16"
     sliding_window: int = 0  # > 0: attend to the last sliding_window positions only
     softcap: float = 0.0     # > 0: logits x -> softcap * tanh(x / softcap)
+    query_tokens: int = 1    # query tokens per row (several: causal within the row)
 
     @property
     def group(self) -> int:
@@ -225,8 +226,10 @@ def make_inputs(
     pool = max(p.num_pool_blocks, used + extra)
     p = replace(p, num_pool_blocks=pool)
 
-    # Q
-    query = (rng.standard_normal((R, H, D), dtype=np.float32) * q_std).astype(np.float16)
+    # Q ([rows, T, heads, D] flattened to [rows * T, heads, D] with T query
+    # tokens per row)
+    T = max(1, p.query_tokens)
+    query = (rng.standard_normal((R * T, H, D), dtype=np.float32) * q_std).astype(np.float16)
 
     # K, V (values or codes)
     kshape = (pool, B, KVH, D)
@@ -322,6 +325,26 @@ def make_inputs(
                   num_candidates=ncand, name=name)
 
 
+def expand_query_tokens(inp: Inputs) -> Inputs:
+    """The same step with one query token per row: row r's T tokens become
+    rows r * T + j, each with the row's block-table row and the length its
+    token attends, max(0, len - (T - 1 - j)) with len clamped to capacity.
+    Pure rearrangement of the inputs (no attention arithmetic)."""
+    p = inp.problem
+    T = max(1, p.query_tokens)
+    if T == 1:
+        return inp
+    lens = np.clip(inp.seq_lens.astype(np.int64), 0, p.capacity)
+    j = np.arange(T)
+    tok_lens = np.maximum(0, lens[:, None] - (T - 1 - j)[None, :]).reshape(-1)
+    return Inputs(problem=replace(p, rows=p.rows * T, query_tokens=1), query=inp.query,
+                  key_cache=inp.key_cache, value_cache=inp.value_cache,
+                  block_table=np.repeat(inp.block_table, T, axis=0),
+                  seq_lens=tok_lens.astype(np.int32), softmax_scale=inp.softmax_scale,
+                  k_scale=inp.k_scale, v_scale=inp.v_scale, head_sink=inp.head_sink,
+                  name=(inp.name + ", as separate rows") if inp.name else "", meta=dict(inp.meta))
+
+
 def sorted_subsets(rng: np.random.Generator, rows: int, universe: int, k: int) -> np.ndarray:
     """Per row, a sorted random subset of [0, universe) of size k."""
     out = np.empty((rows, k), dtype=np.int32)
@@ -360,6 +383,19 @@ def c3(seed: int = 3) -> Inputs:
                 max_blocks_per_row=512, num_pool_blocks=0, cache_dtype="f16")
     return make_inputs(p, seed, lens, softmax_scale=1.0 / np.sqrt(128.0), with_sink=True,
                        name="C3 continuous batching FP16: 16 rows, lengths U[512,8192], 32q/8kv, head 128, block 16, head sink")
+
+
+def c3_tokens(T: int, seed: int = 3) -> Inputs:
+    """C3 with T query tokens per sequence (a speculative / multi-token decode
+    step): the same 16 sequences, lengths (now counting the T new tokens),
+    heads and cache; token j of a sequence attends len - T + 1 + j positions."""
+    rng = np.random.default_rng(seed + 1000)
+    lens = rng.integers(512, 8192, size=16, endpoint=True)
+    p = Problem(rows=16, heads=32, kv_heads=8, head_size=128, v_head_size=128, block_size=16,
+                max_blocks_per_row=512, num_pool_blocks=0, cache_dtype="f16", query_tokens=T)
+    return make_inputs(p, seed, lens, softmax_scale=1.0 / np.sqrt(128.0), with_sink=True,
+                       name=f"C3 with {T} query tokens per sequence: 16 sequences, lengths "
+                            f"U[512,8192], 32q/8kv, head 128, block 16, head sink")
 
 
 def c4(seed: int = 4) -> Inputs:
@@ -419,6 +455,9 @@ WORKLOADS = {"C1": c1, "C2": c2, "C3": c3, "C4": c4, "C5": c5,
              **{f"X{c}b{b}{d}": (lambda seed=7, c=c, b=b, d=d: paged_quantized(c, b, d, seed))
                 for c, b in ((1024, 32), (4096, 8), (4096, 32), (16384, 8), (16384, 32))
                 for d in ("i8", "fp8")},
+             "C3t4": lambda seed=3: c3_tokens(4, seed),
+             "C3t4rows": lambda seed=3: expand_query_tokens(c3_tokens(4, seed)),
+             "C3t8": lambda seed=3: c3_tokens(8, seed),
              "P128": lambda seed=6: dsa_prefill(128, seed=seed),
              "P2048": lambda seed=6: dsa_prefill(2048, seed=seed),
              "P8192": lambda seed=6: dsa_prefill(8192, seed=seed)}

@@ -33,7 +33,8 @@ def problem_kwargs(p, out_dtype: Optional[str] = None) -> dict:
                 max_candidates=p.max_candidates, cache_dtype=p.cache_dtype,
                 out_dtype=out_dtype or p.out_dtype, k_quant=p.k_quant,
                 v_quant="none" if p.layout == "latent" else p.v_quant, layout=p.layout,
-                sliding_window=p.sliding_window, softcap=p.softcap)
+                sliding_window=p.sliding_window, softcap=p.softcap,
+                query_tokens=p.query_tokens)
 
 
 def _t(a, device):
