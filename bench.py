@@ -253,7 +253,8 @@ PMC_SQ = ("SQ_WAVES SQ_WAVE_CYCLES SQ_BUSY_CYCLES SQ_LEVEL_WAVES SQ_ACTIVE_INST_
 def _pmc_commands(w: str, tag: str) -> list:
     """The rocprofv3 runs a counter summary is made from ($R = repository
     root); they run committed files only."""
-    run = f"python3 $R/bench.py --workload {w} --eager --steps 20 --warmup 2 --no-cpu-baseline"
+    run = (f"python3 $R/bench.py --workload {w} --also= --rounds 3 --eager --steps 20 --warmup 2 "
+           "--no-cpu-baseline")
     cmds = []
     for name, pmc in (("FETCH_SIZE", "FETCH_SIZE"), ("WRITE_SIZE", "WRITE_SIZE"), ("SQ", PMC_SQ)):
         cmds.append(f"cd /tmp && export TMPDIR=/tmp && timeout -s KILL 90 rocprofv3 --pmc {pmc} "
@@ -403,7 +404,7 @@ def summarize_trace(tag_dir: str, w: str, bench_log: str = "") -> str:
              "# command ($R = repository root):",
              f"#   cd /tmp && export TMPDIR=/tmp && timeout -k 10 300 rocprofv3 --kernel-trace --stats "
              f"--output-format csv -d $R/gpurun_out/{tag}/kt_{w} -o kt -- python3 $R/bench.py "
-             f"--workload {w} --no-cpu-baseline",
+             f"--workload {w} --also= --no-cpu-baseline",
              "# summary: python3 $R/bench.py --summarize-trace $R/gpurun_out/" + tag + f" --workload {w}",
              f"kernel_source_sha256_16: {kernel_source_hash()}",
              f"{'kernel':<72} {'calls':>6} {'avg_ns':>10} {'min_ns':>8} {'max_ns':>8}"]
@@ -414,7 +415,7 @@ def summarize_trace(tag_dir: str, w: str, bench_log: str = "") -> str:
                      f"{float(row['MinNs']):>8.0f} {float(row['MaxNs']):>8.0f}")
     if bench_log and os.path.exists(bench_log):
         for l in open(bench_log):
-            if "] step" in l:
+            if "] step" in l or ": step " in l:
                 lines.append("# bench.py's own line in the traced run: " + l.strip())
     return "\n".join(lines) + "\n"
 

@@ -529,6 +529,20 @@ def test_prefill_shape_sampled_rows():
     announce(f"P128: S={g.num_splits}")
 
 
+def test_prefill_whole_step_2048_rows():
+    """The dynamic-sparse prefill shape with 2048 rows (each its own 2048
+    sorted candidates of an 8192-token sequence, INT8 per channel; the DSA
+    page's prefill table) at the default geometry, every row against the
+    oracle."""
+    inp = workloads.workload("P2048")
+    announce("P2048 prefill shape: the oracle on all 2048 rows (host cores, ~30 s)")
+    ref, ref_lse = oracle.paged_decode(inp)
+    announce("P2048 prefill shape, whole step")
+    got, lse, g = run_gpu(inp)
+    mx, mn = assert_close_to_oracle(got, lse, ref, ref_lse, what="P2048")
+    announce(f"P2048: S={g.num_splits} max_abs={mx:.2e} mean_abs={mn:.2e}")
+
+
 @pytest.mark.parametrize("name", ["X4096b8i8", "X1024b32fp8"])
 @pytest.mark.parametrize("S", [0, 12, 16])
 def test_paged_page_shapes(name, S):
