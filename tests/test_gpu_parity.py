@@ -272,7 +272,7 @@ def test_hip_graph_replay_matches_eager_with_new_lengths():
         assert torch.equal(o_graph, out) and torch.equal(l_graph, lse)
         # and the replay is right, not just repeatable
         ref_inp = Inputs(**{**inp.__dict__, "seq_lens": np.array(lens, dtype=np.int32)})
-        ref, ref_lse = oracle.paged_decode(ref_inp)
+        ref, ref_lse = oracle.paged_decode(workloads.expand_query_tokens(ref_inp))
         assert_close_to_oracle(o_graph.double().cpu().numpy(), l_graph.double().cpu().numpy(),
                                ref, ref_lse, what=f"replay {lens}")
 
@@ -291,8 +291,9 @@ def _replay_with_lengths(inp, lens_list, what, **geo):
     g = pkv.split_geometry(prob, **geo)
     ws = pkv.workspace_for(g)
     p = inp.problem
-    out = torch.zeros((p.rows, p.heads, p.v_head_size), dtype=torch.float16, device="cuda")
-    lse = torch.zeros((p.rows, p.heads), dtype=torch.float32, device="cuda")
+    qrows = p.rows * max(1, p.query_tokens)
+    out = torch.zeros((qrows, p.heads, p.v_head_size), dtype=torch.float16, device="cuda")
+    lse = torch.zeros((qrows, p.heads), dtype=torch.float32, device="cuda")
 
     def step():
         pkv.paged_decode_attention(prob, g, d.query, d.key_cache, d.value_cache, d.block_table,
@@ -324,7 +325,7 @@ def _replay_with_lengths(inp, lens_list, what, **geo):
         torch.cuda.synchronize()
         assert torch.equal(o_graph, out) and torch.equal(l_graph, lse)
         ref_inp = Inputs(**{**inp.__dict__, "seq_lens": np.array(lens, dtype=np.int32)})
-        ref, ref_lse = oracle.paged_decode(ref_inp)
+        ref, ref_lse = oracle.paged_decode(workloads.expand_query_tokens(ref_inp))
         assert_close_to_oracle(o_graph.double().cpu().numpy(), l_graph.double().cpu().numpy(),
                                ref, ref_lse, what=f"{what} replay {list(lens)}")
     return g
@@ -354,6 +355,20 @@ def test_graph_replay_continuous_batching_shape(kpc):
     geo = {"kv_heads_per_cta": kpc} if kpc else {}
     g = _replay_with_lengths(inp, _replay_lens(16, cap, 31), f"C3 shape kpc={kpc}", **geo)
     assert g.target_ctas > 0 and g.kv_heads_per_cta == (kpc or 4) and g.num_splits > 1
+
+
+@pytest.mark.parametrize("T", [4, 8])
+def test_graph_replay_multitoken_shape(T):
+    """C3's shape with T query tokens per row (four: the four-KV-head kernel,
+    one (token, head) tile per KV head; eight: two head blocks), replayed
+    with changing lengths, including rows shorter than T."""
+    cap = 256
+    p = Problem(rows=16, heads=32, kv_heads=8, head_size=128, v_head_size=128, block_size=16,
+                max_blocks_per_row=cap // 16, num_pool_blocks=0, cache_dtype="f16",
+                query_tokens=T)
+    inp = workloads.make_inputs(p, 33, cap, with_sink=True, softmax_scale=1 / np.sqrt(128))
+    g = _replay_with_lengths(inp, _replay_lens(16, cap, 33), f"C3 shape, {T} tokens per row")
+    assert g.target_ctas > 0 and g.head_blocks == T // 4
 
 
 def test_graph_replay_latent_shape():
