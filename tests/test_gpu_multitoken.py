@@ -76,3 +76,21 @@ def test_multitoken_fp32_path():
         assert np.abs(got - ref).max() <= 1e-4 * scale
         fin = np.isfinite(ref_lse)
         np.testing.assert_allclose(lse[fin], ref_lse[fin], rtol=1e-5, atol=1e-4)
+
+
+@pytest.mark.parametrize("T,kpc", [(3, 4), (8, 1)])
+def test_multitoken_with_softcap(T, kpc):
+    """The soft cap (the kernels' EXT instantiation) with several tokens per
+    row: the cap applies to every (token, head) pair's scaled logits."""
+    from dataclasses import replace
+    inp = _mt("fp8", 128, 32, 8, T, seed=61)
+    inp = workloads.Inputs(**{**inp.__dict__, "problem": replace(inp.problem, softcap=2.5)})
+    inp.query[...] = (inp.query.astype(np.float32) * 3.0).astype(np.float16)  # so the cap binds
+    ref, ref_lse = oracle.paged_decode(workloads.expand_query_tokens(inp))
+    uncapped, _ = oracle.paged_decode(workloads.expand_query_tokens(
+        workloads.Inputs(**{**inp.__dict__, "problem": replace(inp.problem, softcap=0.0)})))
+    assert np.abs(ref - uncapped).max() > 1e-2  # the cap changes the result
+    for S in (1, 4):
+        announce(f"multi-token softcap T={T} S={S} kv_heads_per_cta={kpc}")
+        got, lse, _ = run_gpu(inp, splits_override=S, min_chunk=16, kv_heads_per_cta=kpc)
+        assert_close_to_oracle(got, lse, ref, ref_lse, what=f"softcap T={T} S={S}")
