@@ -120,6 +120,10 @@ pkv_status check_problem(const pkv_problem* p) {
   }
   if ((int64_t)p->num_rows * qtok_of(*p) * p->num_heads > INT32_MAX)
     return fail(PKV_EUNSUPPORTED, "num_rows * query_tokens * num_heads is too large");
+  // one row's query block is addressed through a buffer descriptor whose
+  // range must stay below the past-the-range offset the kernels use
+  if ((int64_t)qtok_of(*p) * p->num_heads * p->head_size * 2 >= (int64_t)1 << 30)
+    return fail(PKV_EUNSUPPORTED, "query_tokens * num_heads * head_size * 2 bytes reach 2^30");
   if ((int64_t)p->num_rows * p->num_kv_heads * ceil_div(vgroup_of(*p), 16) * 64 >
       INT32_MAX)
     return fail(PKV_EUNSUPPORTED, "num_rows * num_kv_heads * ceil(group / 16) is too large");

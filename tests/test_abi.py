@@ -341,6 +341,21 @@ def test_live_balanced_only_when_the_position_total_fits_32_bits():
     assert g.target_ctas > 0
 
 
+def test_query_block_beyond_2p30_bytes_is_rejected():
+    """A row's query block (query_tokens x num_heads x head_size FP16) is read
+    through one buffer descriptor, whose range must stay below 2^30 bytes."""
+    ok = pkv.make_problem(1, (1 << 21) - 8, 8, 256, 256, 16, 4, 10)  # 2^30 - 4 KiB
+    pkv.split_geometry(ok, num_cus=256, ctas_per_cu=2)
+    bad = pkv.make_problem(1, 1 << 21, 8, 256, 256, 16, 4, 10)        # 2^30 bytes
+    with pytest.raises(pkv.PkvError) as e:
+        pkv.split_geometry(bad, num_cus=256, ctas_per_cu=2)
+    assert e.value.status == 2 and "2^30" in str(e.value)
+    bad_t = pkv.make_problem(1, 1 << 17, 8, 256, 256, 16, 4, 10, query_tokens=16)
+    with pytest.raises(pkv.PkvError) as e:
+        pkv.split_geometry(bad_t, num_cus=256, ctas_per_cu=2)
+    assert e.value.status == 2
+
+
 def test_query_tokens_geometry_and_limits():
     """Several query tokens per row: the (token, head) pairs of a KV head are
     taken 16 per head block, the workspace holds a partial per query row, and
