@@ -2270,13 +2270,19 @@ latent_kernel(const SplitArgs a) {
 // loads at once, and the per-thread sums are added across the split subsets
 // in a fixed order through LDS, so the result does not depend on timing.
 
-constexpr int kCombineThreads = 512;
+// Threads per CTA: 128 for 64 channels (8 split subsets of the 16 float4
+// channel groups), 512 for larger heads.  Measured on MI355X: 512 threads at
+// 64 channels -- 32 subsets of two splits each and a 32-way reduction --
+// made the combine of the PagedAttention 16384-token x 32-row shape 8.4 us
+// slower; 256 or 1024 threads at 128 channels were no better.
+template <int VD>
+constexpr int combine_threads() { return VD == 64 ? 128 : 512; }
 
 template <int VD, bool OUT_F32>
-__global__ void __launch_bounds__(kCombineThreads)
+__global__ void __launch_bounds__(combine_threads<VD>())
 combine_kernel(const CombineArgs a) {
   constexpr int CG = VD / 4;                  // float4 channel groups
-  constexpr int KS = kCombineThreads / CG;    // split subsets
+  constexpr int KS = combine_threads<VD>() / CG;  // split subsets
   constexpr int MAXI = (kMaxSplits + KS - 1) / KS;
   const int pair = blockIdx.x;
   const int t = threadIdx.x;
@@ -2587,7 +2593,7 @@ static hipError_t launch_combine_t(const CombineArgs& a, hipStream_t stream) {
   else if (a.num_splits <= 16 && VD <= 256 && pairs >= 512)
     hipLaunchKernelGGL((combine_small_kernel<VD, F32, 16, PARTS>), dim3(ctas), dim3(256), 0, stream, a);
   else
-    hipLaunchKernelGGL((combine_kernel<VD, F32>), dim3(pairs), dim3(kCombineThreads), 0, stream, a);
+    hipLaunchKernelGGL((combine_kernel<VD, F32>), dim3(pairs), dim3(combine_threads<VD>()), 0, stream, a);
   return hipGetLastError();
 }
 
