@@ -368,15 +368,16 @@ __device__ __forceinline__ void scaled_scores(const SplitArgs& a, const f32x4& a
 // (row, unit, split) are numbered row by row, so consecutive CTAs -- which
 // the hardware spreads round-robin over the XCDs -- carry equal work and no
 // CTA launches only to find nothing to do (except trailing padding).  All
-// row lengths are read in one round trip (lane i holds rows i + 64 k; the
-// loads are issued unconditionally, from clamped indices).
-template <bool GATHER, bool EXT>
-__device__ __forceinline__ bool locate_balanced(const SplitArgs& a, int lane, Work& w) {
+// row lengths are read in one round trip (lane i holds rows i + 64 k,
+// k < NR; the loads are issued unconditionally, from clamped indices).
+// locate_balanced takes NR = 1 for up to 64 rows, the common decode batch
+// (C3-shaped steps 0.4 us faster than reading NR = 16 lengths per lane).
+template <bool GATHER, bool EXT, int NR>
+__device__ __forceinline__ bool locate_rows(const SplitArgs& a, int lane, Work& w) {
   const int S = a.num_splits;
   const int units_row = a.units_row;
   const int cap = a.max_blocks_per_row * a.block_size;
   const int c = blockIdx.x;
-  constexpr int NR = kMaxBalancedRows / 64;
   int raw[NR];
 #pragma unroll
   for (int i = 0; i < NR; ++i) {
@@ -452,6 +453,12 @@ __device__ __forceinline__ bool locate_balanced(const SplitArgs& a, int lane, Wo
   w.lo = GATHER ? 0 : window_lo<EXT>(a, w.len);
   w.base = GATHER ? 0 : (w.lo & ~15);
   return true;
+}
+
+template <bool GATHER, bool EXT>
+__device__ __forceinline__ bool locate_balanced(const SplitArgs& a, int lane, Work& w) {
+  if (a.rows <= 64) return locate_rows<GATHER, EXT, 1>(a, lane, w);
+  return locate_rows<GATHER, EXT, kMaxBalancedRows / 64>(a, lane, w);
 }
 
 // Static mode (target_ctas == 0): CTA c is item c of the (row, unit,

@@ -357,6 +357,26 @@ def test_graph_replay_continuous_batching_shape(kpc):
     assert g.target_ctas > 0 and g.kv_heads_per_cta == (kpc or 4) and g.num_splits > 1
 
 
+@pytest.mark.parametrize("rows,kpc", [(63, 0), (64, 4), (65, 0), (65, 4), (200, 4), (1024, 4)])
+def test_live_balanced_row_counts(rows, kpc):
+    """The live-balanced decomposition reads one length per lane up to 64
+    rows and 64-row groups beyond: row counts on both sides of 64 and up to
+    its limit of 1024, lengths from 0 to the capacity, against the oracle on
+    every row (per-KV-head kernel and four KV heads per CTA)."""
+    cap = 128
+    rng = np.random.default_rng(rows)
+    lens = rng.integers(0, cap, size=rows, endpoint=True)
+    lens[:3] = [0, cap, 1]
+    p = Problem(rows=rows, heads=8, kv_heads=4, head_size=64, v_head_size=64, block_size=16,
+                max_blocks_per_row=cap // 16, num_pool_blocks=0, cache_dtype="f16")
+    inp = workloads.make_inputs(p, 40 + rows, lens, with_sink=True, softmax_scale=0.125)
+    ref, ref_lse = oracle.paged_decode(inp)
+    announce(f"live-balanced, {rows} rows, kv_heads_per_cta={kpc or 1}")
+    got, lse, g = run_gpu(inp, balance=1, min_chunk=16, kv_heads_per_cta=kpc or 1)
+    assert g.target_ctas > 0 and g.num_splits > 1
+    assert_close_to_oracle(got, lse, ref, ref_lse, what=f"{rows} rows")
+
+
 @pytest.mark.parametrize("T", [4, 8])
 def test_graph_replay_multitoken_shape(T):
     """C3's shape with T query tokens per row (four: the four-KV-head kernel,
