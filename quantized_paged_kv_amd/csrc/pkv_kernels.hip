@@ -673,15 +673,16 @@ __device__ __forceinline__ int q_channel(int ks, int lj) {
   else return 64 * (ks >> 1) + 16 * lj + 8 * (ks & 1);
 }
 
-// FIXED: every thread issues exactly QPT query loads whatever its head slot
-// (a slot past the unit's heads, or an entry past the stage, reads past the
-// descriptor of the row's query block, which returns zeros without a memory
-// request).  With a load count that does not depend on the path, the
+// With FIXED every thread issues exactly QPT query loads whatever its head
+// slot (a slot past the unit's heads, or an entry past the stage, reads past
+// the descriptor of the row's query block, which returns zeros without a
+// memory request).  With a load count that does not depend on the path, the
 // compiler's wait for the block ids before the first K tile counts these
 // loads and does not wait for them (C3-shaped steps 1.6 % faster).  The
-// latent kernel issues its K tiles as direct-to-LDS loads, which the
-// compiler does not count, so there the query must land before they go out
-// (FIXED = false: its Q' stage would otherwise wait for a round of K).
+// latent kernel keeps FIXED = false: on one-byte dense rows it issues its K
+// tiles as direct-to-LDS loads, which the compiler does not count, so the
+// query must land before they go out (its Q' stage would otherwise wait for
+// a whole round of K, measured 1.3 us slower on C5).
 template <int NKS, int EB, int D, int QPT, int NT = kThreads, bool MT = false, bool FIXED = true>
 __device__ __forceinline__ void q_issue(const SplitArgs& a, const Work& w, uint4 (&qraw)[QPT],
                                         float4 (&ksc)[QPT][2]) {
