@@ -123,7 +123,9 @@ typedef enum { PKV_SEPARATE = 0, PKV_LATENT = 1 } pkv_layout;
  * SEPARATE and (576,512) for LATENT; block_size a power of two >= 16;
  * cache_dtype F16 (any quant), I8 or FP8_E4M3FN (quant PER_TENSOR or
  * PER_CHANNEL); out_dtype F16 or F32; num_heads a multiple of num_kv_heads;
- * capacity max_blocks_per_row * block_size and max_candidates at most 2^30. */
+ * capacity max_blocks_per_row * block_size and max_candidates at most 2^30;
+ * one row's query block, query_tokens * num_heads * head_size FP16 values,
+ * under 2^30 bytes (PKV_EUNSUPPORTED otherwise). */
 typedef struct {
   int32_t num_rows;
   int32_t num_heads;
@@ -155,9 +157,10 @@ typedef struct {
   int32_t balance;          /* 0: auto (live-balanced for 16..1024 rows), 1: live-
                                balanced (up to 1024 rows), 2: static; rows whose
                                positions could sum to 2^31 always use static */
-  int32_t kv_heads_per_cta; /* 0: auto (4 when allowed, else 1); 1; 4: one CTA takes four
-                               neighbouring KV heads, one per wave (dense rows, SEPARATE
-                               layout, num_kv_heads a multiple of 4, group <= 16) */
+  int32_t kv_heads_per_cta; /* 0: auto (4 when allowed, else 1); 1; 4 or 8: one CTA takes
+                               that many neighbouring KV heads, one per wave (dense rows,
+                               SEPARATE layout, num_kv_heads a multiple of it, at most 16
+                               (token, head) slots per KV head) */
 } pkv_geometry_opts;
 
 /* Launch geometry; produced by split_geometry, consumed unchanged. */
