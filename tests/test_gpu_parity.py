@@ -377,6 +377,36 @@ def test_live_balanced_row_counts(rows, kpc):
     assert_close_to_oracle(got, lse, ref, ref_lse, what=f"{rows} rows")
 
 
+@pytest.mark.parametrize("cache,heads,kvh,D,VD,lay", [
+    ("f16", 64, 8, 64, 64, "separate"), ("f16", 32, 8, 128, 128, "separate"),
+    ("i8", 24, 2, 256, 256, "separate"), ("fp8", 16, 1, 576, 512, "latent")])
+@pytest.mark.parametrize("out_dtype", ["f16", "f32"])
+def test_combine_many_live_balanced_splits(cache, heads, kvh, D, VD, lay, out_dtype):
+    """The CTA-per-pair combine with more splits than it reads speculatively
+    (rows of up to 64 live-balanced splits, where the slots past 16 are read
+    only when their weight is nonzero), for every value-head size, against
+    the oracle; paged_decode_attention equals partials + split_combine."""
+    cap = 1024
+    rows = 32
+    rng = np.random.default_rng(D + heads)
+    lens = rng.integers(0, cap, size=rows, endpoint=True)
+    lens[:4] = [cap, 0, 1, cap - 17]
+    quant = "none" if cache == "f16" else "tensor"
+    p = Problem(rows=rows, heads=heads, kv_heads=kvh, head_size=D, v_head_size=VD, block_size=16,
+                max_blocks_per_row=cap // 16, num_pool_blocks=0, cache_dtype=cache,
+                k_quant=quant, v_quant=quant, layout=lay)
+    inp = workloads.make_inputs(p, 50 + D, lens, with_sink=True, softmax_scale=1.0 / np.sqrt(D))
+    ref, ref_lse = oracle.paged_decode(inp)
+    announce(f"combine, {cache} {VD} channels, {out_dtype} output, up to 64 live-balanced splits")
+    geo = dict(num_cus=256, ctas_per_cu=8, balance=1, splits_override=64, min_chunk=16)
+    got, lse, g = run_gpu(inp, out_dtype=out_dtype, **geo)
+    assert g.target_ctas > 0 and g.num_splits == 64
+    tol = dict(max_abs=1e-3, mean_abs=1e-4) if out_dtype == "f32" else {}
+    assert_close_to_oracle(got, lse, ref, ref_lse, what=f"{VD} channels {out_dtype}", **tol)
+    b, lb, _ = run_gpu(inp, out_dtype=out_dtype, geometry=g, partials_then_combine=True)
+    assert np.array_equal(got, b) and np.array_equal(lse, lb)
+
+
 @pytest.mark.parametrize("T", [4, 8])
 def test_graph_replay_multitoken_shape(T):
     """C3's shape with T query tokens per row (four: the four-KV-head kernel,
