@@ -1360,9 +1360,10 @@ constexpr int kKvpWavesPerSimd = 2;
 // reading with little in flight.  So every wave runs its prologue at the
 // highest priority and then lowers its priority as its remaining work
 // shrinks (3, 2, 1, 0 for the quarters of its tiles): the CTAs of a CU
-// progress together and finish together.  Two tiles stay in flight per wave, two
-// waves per SIMD (measured better than one tile at three waves per SIMD
-// once the priorities are set).
+// progress together and finish together.  Two tiles stay in flight per wave
+// for head-128 FP16 tiles, at two waves per SIMD (measured better than one
+// tile at three waves per SIMD once the priorities are set), one for smaller
+// tiles (see NST).
 
 template <int CT, int D, int VD, bool EXT, int KPC, bool MT>
 __global__ void __launch_bounds__(64 * KPC)
@@ -1372,7 +1373,12 @@ split_kvp_kernel(const SplitArgs a) {
   using C = SplitCfg<CT, D, VD, false, false>;
   constexpr int W = KPC;       // KV heads per CTA, one per wave
   constexpr int NT = 64 * W;   // threads per CTA
-  constexpr int NST = 3;       // tiles held per wave: one consumed, two in flight
+  // tiles held per wave: one consumed, two in flight -- or one for tiles of
+  // at most 16 registers (one-byte codes up to head 128, FP16 head 64), where
+  // the registers saved raise the CTAs per CU (measured on MI355X: the
+  // PagedAttention 16384-token x 32-row shapes 5 % faster, C3 with head 64
+  // 2 %, the rest unchanged; one tile in flight for head-128 FP16 was slower)
+  constexpr int NST = C::TILE_REGS <= 16 ? 2 : 3;
   static_assert(C::CPL % 4 == 0, "float4 groups of channels per lane");
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
