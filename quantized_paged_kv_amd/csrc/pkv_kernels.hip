@@ -2285,12 +2285,14 @@ latent_kernel(const SplitArgs a) {
 // in a fixed order through LDS, so the result does not depend on timing.
 
 // Threads per CTA: 128 for 64 channels (8 split subsets of the 16 float4
-// channel groups), 512 for larger heads.  Measured on MI355X: 512 threads at
-// 64 channels -- 32 subsets of two splits each and a 32-way reduction --
-// made the combine of the PagedAttention 16384-token x 32-row shape 8.4 us
-// slower; 256 or 1024 threads at 128 channels were no better.
+// channel groups), 512 for 128 and 512 channels, 1024 for 256 (16 subsets).
+// Measured on MI355X: 512 threads at 64 channels -- 32 subsets of two
+// splits each and a 32-way reduction -- made the combine of the
+// PagedAttention 16384-token x 32-row shape 8.4 us slower; 256 or 1024
+// threads at 128 channels were no better; at 256 channels 1024 threads took
+// 0.35 us off the single-row INT8 step and 256 added 0.6.
 template <int VD>
-constexpr int combine_threads() { return VD == 64 ? 128 : 512; }
+constexpr int combine_threads() { return VD == 64 ? 128 : (VD == 256 ? 1024 : 512); }
 
 template <int VD, bool OUT_F32>
 __global__ void __launch_bounds__(combine_threads<VD>())
