@@ -476,8 +476,8 @@ def main():
         sys.stdout.write(summarize_trace(args.summarize_trace, args.workload, args.trace_log))
         return 0
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this build has "
-              "no multi-GPU path. Run with --gpus 1.", file=sys.stderr)
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the library "
+              "has no multi-GPU path. Run with --gpus 1.", file=sys.stderr)
         return 2
 
     import numpy as np
