@@ -160,7 +160,8 @@ typedef struct {
   int32_t kv_heads_per_cta; /* 0: auto (4 when allowed, else 1); 1; 4 or 8: one CTA takes
                                that many neighbouring KV heads, one per wave (dense rows,
                                SEPARATE layout, num_kv_heads a multiple of it, at most 16
-                               (token, head) slots per KV head) */
+                               (token, head) slots per KV head; with 4, up to 32 slots at
+                               head sizes up to 128, each wave taking both 16-slot blocks) */
 } pkv_geometry_opts;
 
 /* Launch geometry; produced by split_geometry, consumed unchanged. */
@@ -168,22 +169,26 @@ typedef struct {
   int32_t num_splits;       /* S: CTAs per (row, KV head, head block) */
   int32_t min_chunk;        /* positions per active split are >= this */
   int32_t threads;          /* threads per CTA of the split kernel */
-  int32_t head_blocks;      /* ceil(group / 16): query heads go 16 per CTA */
+  int32_t head_blocks;      /* ceil(query_tokens * group / 16): (token, head) slots go 16
+                               per MFMA column tile */
   int32_t grid_x, grid_y, grid_z;  /* split-kernel grid (1-D: grid_y = grid_z = 1) */
   int32_t target_ctas;      /* active CTAs the live chunk size aims at (0: per-row rule) */
-  int32_t kv_heads_per_cta; /* 1, or 4 (the four-KV-head CTAs of split_geometry's opts) */
+  int32_t kv_heads_per_cta; /* 1, 4 or 8 (the several-KV-head CTAs of split_geometry's opts) */
   uint64_t workspace_bytes; /* bytes of workspace the calls below need */
 } pkv_geometry;
 
 /*
  * split_geometry -- choose the split count S from static shapes only.
  *
- * units = num_rows * (num_kv_heads / kv_heads_per_cta) * ceil(group / 16), where
+ * units = num_rows * num_kv_heads * ceil(slots / 16) with one KV head per CTA,
+ *         num_rows * (num_kv_heads / kv_heads_per_cta) with several (slots =
+ *         query_tokens * group, the (token, head) slots of a KV head);
  *         kv_heads_per_cta is 4 when the problem allows it (dense rows, SEPARATE
- *         layout, a multiple of four KV heads, group <= 16: the cache keeps
- *         the KV heads of a token side by side, and a CTA whose four waves
- *         read four neighbouring heads of the same records streams faster
- *         than four CTAs reading one head each) and opts do not ask for 1;
+ *         layout, a multiple of four KV heads, head size <= 128, slots <= 16 --
+ *         or slots <= 32 with an FP16 cache: the cache keeps the KV heads of a
+ *         token side by side, and a CTA whose four waves read four
+ *         neighbouring heads of the same records streams faster than four CTAs
+ *         reading one head each) and opts do not ask for 1;
  * cap   = max_blocks_per_row * block_size (dense; with a sliding window W
  *         at most W + 15, the positions from the window start rounded down
  *         to a multiple of 16) or max_candidates (gathered);
@@ -224,7 +229,10 @@ typedef struct {
  * shorter splits.  P and the KV bytes are those of a work unit (four KV
  * heads in the four-head mode).  waves: 2 in the live-balanced mode with
  * one KV head per CTA when 2 P is less than the KV bytes of min_chunk
- * positions, else 1.
+ * positions, else 1.  With 17-32 slots per KV head in the four-head mode:
+ * ctas_per_cu defaults to 1, min_chunk to the quarter rule alone, and in the
+ * live-balanced mode target = resident - units when units <= resident / 2
+ * (so that the rounded per-row split counts fit one round).
  * Returns PKV_EINVAL / PKV_EUNSUPPORTED as paged_decode_attention would, or
  * PKV_EHIP if the device query fails.  Does not touch device memory.
  */

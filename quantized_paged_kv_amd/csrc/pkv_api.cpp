@@ -47,22 +47,34 @@ pkv::Variant variant_of(const pkv_problem& p) {
   v.ext = p.sliding_window > 0 || p.softcap > 0.0f;
   v.kvp = 0;
   v.mt = qtok_of(p) > 1;
+  v.vb = 1;
   return v;
 }
 
 // Several KV heads per CTA (split_kvp_kernel, kpc = 4 or 8): dense rows,
-// separate caches, a multiple of kpc KV heads and at most 16 query heads per
-// KV head.
+// separate caches, a multiple of kpc KV heads and at most 16 head slots
+// (query heads x query tokens) per KV head -- or 32 (two head blocks per
+// wave) with four KV heads per CTA and head sizes up to 128.
 bool kvp_allowed(const pkv_problem& p, int kpc) {
+  const int vg = vgroup_of(p);
   return (kpc == pkv::kKvHeadsPerCta || kpc == pkv::kKvHeadsPerCtaWide) &&
          p.layout == PKV_SEPARATE && p.max_candidates == 0 && p.num_kv_heads % kpc == 0 &&
-         vgroup_of(p) <= 16;
+         (vg <= 16 || (vg <= 32 && kpc == pkv::kKvHeadsPerCta && p.head_size <= 128));
 }
 
-// Work units per row: (KV head, 16-query-head block), or groups of four KV
-// heads in the four-head mode.
+// The kernel variant of a problem run with kv_per_cta KV heads per CTA.
+pkv::Variant variant_for(const pkv_problem& p, int kv_per_cta) {
+  pkv::Variant v = variant_of(p);
+  v.kvp = kv_per_cta > 1 ? kv_per_cta : 0;
+  v.vb = v.kvp ? ceil_div(vgroup_of(p), 16) : 1;
+  return v;
+}
+
+// Work units per row: (KV head, 16-slot head block), or groups of kpc KV
+// heads with all their head slots in the several-heads mode.
 int64_t units_row_of(const pkv_problem& p, int kv_per_cta) {
-  return (int64_t)(p.num_kv_heads / kv_per_cta) * ceil_div(vgroup_of(p), 16);
+  if (kv_per_cta > 1) return p.num_kv_heads / kv_per_cta;
+  return (int64_t)p.num_kv_heads * ceil_div(vgroup_of(p), 16);
 }
 
 // Most positions one row can have: the candidate-list capacity (gathered
@@ -170,8 +182,9 @@ std::mutex g_dev_mu;
 std::unordered_map<int, DeviceInfo> g_dev;
 
 uint64_t variant_key(const pkv::Variant& v) {
-  return ((uint64_t)v.cache_dtype << 40) | ((uint64_t)v.head_size << 24) |
-         ((uint64_t)v.v_head_size << 8) | (v.kvp << 3) | (v.ext << 2) | (v.latent << 1) | v.gathered;
+  return ((uint64_t)v.cache_dtype << 48) | ((uint64_t)v.head_size << 32) |
+         ((uint64_t)v.v_head_size << 16) | ((uint64_t)v.mt << 10) | ((uint64_t)v.vb << 8) |
+         (v.kvp << 3) | (v.ext << 2) | (v.latent << 1) | v.gathered;
 }
 
 pkv_status device_numbers(const pkv::Variant& v, int* cus, int* occ) {
@@ -206,8 +219,7 @@ pkv_status check_geometry(const pkv_problem& p, const pkv_geometry* g) {
     return fail(PKV_EINVAL, "geometry num_splits %d outside [1, %d]", g->num_splits, pkv::kMaxSplits);
   if (g->min_chunk < 16 || g->min_chunk % 16)
     return fail(PKV_EINVAL, "geometry min_chunk %d is not a positive multiple of 16", g->min_chunk);
-  pkv::Variant var = variant_of(p);
-  var.kvp = g->kv_heads_per_cta > 1 ? g->kv_heads_per_cta : 0;
+  const pkv::Variant var = variant_for(p, g->kv_heads_per_cta);
   if (g->head_blocks != ceil_div(vgroup_of(p), 16) || g->threads != pkv::threads_of(var) ||
       (g->kv_heads_per_cta != 1 && !kvp_allowed(p, g->kv_heads_per_cta)) ||
       g->grid_x != grid_ctas_for(p, g->num_splits, g->target_ctas, g->kv_heads_per_cta) || g->grid_y != 1 ||
@@ -478,14 +490,19 @@ pkv_status split_geometry(const pkv_problem* problem, const pkv_geometry_opts* o
                 pkv::kKvHeadsPerCtaWide);
   if (o.kv_heads_per_cta > 1 && !kvp_allowed(p, o.kv_heads_per_cta))
     return fail(PKV_EUNSUPPORTED, "%d KV heads per CTA need dense rows, the SEPARATE layout, a "
-                                  "multiple of %d KV heads and at most 16 query heads per KV head",
+                                  "multiple of %d KV heads and at most 16 head slots per KV head "
+                                  "(32 with 4 KV heads per CTA and head size up to 128)",
                 o.kv_heads_per_cta, o.kv_heads_per_cta);
   // (automatic for head sizes up to 128: measured faster there; larger
-  // heads need more registers per wave than two waves per SIMD allow)
-  const int kv_per_cta = o.kv_heads_per_cta ? o.kv_heads_per_cta
-                         : (kvp_allowed(p, pkv::kKvHeadsPerCta) && p.head_size <= 128 ? pkv::kKvHeadsPerCta : 1);
-  pkv::Variant var = variant_of(p);
-  var.kvp = kv_per_cta > 1 ? kv_per_cta : 0;
+  // heads need more registers per wave than two waves per SIMD allow.  With
+  // 17-32 head slots per KV head only for FP16 caches: with one-byte codes
+  // the KV bytes per position halve while a split's partial does not, and
+  // one KV head per CTA with fewer splits measured faster -- C3's lengths,
+  // INT8, 8 tokens per row: 59.3 us against 63.3 at best)
+  const bool auto_kvp = kvp_allowed(p, pkv::kKvHeadsPerCta) && p.head_size <= 128 &&
+                        (vgroup_of(p) <= 16 || p.cache_dtype == PKV_F16);
+  const int kv_per_cta = o.kv_heads_per_cta ? o.kv_heads_per_cta : (auto_kvp ? pkv::kKvHeadsPerCta : 1);
+  const pkv::Variant var = variant_for(p, kv_per_cta);
   const int64_t units = std::max<int64_t>(1, (int64_t)p.num_rows * units_row_of(p, kv_per_cta));
   const int64_t cap = positions_cap(p);
 
@@ -496,13 +513,21 @@ pkv_status split_geometry(const pkv_problem* problem, const pkv_geometry_opts* o
   // sum cannot reach 2^31)
   const bool balanced = balance_fits(p) &&
                         (o.balance == 1 || (o.balance == 0 && p.num_rows >= kMinBalancedRows));
+  // Two head blocks per wave (17-32 head slots per KV head): one CTA per CU
+  // (its four waves already carry twice the scores and accumulators), all
+  // CTAs resident in one round (see target below) and the quarter-partial
+  // chunk floor -- measured on MI355X with C3's lengths: 8 tokens per row
+  // 92.5 -> 79.2 us, 32 query heads per KV head 53.8 -> 46.4 us, 20 query
+  // heads 50.2 -> 41.7 us against one KV head per CTA; two CTAs per CU, a
+  // partial second round or the eighth-partial floor left tails.
+  const bool two_blocks = var.vb == 2;
   int cus = o.num_cus, occ = o.ctas_per_cu;
   if (cus == 0 || occ == 0) {
     int qc = 0, qo = 0;
     st = device_numbers(var, &qc, occ == 0 ? &qo : nullptr);
     if (st != PKV_OK) return st;
     if (cus == 0) cus = qc;
-    if (occ == 0) occ = qo;
+    if (occ == 0) occ = two_blocks ? 1 : qo;
   }
   // Live-balanced mode: about two rounds of CTAs per resident slot let the
   // dispatcher even out what per-row rounding leaves (measured on MI355X),
@@ -521,7 +546,8 @@ pkv_status split_geometry(const pkv_problem* problem, const pkv_geometry_opts* o
   // most an eighth of the KV bytes it covers while the grid still gives
   // every CU a CTA; else at most a quarter while it still fills a quarter
   // of the resident CTAs; else 64 (a small step is bound by latency, and
-  // more, shorter splits finish sooner).
+  // more, shorter splits finish sooner).  With two head blocks per wave: at
+  // most a quarter, always.
   int min_chunk = o.min_chunk;
   if (min_chunk == 0) {
     min_chunk = 64;
@@ -531,7 +557,9 @@ pkv_status split_geometry(const pkv_problem* problem, const pkv_geometry_opts* o
       return std::min<int64_t>(c, 1 << 20);
     };
     const int64_t c8 = floor_for(8), c4 = floor_for(4);
-    if (c8 > min_chunk && units * ceil_div(cap, c8) >= (int64_t)cus)
+    if (two_blocks)
+      min_chunk = (int)std::max<int64_t>(min_chunk, c4);
+    else if (c8 > min_chunk && units * ceil_div(cap, c8) >= (int64_t)cus)
       min_chunk = (int)c8;
     else if (c4 > min_chunk && units * ceil_div(cap, c4) * 4 >= (int64_t)cus * occ)
       min_chunk = (int)c4;
@@ -541,7 +569,10 @@ pkv_status split_geometry(const pkv_problem* problem, const pkv_geometry_opts* o
   // units' partials, and a second round measured slower)
   const int waves = waves_req ? waves_req
                               : (balanced && cheap_partials && kv_per_cta == 1 ? 2 : 1);
-  const int64_t target = (int64_t)waves * cus * occ;
+  int64_t target = (int64_t)waves * cus * occ;
+  // (per-row rounding adds at most one CTA per unit to the live-balanced
+  // count: with two head blocks, leave that room in the round)
+  if (two_blocks && balanced && 2 * units <= target) target -= units;
   int S;
   if (o.splits_override > 0) {
     S = o.splits_override;

@@ -24,7 +24,7 @@ struct SplitArgs {
   float* ws_ml;                 // [rows, heads, S, 2]
   int rows, heads, kv_heads, group, head_blocks;
   int qtok;                     // query tokens per row (T >= 1; T > 1: head slots are (token, head))
-  int units_row;                // work units per row: kv_heads * head_blocks, or kv_heads / 4
+  int units_row;                // work units per row: kv_heads * head_blocks, or kv_heads / kvp
   int kvp;                      // 4 or 8: that many KV heads per CTA (split_kvp_kernel); else 0
   int block_size, log2_block, max_blocks_per_row, num_pool_blocks, max_candidates;
   int num_splits, min_chunk;
@@ -83,6 +83,7 @@ struct Variant {
   int ext;          // a sliding window or a soft cap is set
   int kvp;          // 4 or 8 KV heads per CTA (dense rows, separate caches); else 0
   int mt;           // several query tokens per row (dense rows, separate caches)
+  int vb;           // with kvp: 16-slot head blocks per wave (1, or 2 for 17-32 slots)
 };
 
 constexpr int kWaves = 4;          // waves per split-kernel CTA

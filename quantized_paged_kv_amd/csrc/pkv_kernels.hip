@@ -1345,13 +1345,15 @@ constexpr int kKvpWavesPerSimd = 2;
 // every token record, at its own pace; on MI355X a streaming probe reads
 // such per-head slices at 5.4-5.6 TB/s, but 6.3 TB/s when the four waves of
 // one CTA read four neighbouring slices of the same records together.  So
-// when a problem has a multiple of four KV heads (and at most 16 query
-// heads per KV head), one CTA takes KV heads 4u .. 4u + 3 of a row and
-// split: wave w takes KV head 4u + w and every tile of the split's range,
-// with split_kernel's per-tile code (gather, exact conversion, MFMA scores,
-// online softmax, PV).  Each wave holds the complete state of its query
-// heads, so the waves need no merge: every wave writes its own partials
-// straight from registers.
+// when a problem has a multiple of four KV heads, one CTA takes KV heads
+// 4u .. 4u + 3 of a row and split: wave w takes KV head 4u + w and every
+// tile of the split's range, with split_kernel's per-tile code (gather,
+// exact conversion, MFMA scores, online softmax, PV) for VB 16-slot head
+// blocks of its KV head (VB = 2 for 17-32 (token, head) slots: both MFMA
+// column tiles share each K / V tile the wave loads and converts, so every
+// KV byte is read once for all slots).  Each wave holds the complete state
+// of its slots, so the waves need no merge: every wave writes its own
+// partials straight from registers.
 //
 // Several CTAs share a CU, and the sequencer issues the oldest wave first,
 // so with equal priorities the CTAs dispatched last to a CU starved: on the
@@ -1365,12 +1367,13 @@ constexpr int kKvpWavesPerSimd = 2;
 // tile at three waves per SIMD once the priorities are set), one for smaller
 // tiles (see NST).
 
-template <int CT, int D, int VD, bool EXT, int KPC, bool MT>
+template <int CT, int D, int VD, bool EXT, int KPC, bool MT, int VB>
 __global__ void __launch_bounds__(64 * KPC)
 __attribute__((amdgpu_waves_per_eu(kKvpWavesPerSimd)))
 split_kvp_kernel(const SplitArgs a) {
   __builtin_amdgcn_s_setprio(3);
   using C = SplitCfg<CT, D, VD, false, false>;
+  static_assert(VB == 1 || VB == 2, "one or two 16-slot head blocks per wave");
   constexpr int W = KPC;       // KV heads per CTA, one per wave
   constexpr int NT = 64 * W;   // threads per CTA
   // tiles held per wave: one consumed, two in flight -- or one for tiles of
@@ -1407,28 +1410,33 @@ split_kvp_kernel(const SplitArgs a) {
   const int r = wk.r;
   const int g = wk.g + wave;     // this wave's KV head
 
-  __shared__ uint4 s_q[W][C::NKS * 64];
-  __shared__ float s_err[W][C::NKS * 64];
+  // Q' of head block vb of KV head 4u + w at [w * VB + vb]
+  __shared__ uint4 s_q[W * VB][C::NKS * 64];
+  __shared__ float s_err[W * VB][C::NKS * 64];
   __shared__ int s_flag[2 * W];  // [w]: deep tail, [W + w]: folding, of wave w
   __shared__ float s_vs[W][VD];
   constexpr int QPT = (C::NKS * 64 + NT - 1) / NT;
-  uint4 qraw[W][QPT];
-  float4 ksc[W][QPT][2];
+  uint4 qraw[W * VB][QPT];
+  float4 ksc[W * VB][QPT][2];
   Scales sc[W];
   const int32_t* bt_row = a.block_table + (size_t)r * a.max_blocks_per_row;
   // every wave walks every tile: the block ids of the split's first 64 tiles
   WaveBlocks wb{bt_row, wk.base + split_p0(a, wk), 0, 1, 0, 0};
   wb.load(a, 0, lane);
-  auto unit_of = [&](int u4) __attribute__((always_inline)) {
+  // head block vb (slots 16 vb .. 16 vb + 15) of KV head 4u + u4
+  auto unit_of = [&](int u4, int vb) __attribute__((always_inline)) {
     Work w = wk;
     w.g = wk.g + u4;
-    w.h0 = w.g * group;
-    w.nh = vgroup;
+    w.hb = vb;
+    w.h0 = w.g * group + (MT ? 0 : 16 * vb);
+    w.nh = min(16, vgroup - 16 * vb);
     return w;
   };
 #pragma unroll
   for (int u4 = 0; u4 < W; ++u4) {
-    q_issue<C::NKS, C::EB, D, QPT, NT, MT>(a, unit_of(u4), qraw[u4], ksc[u4]);
+#pragma unroll
+    for (int vb = 0; vb < VB; ++vb)
+      q_issue<C::NKS, C::EB, D, QPT, NT, MT>(a, unit_of(u4, vb), qraw[u4 * VB + vb], ksc[u4 * VB + vb]);
     sc[u4] = load_scales<VD, NT>(a, wk.g + u4);
   }
   finish_item<false, EXT>(a, wk, balanced, raw_npos, 0);
@@ -1447,9 +1455,15 @@ split_kvp_kernel(const SplitArgs a) {
   const int split = wk.split;
   const int ntiles = (p1 - p0 + 15) >> 4;
   // several tokens per row: positions of this lane's head slot
-  int lim = p1;
-  if constexpr (MT)
-    lim = li < vgroup ? wk.npos - (a.qtok - 1 - head_slot<MT>(a, unit_of(wave), li).tok) : p1;
+  int lim[VB];
+#pragma unroll
+  for (int vb = 0; vb < VB; ++vb) {
+    lim[vb] = p1;
+    if constexpr (MT)
+      lim[vb] = li < min(16, vgroup - 16 * vb)
+                    ? wk.npos - (a.qtok - 1 - head_slot<MT>(a, unit_of(wave, vb), li).tok)
+                    : p1;
+  }
 
   const uint32_t tok_k = (uint32_t)KVH * C::KROW;
   const uint32_t tok_v = (uint32_t)KVH * C::VROW;
@@ -1491,25 +1505,37 @@ split_kvp_kernel(const SplitArgs a) {
     T.vmask = vm;
   };
 
-  f32x4 acc[C::NCT];
+  // per head block: accumulator, running maximum and sum of the lane's head
+  // slot, smallest valid score
+  f32x4 acc[VB][C::NCT];
+  float m_ref[VB], l_part[VB], smin[VB];
+  const uint4* sq[VB];
 #pragma unroll
-  for (int ct = 0; ct < C::NCT; ++ct) acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_ref = kNegInf;
-  float l_part = 0.0f;
-  float smin = __builtin_inff();
-  const uint4* const sq = s_q[wave];
+  for (int vb = 0; vb < VB; ++vb) {
+#pragma unroll
+    for (int ct = 0; ct < C::NCT; ++ct) acc[vb][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+    m_ref[vb] = kNegInf;
+    l_part[vb] = 0.0f;
+    smin[vb] = __builtin_inff();
+    sq[vb] = s_q[wave * VB + vb];
+  }
 
   // split_kernel's tile consumer, on this wave's query block
   auto consume = [&](const Tile<C>& T, int tt, auto lo) __attribute__((always_inline)) {
     constexpr bool LO = decltype(lo)::value;
-    f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
+    f32x4 sacc[VB];
+#pragma unroll
+    for (int vb = 0; vb < VB; ++vb) sacc[vb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < C::NKL; ++s) {
       if constexpr (C::EB == 2) {
         const half8 kop = __builtin_bit_cast(
             half8, uint4{T.k[4 * s], T.k[4 * s + 1], T.k[4 * s + 2], T.k[4 * s + 3]});
-        const half8 qop = __builtin_bit_cast(half8, sq[s * 64 + lane]);
-        sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop, qop, sacc, 0, 0, 0);
+#pragma unroll
+        for (int vb = 0; vb < VB; ++vb) {
+          const half8 qop = __builtin_bit_cast(half8, sq[vb][s * 64 + lane]);
+          sacc[vb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop, qop, sacc[vb], 0, 0, 0);
+        }
       } else {
         const half4 c0 = codes4_to_half4<CT>(T.k[4 * s + 0]);
         const half4 c1 = codes4_to_half4<CT>(T.k[4 * s + 1]);
@@ -1517,40 +1543,47 @@ split_kvp_kernel(const SplitArgs a) {
         const half4 c3 = codes4_to_half4<CT>(T.k[4 * s + 3]);
         const half8 k0 = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
         const half8 k1 = {c2[0], c2[1], c2[2], c2[3], c3[0], c3[1], c3[2], c3[3]};
-        const half8 q0 = __builtin_bit_cast(half8, sq[(2 * s) * 64 + lane]);
-        const half8 q1 = __builtin_bit_cast(half8, sq[(2 * s + 1) * 64 + lane]);
-        sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(k0, q0, sacc, 0, 0, 0);
-        sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(k1, q1, sacc, 0, 0, 0);
+#pragma unroll
+        for (int vb = 0; vb < VB; ++vb) {
+          const half8 q0 = __builtin_bit_cast(half8, sq[vb][(2 * s) * 64 + lane]);
+          const half8 q1 = __builtin_bit_cast(half8, sq[vb][(2 * s + 1) * 64 + lane]);
+          sacc[vb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(k0, q0, sacc[vb], 0, 0, 0);
+          sacc[vb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(k1, q1, sacc[vb], 0, 0, 0);
+        }
       }
     }
-    float x[4];
-    scaled_scores<EXT>(a, sacc, x);
+    half4 pop[VB], pol[VB];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      bool valid = (T.vmask >> q) & 1u;
-      if constexpr (MT) valid = valid && p0 + 16 * tt + 4 * lj + q < lim;
-      else (void)tt;
-      x[q] = valid ? x[q] : kNegInf;
-      smin = fminf(smin, valid ? x[q] : __builtin_inff());
+    for (int vb = 0; vb < VB; ++vb) {
+      float x[4];
+      scaled_scores<EXT>(a, sacc[vb], x);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        bool valid = (T.vmask >> q) & 1u;
+        if constexpr (MT) valid = valid && p0 + 16 * tt + 4 * lj + q < lim[vb];
+        else (void)tt;
+        x[q] = valid ? x[q] : kNegInf;
+        smin[vb] = fminf(smin[vb], valid ? x[q] : __builtin_inff());
+      }
+      float mt = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+      mt = fmaxf(mt, __shfl_xor(mt, 16));
+      mt = fmaxf(mt, __shfl_xor(mt, 32));
+      if (__any(mt > m_ref[vb] + kRescaleSlack)) {
+        const float mn = fmaxf(m_ref[vb], mt);
+        const float alpha =
+            (m_ref[vb] == kNegInf) ? 0.0f : __builtin_amdgcn_exp2f((m_ref[vb] - mn) * kLog2e);
+        l_part[vb] *= alpha;
+#pragma unroll
+        for (int ct = 0; ct < C::NCT; ++ct) acc[vb][ct] *= alpha;
+        m_ref[vb] = mn;
+      }
+      const float mu = (m_ref[vb] == kNegInf) ? 0.0f : m_ref[vb];
+      float p[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) p[q] = __builtin_amdgcn_exp2f((x[q] - mu) * kLog2e);
+      l_part[vb] += (p[0] + p[1]) + (p[2] + p[3]);
+      split_prob<LO>(p, pop[vb], pol[vb]);
     }
-    float mt = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-    mt = fmaxf(mt, __shfl_xor(mt, 16));
-    mt = fmaxf(mt, __shfl_xor(mt, 32));
-    if (__any(mt > m_ref + kRescaleSlack)) {
-      const float mn = fmaxf(m_ref, mt);
-      const float alpha = (m_ref == kNegInf) ? 0.0f : __builtin_amdgcn_exp2f((m_ref - mn) * kLog2e);
-      l_part *= alpha;
-#pragma unroll
-      for (int ct = 0; ct < C::NCT; ++ct) acc[ct] *= alpha;
-      m_ref = mn;
-    }
-    const float mu = (m_ref == kNegInf) ? 0.0f : m_ref;
-    float p[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) p[q] = __builtin_amdgcn_exp2f((x[q] - mu) * kLog2e);
-    l_part += (p[0] + p[1]) + (p[2] + p[3]);
-    half4 pop, pol;
-    split_prob<LO>(p, pop, pol);
     if constexpr (C::EB == 2) {
 #pragma unroll
       for (int w = 0; w < C::NVW; ++w) {
@@ -1559,12 +1592,16 @@ split_kvp_kernel(const SplitArgs a) {
         const uint32_t a01 = perm(r1, r0, 0x05040100u), a23 = perm(r3, r2, 0x05040100u);
         const uint32_t b01 = perm(r1, r0, 0x07060302u), b23 = perm(r3, r2, 0x07060302u);
         const half4 va = __builtin_bit_cast(half4, uint2{a01, a23});
-        const half4 vb = __builtin_bit_cast(half4, uint2{b01, b23});
-        acc[2 * w] = __builtin_amdgcn_mfma_f32_16x16x16f16(va, pop, acc[2 * w], 0, 0, 0);
-        acc[2 * w + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(vb, pop, acc[2 * w + 1], 0, 0, 0);
-        if constexpr (LO) {
-          acc[2 * w] = __builtin_amdgcn_mfma_f32_16x16x16f16(va, pol, acc[2 * w], 0, 0, 0);
-          acc[2 * w + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(vb, pol, acc[2 * w + 1], 0, 0, 0);
+        const half4 vc = __builtin_bit_cast(half4, uint2{b01, b23});
+#pragma unroll
+        for (int vb = 0; vb < VB; ++vb) {
+          acc[vb][2 * w] = __builtin_amdgcn_mfma_f32_16x16x16f16(va, pop[vb], acc[vb][2 * w], 0, 0, 0);
+          acc[vb][2 * w + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(vc, pop[vb], acc[vb][2 * w + 1], 0, 0, 0);
+          if constexpr (LO) {
+            acc[vb][2 * w] = __builtin_amdgcn_mfma_f32_16x16x16f16(va, pol[vb], acc[vb][2 * w], 0, 0, 0);
+            acc[vb][2 * w + 1] =
+                __builtin_amdgcn_mfma_f32_16x16x16f16(vc, pol[vb], acc[vb][2 * w + 1], 0, 0, 0);
+          }
         }
       }
     } else {
@@ -1578,15 +1615,18 @@ split_kvp_kernel(const SplitArgs a) {
         const uint32_t o2 = perm(t3, t1, 0x05040100u), o3 = perm(t3, t1, 0x07060302u);
         const half4 h0 = codes4_to_half4<CT>(o0), h1 = codes4_to_half4<CT>(o1);
         const half4 h2 = codes4_to_half4<CT>(o2), h3 = codes4_to_half4<CT>(o3);
-        acc[4 * w + 0] = __builtin_amdgcn_mfma_f32_16x16x16f16(h0, pop, acc[4 * w + 0], 0, 0, 0);
-        acc[4 * w + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(h1, pop, acc[4 * w + 1], 0, 0, 0);
-        acc[4 * w + 2] = __builtin_amdgcn_mfma_f32_16x16x16f16(h2, pop, acc[4 * w + 2], 0, 0, 0);
-        acc[4 * w + 3] = __builtin_amdgcn_mfma_f32_16x16x16f16(h3, pop, acc[4 * w + 3], 0, 0, 0);
-        if constexpr (LO) {
-          acc[4 * w + 0] = __builtin_amdgcn_mfma_f32_16x16x16f16(h0, pol, acc[4 * w + 0], 0, 0, 0);
-          acc[4 * w + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(h1, pol, acc[4 * w + 1], 0, 0, 0);
-          acc[4 * w + 2] = __builtin_amdgcn_mfma_f32_16x16x16f16(h2, pol, acc[4 * w + 2], 0, 0, 0);
-          acc[4 * w + 3] = __builtin_amdgcn_mfma_f32_16x16x16f16(h3, pol, acc[4 * w + 3], 0, 0, 0);
+#pragma unroll
+        for (int vb = 0; vb < VB; ++vb) {
+          acc[vb][4 * w + 0] = __builtin_amdgcn_mfma_f32_16x16x16f16(h0, pop[vb], acc[vb][4 * w + 0], 0, 0, 0);
+          acc[vb][4 * w + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(h1, pop[vb], acc[vb][4 * w + 1], 0, 0, 0);
+          acc[vb][4 * w + 2] = __builtin_amdgcn_mfma_f32_16x16x16f16(h2, pop[vb], acc[vb][4 * w + 2], 0, 0, 0);
+          acc[vb][4 * w + 3] = __builtin_amdgcn_mfma_f32_16x16x16f16(h3, pop[vb], acc[vb][4 * w + 3], 0, 0, 0);
+          if constexpr (LO) {
+            acc[vb][4 * w + 0] = __builtin_amdgcn_mfma_f32_16x16x16f16(h0, pol[vb], acc[vb][4 * w + 0], 0, 0, 0);
+            acc[vb][4 * w + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(h1, pol[vb], acc[vb][4 * w + 1], 0, 0, 0);
+            acc[vb][4 * w + 2] = __builtin_amdgcn_mfma_f32_16x16x16f16(h2, pol[vb], acc[vb][4 * w + 2], 0, 0, 0);
+            acc[vb][4 * w + 3] = __builtin_amdgcn_mfma_f32_16x16x16f16(h3, pol[vb], acc[vb][4 * w + 3], 0, 0, 0);
+          }
         }
       }
     }
@@ -1598,11 +1638,17 @@ split_kvp_kernel(const SplitArgs a) {
   for (int i = 0; i < NST - 1; ++i) issue(buf[i], i);
 #pragma unroll
   for (int u4 = 0; u4 < W; ++u4) {
-    q_stage<C::NKS, C::EB, D, QPT, NT>(qraw[u4], ksc[u4], sc[u4].k_tensor, s_q[u4], s_err[u4]);
+#pragma unroll
+    for (int vb = 0; vb < VB; ++vb)
+      q_stage<C::NKS, C::EB, D, QPT, NT>(qraw[u4 * VB + vb], ksc[u4 * VB + vb], sc[u4].k_tensor,
+                                         s_q[u4 * VB + vb], s_err[u4 * VB + vb]);
     stage_scales<VD, NT>(a, sc[u4], s_vs[u4]);
   }
   __syncthreads();
-  const bool fold = fold_over_budget<CT, C::NKS>(a, s_err[wave], vgroup, lane);
+  bool fold = false;
+#pragma unroll
+  for (int vb = 0; vb < VB; ++vb)
+    fold |= fold_over_budget<CT, C::NKS>(a, s_err[wave * VB + vb], min(16, vgroup - 16 * vb), lane);
 
   auto tile_loop = [&](auto lo) __attribute__((always_inline)) {
     for (int t = 0; t < ntiles; t += NST) {
@@ -1625,9 +1671,13 @@ split_kvp_kernel(const SplitArgs a) {
     }
   };
   tile_loop(std::integral_constant<bool, kResidualTile>{});
-  const bool deep = smin != __builtin_inff() && smin - m_ref < kTailLog;
-  l_part += __shfl_xor(l_part, 16);
-  l_part += __shfl_xor(l_part, 32);
+  bool deep = false;
+#pragma unroll
+  for (int vb = 0; vb < VB; ++vb) {
+    deep = deep || (smin[vb] != __builtin_inff() && smin[vb] - m_ref[vb] < kTailLog);
+    l_part[vb] += __shfl_xor(l_part[vb], 16);
+    l_part[vb] += __shfl_xor(l_part[vb], 32);
+  }
   {
     const bool dw = __any(deep);
     if (lane == 0) {
@@ -1651,33 +1701,36 @@ split_kvp_kernel(const SplitArgs a) {
       // value scales come from s_vs
       static_assert(W * (VD + 2) * 4 <= (int)sizeof(s_q), "FP32-path scratch fits the query stage");
 #pragma unroll 1
-      for (int u4 = 0; u4 < W; ++u4)
-        exact_partial<CT, D, VD, false, false, W, EXT, MT>(a, unit_of(u4), p0, p1, sc[0], s_vs[u4],
+      for (int u = 0; u < W * VB; ++u)
+        exact_partial<CT, D, VD, false, false, W, EXT, MT>(a, unit_of(u / VB, u % VB), p0, p1, sc[0],
+                                                           s_vs[u / VB],
                                                            reinterpret_cast<float*>(&s_q[0][0]));
       return;
     }
   }
 
   // ---- this wave's partials, straight from registers: lane (li, lj) holds
-  // channels (4 lj + q) CPL + ct of head li
-  if (li < vgroup) {
-    const HeadSlot hs = head_slot<MT>(a, unit_of(wave), li);
+  // channels (4 lj + q) CPL + ct of slot li of each head block
+#pragma unroll
+  for (int vb = 0; vb < VB; ++vb) {
+    if (li >= min(16, vgroup - 16 * vb)) continue;
+    const HeadSlot hs = head_slot<MT>(a, unit_of(wave, vb), li);
     const int h = hs.h;
     const size_t pair = hs.pair;
     const size_t pidx = pair * S + split;
     Final fin{0.0f, kNegInf};
     if (a.direct) {
-      fin = final_of(a, h, m_ref, l_part);
+      fin = final_of(a, h, m_ref[vb], l_part[vb]);
       if (a.lse_out && lj == 0) a.lse_out[pair] = fin.lse;
     } else if (lj == 0) {
-      reinterpret_cast<float2*>(a.ws_ml)[pidx] = make_float2(m_ref, l_part);
+      reinterpret_cast<float2*>(a.ws_ml)[pidx] = make_float2(m_ref[vb], l_part[vb]);
     }
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
 #pragma unroll
       for (int c4 = 0; c4 < C::CPL; c4 += 4) {
         const int ch = (4 * lj + q) * C::CPL + c4;
-        float4 o = make_float4(acc[c4][q], acc[c4 + 1][q], acc[c4 + 2][q], acc[c4 + 3][q]);
+        float4 o = make_float4(acc[vb][c4][q], acc[vb][c4 + 1][q], acc[vb][c4 + 2][q], acc[vb][c4 + 3][q]);
         o.x *= a.v_mult * v_scale_of(a, sc[0], s_vs[wave], ch);
         o.y *= a.v_mult * v_scale_of(a, sc[0], s_vs[wave], ch + 1);
         o.z *= a.v_mult * v_scale_of(a, sc[0], s_vs[wave], ch + 2);
@@ -2498,14 +2551,21 @@ static hipError_t launch_one(const SplitArgs& a, hipStream_t stream) {
     return hipErrorInvalidValue;  // several tokens per row: dense rows, separate caches
   } else {
     if constexpr (!LAT && !GA) {
-      if (a.kvp == 4) {
-        hipLaunchKernelGGL((split_kvp_kernel<CT, D, VD, EXT, 4, MT>), grid, dim3(256), 0, stream, a);
+      const bool two = a.qtok * a.group > 16;  // two head blocks per wave
+      if (a.kvp == 4 && !two) {
+        hipLaunchKernelGGL((split_kvp_kernel<CT, D, VD, EXT, 4, MT, 1>), grid, dim3(256), 0, stream, a);
         return hipGetLastError();
       }
-      if (a.kvp == 8) {
-        hipLaunchKernelGGL((split_kvp_kernel<CT, D, VD, EXT, 8, MT>), grid, dim3(512), 0, stream, a);
+      if constexpr (D <= 128)
+        if (a.kvp == 4 && two) {
+          hipLaunchKernelGGL((split_kvp_kernel<CT, D, VD, EXT, 4, MT, 2>), grid, dim3(256), 0, stream, a);
+          return hipGetLastError();
+        }
+      if (a.kvp == 8 && !two) {
+        hipLaunchKernelGGL((split_kvp_kernel<CT, D, VD, EXT, 8, MT, 1>), grid, dim3(512), 0, stream, a);
         return hipGetLastError();
       }
+      if (a.kvp) return hipErrorInvalidValue;
     }
     if constexpr (LAT)
       hipLaunchKernelGGL((latent_kernel<CT, GA, EXT>), grid, dim3(LatCfg<CT, GA>::NT), 0, stream, a);
@@ -2516,17 +2576,22 @@ static hipError_t launch_one(const SplitArgs& a, hipStream_t stream) {
 }
 
 template <int CT, int D, int VD, bool LAT, bool GA, bool EXT, bool MT>
-static hipError_t occupancy_one(int* n, int kvp) {
+static hipError_t occupancy_one(int* n, int kvp, int vb) {
   if constexpr (MT && (LAT || GA)) {
     return hipErrorInvalidValue;
   } else {
     if constexpr (!LAT && !GA) {
-      if (kvp == 4)
-        return hipOccupancyMaxActiveBlocksPerMultiprocessor(n, split_kvp_kernel<CT, D, VD, EXT, 4, MT>,
+      if (kvp == 4 && vb == 1)
+        return hipOccupancyMaxActiveBlocksPerMultiprocessor(n, split_kvp_kernel<CT, D, VD, EXT, 4, MT, 1>,
                                                              256, 0);
-      if (kvp == 8)
-        return hipOccupancyMaxActiveBlocksPerMultiprocessor(n, split_kvp_kernel<CT, D, VD, EXT, 8, MT>,
+      if constexpr (D <= 128)
+        if (kvp == 4 && vb == 2)
+          return hipOccupancyMaxActiveBlocksPerMultiprocessor(
+              n, split_kvp_kernel<CT, D, VD, EXT, 4, MT, 2>, 256, 0);
+      if (kvp == 8 && vb == 1)
+        return hipOccupancyMaxActiveBlocksPerMultiprocessor(n, split_kvp_kernel<CT, D, VD, EXT, 8, MT, 1>,
                                                              512, 0);
+      if (kvp) return hipErrorInvalidValue;
     }
     if constexpr (LAT)
       return hipOccupancyMaxActiveBlocksPerMultiprocessor(n, latent_kernel<CT, GA, EXT>,
@@ -2591,7 +2656,7 @@ hipError_t launch_split(const Variant& v, const SplitArgs& a, hipStream_t stream
 
 hipError_t split_occupancy(const Variant& v, int* ctas_per_cu) {
   hipError_t err = hipErrorInvalidValue;
-#define PKV_OCC(CT, D, VD, LAT, GA, EXT, MT) err = occupancy_one<CT, D, VD, LAT, GA, EXT, MT>(ctas_per_cu, v.kvp)
+#define PKV_OCC(CT, D, VD, LAT, GA, EXT, MT) err = occupancy_one<CT, D, VD, LAT, GA, EXT, MT>(ctas_per_cu, v.kvp, v.vb)
   PKV_FOR_VARIANT(v, PKV_OCC);
 #undef PKV_OCC
   return err;

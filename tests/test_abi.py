@@ -367,7 +367,34 @@ def test_query_tokens_geometry_and_limits():
     assert g.workspace_bytes == 16 * 4 * 32 * g.num_splits * (128 + 2) * 4
     p8 = pkv.make_problem(16, 32, 8, 128, 128, 16, 512, 5000, query_tokens=8)
     g8 = pkv.split_geometry(p8, num_cus=256, ctas_per_cu=2)
-    assert g8.head_blocks == 2 and g8.kv_heads_per_cta == 1
+    # 32 slots per KV head: two head blocks, both taken by each wave of the
+    # four-KV-head kernel, so a row has two units (not 8 * 2)
+    assert g8.head_blocks == 2 and g8.kv_heads_per_cta == 4
+    assert g8.grid_x == min(16 * 2 * g8.num_splits, g8.target_ctas + 16 * 2)
+    # two head blocks per wave: the live-balanced target leaves room for the
+    # per-row rounding (one CTA per unit) in the round, and the chunk floor
+    # keeps a split's partial (4 KV heads x 32 slots x 130 FP32) at most a
+    # quarter of the KV bytes it covers (4 KV heads x 512 bytes a position)
+    assert g8.target_ctas == 256 * 2 - 16 * 2 and g8.grid_x <= 256 * 2
+    assert g8.min_chunk == 256
+    # automatic only for FP16 caches: one-byte codes keep one KV head per CTA
+    p8i = pkv.make_problem(16, 32, 8, 128, 128, 16, 512, 5000, query_tokens=8, cache_dtype="i8",
+                           k_quant="tensor", v_quant="tensor")
+    assert pkv.split_geometry(p8i, num_cus=256, ctas_per_cu=2).kv_heads_per_cta == 1
+    assert pkv.split_geometry(p8i, num_cus=256, ctas_per_cu=2, kv_heads_per_cta=4).kv_heads_per_cta == 4
+    g81 = pkv.split_geometry(p8, num_cus=256, ctas_per_cu=2, kv_heads_per_cta=1)
+    assert g81.head_blocks == 2 and g81.kv_heads_per_cta == 1
+    assert g81.grid_x == min(16 * 16 * g81.num_splits, g81.target_ctas + 16 * 16)
+    # eight KV heads per CTA take at most 16 slots per KV head; four take 32
+    # up to head size 128
+    # (9 heads x 4 tokens = 36 slots)
+    for (heads, kvh, D, T), kpc in (((32, 8, 128, 8), 8), ((32, 8, 256, 8), 4), ((36, 4, 128, 4), 4)):
+        q = pkv.make_problem(16, heads, kvh, D, D, 16, 512, 5000, query_tokens=T)
+        with pytest.raises(pkv.PkvError) as e:
+            pkv.split_geometry(q, num_cus=256, ctas_per_cu=2, kv_heads_per_cta=kpc)
+        assert e.value.status == 2
+    assert pkv.split_geometry(pkv.make_problem(16, 32, 8, 256, 256, 16, 512, 5000, query_tokens=8),
+                              num_cus=256, ctas_per_cu=2).kv_heads_per_cta == 1
     for kw, st in ((dict(max_candidates=64), 2), (dict(layout="latent", cache_dtype="fp8",
                                                         k_quant="tensor"), 2),
                    (dict(sliding_window=32), 2), (dict(query_tokens=17), 2),

@@ -28,7 +28,13 @@ def _mt(cache, D, heads, kvh, T, seed=50, rows=6, B=16, mbpr=12):
 
 
 CASES = [("f16", 128, 32, 8, T) for T in (1, 2, 3, 4, 8)] + [
-    ("i8", 256, 24, 2, 3), ("fp8", 64, 64, 8, 2), ("i8", 128, 8, 4, 8), ("fp8", 128, 16, 4, 4)]
+    ("i8", 256, 24, 2, 3), ("fp8", 64, 64, 8, 2), ("i8", 128, 8, 4, 8), ("fp8", 128, 16, 4, 4),
+    ("fp8", 64, 24, 4, 3), ("i8", 128, 40, 4, 3), ("f16", 64, 16, 4, 7)]
+
+
+def _kpc_allowed(D, heads, kvh, T, kpc):
+    vgroup = T * heads // kvh
+    return kpc == 1 or (kvh % kpc == 0 and (vgroup <= 16 or (kpc == 4 and vgroup <= 32 and D <= 128)))
 
 
 @pytest.mark.parametrize("case", CASES, ids=lambda c: "-".join(map(str, c)))
@@ -38,7 +44,7 @@ def test_multitoken_rows_against_the_oracle(case):
     ref, ref_lse = oracle.paged_decode(workloads.expand_query_tokens(inp))
     vgroup = T * heads // kvh
     for S in (1, 5):
-        for kpc in [k for k in (1, 4) if k == 1 or (kvh % k == 0 and vgroup <= 16)]:
+        for kpc in [k for k in (1, 4, 8) if _kpc_allowed(D, heads, kvh, T, k)]:
             announce(f"multi-token {case} S={S} kv_heads_per_cta={kpc}")
             got, lse, g = run_gpu(inp, splits_override=S, min_chunk=16, kv_heads_per_cta=kpc)
             assert g.head_blocks == -(-vgroup // 16)
@@ -51,25 +57,29 @@ def test_multitoken_rows_against_the_oracle(case):
 @pytest.mark.parametrize("name", ["C3t4", "C3t8"])
 def test_multitoken_continuous_batching_full_size(name):
     """C3's 16 sequences with 4 (one MFMA tile of (token, head) pairs per KV
-    head, the four-KV-head kernel) or 8 query tokens (two head blocks) each,
-    default geometry, against the oracle on all their query rows."""
+    head) or 8 query tokens (two tiles, both taken by each wave) each, in the
+    four-KV-head kernel of the default geometry, against the oracle on all
+    their query rows."""
     inp = workloads.workload(name)
     ref, ref_lse = oracle.paged_decode(workloads.expand_query_tokens(inp))
     announce(f"{name} default geometry")
     got, lse, g = run_gpu(inp)
+    assert g.kv_heads_per_cta == 4
     mx, mn = assert_close_to_oracle(got, lse, ref, ref_lse, what=name)
     announce(f"{name}: S={g.num_splits} kv_heads_per_cta={g.kv_heads_per_cta} "
              f"head_blocks={g.head_blocks} max_abs={mx:.2e} mean_abs={mn:.2e}")
 
 
-def test_multitoken_fp32_path():
+@pytest.mark.parametrize("T", [3, 8])
+def test_multitoken_fp32_path(T):
     """A CTA over budget (large queries: the FP32 path) with several tokens
-    per row evaluates each (token, head) pair with its own length."""
-    inp = _mt("i8", 128, 32, 8, 3, seed=13)
+    per row evaluates each (token, head) pair with its own length (with 8
+    tokens: both head blocks of each wave)."""
+    inp = _mt("i8", 128, 32, 8, T, seed=13)
     inp.query[...] = (inp.query.astype(np.float32) * 200.0).astype(np.float16)
     ref, ref_lse = oracle.paged_decode(workloads.expand_query_tokens(inp))
     for kpc in (1, 4):
-        announce(f"multi-token FP32 path kv_heads_per_cta={kpc}")
+        announce(f"multi-token FP32 path T={T} kv_heads_per_cta={kpc}")
         got, lse, _ = run_gpu(inp, splits_override=2, min_chunk=16, out_dtype="f32",
                               kv_heads_per_cta=kpc)
         scale = np.abs(ref).max()
@@ -78,7 +88,7 @@ def test_multitoken_fp32_path():
         np.testing.assert_allclose(lse[fin], ref_lse[fin], rtol=1e-5, atol=1e-4)
 
 
-@pytest.mark.parametrize("T,kpc", [(3, 4), (8, 1)])
+@pytest.mark.parametrize("T,kpc", [(3, 4), (8, 1), (8, 4)])
 def test_multitoken_with_softcap(T, kpc):
     """The soft cap (the kernels' EXT instantiation) with several tokens per
     row: the cap applies to every (token, head) pair's scaled logits."""

@@ -684,26 +684,42 @@ def test_four_kv_heads_per_cta(cache, D, heads, kvh):
             assert_close_to_oracle(got, lse, ref, ref_lse, what=f"{cache} D={D} S={S} kpc={kpc}")
 
 
+@pytest.mark.parametrize("cache,D", [("f16", 128), ("i8", 64), ("fp8", 128)], ids=lambda v: str(v))
+@pytest.mark.parametrize("heads", [72, 128])
+def test_four_kv_heads_per_cta_two_head_blocks(cache, D, heads):
+    """17-32 query heads per KV head (group 18, a ragged second block, and
+    32): each wave takes both 16-slot head blocks of its KV head."""
+    inp = _small(cache, D, D, "separate", False, seed=23, heads=heads, kvh=4)
+    ref, ref_lse = oracle.paged_decode(inp)
+    for S in (1, 5):
+        for kpc in (1, 4):
+            announce(f"{cache} D={D} {heads}q/4kv S={S} kv_heads_per_cta={kpc}")
+            got, lse, g = run_gpu(inp, splits_override=S, min_chunk=16, kv_heads_per_cta=kpc)
+            assert g.kv_heads_per_cta == kpc and g.head_blocks == 2
+            assert_close_to_oracle(got, lse, ref, ref_lse, what=f"{cache} D={D} {heads}q S={S} kpc={kpc}")
+
+
 def test_four_kv_heads_per_cta_is_the_default_where_allowed():
     import quantized_paged_kv_amd as pkv
     from workloads.device import problem_kwargs
 
-    for name, expect in (("C3", 4), ("X4096b8i8", 4), ("C2", 1), ("C4", 1), ("C5", 1)):
+    for name, expect in (("C3", 4), ("X4096b8i8", 4), ("C3t8", 4), ("C2", 1), ("C4", 1), ("C5", 1)):
         inp, _ = named(name)
         g = pkv.split_geometry(pkv.make_problem(**problem_kwargs(inp.problem)))
         assert g.kv_heads_per_cta == expect, name
 
 
+@pytest.mark.parametrize("heads,kvh", [(32, 8), (80, 4)])
 @pytest.mark.parametrize("case", ["fold", "tail"])
-def test_four_kv_heads_per_cta_fp32_path(case):
+def test_four_kv_heads_per_cta_fp32_path(case, heads, kvh):
     # every CTA takes the FP32 path: folding over budget (large queries), or
-    # a deep tail with a large value scale
+    # a deep tail with a large value scale (group 20: two head blocks per wave)
     if case == "fold":
-        inp = _small("i8", 128, 128, "separate", False, seed=13, quant="channel", heads=32, kvh=8)
+        inp = _small("i8", 128, 128, "separate", False, seed=13, quant="channel", heads=heads, kvh=kvh)
         inp.query[...] = (inp.query.astype(np.float32) * 200.0).astype(np.float16)
         rel = 1e-4
     else:
-        inp = _small("i8", 128, 128, "separate", False, seed=11, quant="tensor", heads=32, kvh=8,
+        inp = _small("i8", 128, 128, "separate", False, seed=11, quant="tensor", heads=heads, kvh=kvh,
                      sink=False)
         inp.query[...] = (inp.query.astype(np.float32) * 6.0).astype(np.float16)
         inp.v_scale = (inp.v_scale * 2.0 ** 20).astype(np.float32)
