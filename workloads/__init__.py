@@ -458,6 +458,7 @@ WORKLOADS = {"C1": c1, "C2": c2, "C3": c3, "C4": c4, "C5": c5,
              "C3t4": lambda seed=3: c3_tokens(4, seed),
              "C3t4rows": lambda seed=3: expand_query_tokens(c3_tokens(4, seed)),
              "C3t8": lambda seed=3: c3_tokens(8, seed),
+             "C3t8rows": lambda seed=3: expand_query_tokens(c3_tokens(8, seed)),
              "P128": lambda seed=6: dsa_prefill(128, seed=seed),
              "P2048": lambda seed=6: dsa_prefill(2048, seed=seed),
              "P8192": lambda seed=6: dsa_prefill(8192, seed=seed)}
