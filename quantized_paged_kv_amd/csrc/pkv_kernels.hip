@@ -2454,11 +2454,11 @@ combine_kernel(const CombineArgs a) {
 
 // ---- the combine for few splits -------------------------------------------
 //
-// For few splits (S <= 8, or S <= 16 with many pairs and VD <= 256): PARTS
-// waves per (row, query head), each owning VD / PARTS channels (PARTS = 2
-// for 512 channels, so every lane loads one float4 per split and twice as
-// many CUs pull the partials), four waves per CTA, so a step with many rows
-// does not launch one 512-thread CTA per pair.  The (m, l) pairs are
+// For few splits (S <= 8): PARTS waves per (row, query head), each owning
+// VD / PARTS channels (PARTS = 2 for 512 channels, so every lane loads one
+// float4 per split and twice as many CUs pull the partials), four waves per
+// CTA, so a step with many rows does not launch one 512-thread CTA per
+// pair.  The (m, l) pairs are
 // wave-uniform and come through scalar loads; every lane owns VD / 64 /
 // PARTS consecutive channels, issues all of its partial loads first and sums
 // the weighted partials in split order (deterministic).  Same arithmetic as
@@ -2520,6 +2520,118 @@ __global__ void __launch_bounds__(256) combine_small_kernel(const CombineArgs a)
       if (w != 0.0f) {  // empty splits' accumulators are never used
 #pragma unroll
         for (int j = 0; j < CPL; ++j) o[j] += w * v[k][j];
+      }
+    }
+  }
+  float lse = kNegInf;
+  float f = 0.0f;
+  if (L > 0.0f) {
+    lse = M + logf(L);
+    f = 1.0f / L;
+    if (a.head_sink) f *= 1.0f / (1.0f + expf(a.head_sink[h] - lse));
+  }
+  if (a.lse_out && lane == 0 && part == 0) a.lse_out[pair] = lse;
+  if constexpr (OUT_F32) {
+    float* dst = reinterpret_cast<float*>(a.out) + (size_t)pair * VD + c0;
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) dst[j] = o[j] * f;
+  } else {
+    half_t* dst = reinterpret_cast<half_t*>(a.out) + (size_t)pair * VD + c0;
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) dst[j] = (half_t)(o[j] * f);
+  }
+}
+
+// ---- the wave-per-pair combine for many pairs ------------------------------
+//
+// One wave per (row, query head) (PARTS waves for 512 channels), four waves
+// per CTA, for any S up to 64: lane k reads the (m, l) of split k, the wave
+// reduces M and L with butterflies (a fixed order), and n = 1 + the last
+// split with a nonzero weight bounds the partial loads -- the splits of a
+// row that hold work come first in both decompositions, so a short row of
+// the live-balanced decomposition reads only its own few partials.  The
+// first SPEC splits are loaded before the weights are known (a slot past n
+// is read and ignored), the rest in batches once n is known.  Each lane owns
+// VD / 64 / PARTS consecutive channels and adds the weighted partials in
+// split order.  With many pairs this keeps every CU busy with small CTAs
+// where combine_kernel's one 512-thread CTA per pair runs in several
+// dependent rounds.
+
+template <int CPL>
+__device__ __forceinline__ void load_channels(const float* p, float (&d)[CPL]) {
+  if constexpr (CPL % 4 == 0) {
+#pragma unroll
+    for (int j = 0; j < CPL; j += 4) {
+      const float4 q = *reinterpret_cast<const float4*>(p + j);
+      d[j] = q.x; d[j + 1] = q.y; d[j + 2] = q.z; d[j + 3] = q.w;
+    }
+  } else if constexpr (CPL == 2) {
+    const float2 q = *reinterpret_cast<const float2*>(p);
+    d[0] = q.x; d[1] = q.y;
+  } else {
+    d[0] = p[0];
+  }
+}
+
+template <int VD, bool OUT_F32, int PARTS, int SPEC>
+__global__ void __launch_bounds__(256) combine_wave_kernel(const CombineArgs a) {
+  constexpr int CPL = VD / 64 / PARTS;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int item = blockIdx.x * 4 + wave;
+  const int pair = item / PARTS;
+  const int part = item - pair * PARTS;
+  if (pair >= a.rows * a.heads) return;
+  const int S = a.num_splits;
+  const int h = pair % a.heads;
+  const int c0 = part * (VD / PARTS) + lane * CPL;
+  const float* base = a.ws_acc + (size_t)pair * S * VD + c0;
+  float v[SPEC > 0 ? SPEC : 1][CPL];
+#pragma unroll
+  for (int k = 0; k < SPEC; ++k)
+    if (k < S) load_channels<CPL>(base + (size_t)k * VD, v[k]);
+  float mk = kNegInf, lk = 0.0f;
+  if (lane < S) {
+    const float2 q = reinterpret_cast<const float2*>(a.ws_ml)[(size_t)pair * S + lane];
+    mk = q.x;
+    lk = q.y;
+  }
+  float M = mk;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+  const float w = (mk == kNegInf) ? 0.0f : expf(mk - M);
+  float L = w * lk;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) L += __shfl_xor(L, off);
+  const uint64_t nz = __ballot(w != 0.0f);
+  const int n = nz ? 64 - __builtin_clzll(nz) : 0;
+  float o[CPL];
+#pragma unroll
+  for (int j = 0; j < CPL; ++j) o[j] = 0.0f;
+#pragma unroll
+  for (int k = 0; k < SPEC; ++k) {
+    if (k < n) {
+      const float wk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), k));
+      if (wk != 0.0f) {
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) o[j] += wk * v[k][j];
+      }
+    }
+  }
+  constexpr int NB = CPL <= 2 ? 32 : 16;  // partial loads per batch
+  for (int k0 = SPEC; k0 < n; k0 += NB) {
+    float u[NB][CPL];
+#pragma unroll
+    for (int i = 0; i < NB; ++i)
+      if (k0 + i < n) load_channels<CPL>(base + (size_t)(k0 + i) * VD, u[i]);
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      if (k0 + i < n) {
+        const float wk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), k0 + i));
+        if (wk != 0.0f) {
+#pragma unroll
+          for (int j = 0; j < CPL; ++j) o[j] += wk * u[i][j];
+        }
       }
     }
   }
@@ -2665,14 +2777,20 @@ hipError_t split_occupancy(const Variant& v, int* ctas_per_cu) {
 template <int VD, bool F32>
 static hipError_t launch_combine_t(const CombineArgs& a, hipStream_t stream) {
   const int pairs = a.rows * a.heads;
-  // measured on MI355X: the wave-per-pair combine wins up to 8 splits, and up
-  // to 16 once there are enough pairs to fill the chip with its small CTAs
+  // measured on MI355X: a wave per pair wins up to 8 splits, up to 16 once
+  // there are enough pairs to fill the chip with its small CTAs, and for any
+  // split count from 1024 pairs (C3 with 8 tokens per row: 4096 pairs, 28
+  // splits, step 79.3 -> 70.5 us); with fewer pairs and more splits one CTA per
+  // pair pulls its partials in fewer dependent rounds (C2: 64 splits, 6.6
+  // against 8.5 us or more)
   constexpr int PARTS = VD > 256 ? 2 : 1;  // waves per pair
   const int ctas = (pairs * PARTS + 3) / 4;
   if (a.num_splits <= 8)
     hipLaunchKernelGGL((combine_small_kernel<VD, F32, 8, PARTS>), dim3(ctas), dim3(256), 0, stream, a);
   else if (a.num_splits <= 16 && VD <= 256 && pairs >= 512)
-    hipLaunchKernelGGL((combine_small_kernel<VD, F32, 16, PARTS>), dim3(ctas), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((combine_wave_kernel<VD, F32, PARTS, 16>), dim3(ctas), dim3(256), 0, stream, a);
+  else if (pairs >= 1024)
+    hipLaunchKernelGGL((combine_wave_kernel<VD, F32, PARTS, 8>), dim3(ctas), dim3(256), 0, stream, a);
   else
     hipLaunchKernelGGL((combine_kernel<VD, F32>), dim3(pairs), dim3(combine_threads<VD>()), 0, stream, a);
   return hipGetLastError();

@@ -382,9 +382,10 @@ def test_live_balanced_row_counts(rows, kpc):
     ("i8", 24, 2, 256, 256, "separate"), ("fp8", 16, 1, 576, 512, "latent")])
 @pytest.mark.parametrize("out_dtype", ["f16", "f32"])
 def test_combine_many_live_balanced_splits(cache, heads, kvh, D, VD, lay, out_dtype):
-    """The CTA-per-pair combine with more splits than it reads speculatively
-    (rows of up to 64 live-balanced splits, where the slots past 16 are read
-    only when their weight is nonzero), for every value-head size, against
+    """The combine with more splits than it reads speculatively (rows of up
+    to 64 live-balanced splits; 512-2048 pairs: the CTA-per-pair combine,
+    whose slots past 16 are read only when their weight is nonzero, and from
+    1024 pairs the wave-per-pair one), for every value-head size, against
     the oracle; paged_decode_attention equals partials + split_combine."""
     cap = 1024
     rows = 32
@@ -403,6 +404,40 @@ def test_combine_many_live_balanced_splits(cache, heads, kvh, D, VD, lay, out_dt
     assert g.target_ctas > 0 and g.num_splits == 64
     tol = dict(max_abs=1e-3, mean_abs=1e-4) if out_dtype == "f32" else {}
     assert_close_to_oracle(got, lse, ref, ref_lse, what=f"{VD} channels {out_dtype}", **tol)
+    b, lb, _ = run_gpu(inp, out_dtype=out_dtype, geometry=g, partials_then_combine=True)
+    assert np.array_equal(got, b) and np.array_equal(lse, lb)
+
+
+@pytest.mark.parametrize("cache,heads,kvh,D,VD,lay,rows,S,balance", [
+    ("i8", 24, 2, 256, 256, "separate", 48, 64, 1),     # 1152 pairs, 16-split batches
+    ("fp8", 16, 1, 576, 512, "latent", 64, 40, 1),      # two waves per pair
+    ("f16", 32, 8, 128, 128, "separate", 16, 16, 1),    # 512 pairs, S <= 16: all speculative
+    ("f16", 64, 8, 64, 64, "separate", 16, 12, 1),
+    ("f16", 32, 8, 128, 128, "separate", 32, 48, 2)])   # static decomposition
+@pytest.mark.parametrize("out_dtype", ["f16", "f32"])
+def test_combine_wave_per_pair(cache, heads, kvh, D, VD, lay, rows, S, balance, out_dtype):
+    """The wave-per-pair combine (at most 16 splits from 512 pairs, any
+    split count from 1024): rows with no position, one position, one split
+    and all S splits, with the loads past the speculated splits taken in
+    batches up to the last split with a weight; against the oracle, and
+    paged_decode_attention equals partials + split_combine."""
+    cap = 1024
+    rng = np.random.default_rng(rows + S + D)
+    lens = rng.integers(0, cap, size=rows, endpoint=True)
+    lens[:5] = [cap, 0, 1, 16, cap - 17]
+    quant = "none" if cache == "f16" else "tensor"
+    p = Problem(rows=rows, heads=heads, kv_heads=kvh, head_size=D, v_head_size=VD, block_size=16,
+                max_blocks_per_row=cap // 16, num_pool_blocks=0, cache_dtype=cache,
+                k_quant=quant, v_quant=quant, layout=lay)
+    inp = workloads.make_inputs(p, 70 + D, lens, with_sink=True, softmax_scale=1.0 / np.sqrt(D))
+    ref, ref_lse = oracle.paged_decode(inp)
+    announce(f"wave combine, {cache} {VD} channels, {rows * heads} pairs, S={S}, {out_dtype}")
+    geo = dict(num_cus=256, ctas_per_cu=8, balance=balance, splits_override=S, min_chunk=16,
+               kv_heads_per_cta=1)
+    got, lse, g = run_gpu(inp, out_dtype=out_dtype, **geo)
+    assert g.num_splits == S and (g.target_ctas > 0) == (balance == 1)
+    tol = dict(max_abs=1e-3, mean_abs=1e-4) if out_dtype == "f32" else {}
+    assert_close_to_oracle(got, lse, ref, ref_lse, what=f"{VD} channels S={S} {out_dtype}", **tol)
     b, lb, _ = run_gpu(inp, out_dtype=out_dtype, geometry=g, partials_then_combine=True)
     assert np.array_equal(got, b) and np.array_equal(lse, lb)
 
