@@ -111,3 +111,19 @@ def test_continuous_batching_workload_with_window_and_cap():
     got, lse, g = run_gpu(inp)
     mx, mn = assert_close_to_oracle(got, lse, ref, ref_lse, what="C3 window+cap")
     announce(f"C3 window: S={g.num_splits} max_abs={mx:.2e} mean_abs={mn:.2e}")
+
+
+@pytest.mark.parametrize("cache,D", [("f16", 128), ("i8", 64)], ids=lambda v: str(v))
+@pytest.mark.parametrize("heads,kvh", [(32, 8), (80, 4)])
+@pytest.mark.parametrize("W,cap", [(20, 0.0), (100, 2.0), (0, 30.0)])
+def test_window_and_cap_with_four_kv_heads_per_cta(cache, D, heads, kvh, W, cap):
+    """The window and the cap in the four-KV-head kernel, with one head block
+    per wave (group 4) and two (group 20), both decompositions."""
+    inp = _with(_small(cache, D, D, "separate", False, seed=13, heads=heads, kvh=kvh),
+                window=W, softcap=cap)
+    ref, ref_lse = oracle.paged_decode(inp)
+    for geo in (dict(splits_override=3, min_chunk=16), dict(balance=1)):
+        announce(f"four KV heads per CTA, {cache} D={D} {heads}q/{kvh}kv window {W} cap {cap} {geo}")
+        got, lse, g = run_gpu(inp, kv_heads_per_cta=4, **geo)
+        assert g.kv_heads_per_cta == 4
+        assert_close_to_oracle(got, lse, ref, ref_lse, what=f"{cache} {heads}q W={W} cap={cap} {geo}")
