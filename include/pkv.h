@@ -229,10 +229,12 @@ typedef struct {
  * shorter splits.  P and the KV bytes are those of a work unit (four KV
  * heads in the four-head mode).  waves: 2 in the live-balanced mode with
  * one KV head per CTA when 2 P is less than the KV bytes of min_chunk
- * positions, else 1.  With 17-32 slots per KV head in the four-head mode:
- * ctas_per_cu defaults to 1, min_chunk to the quarter rule alone, and in the
- * live-balanced mode target = resident - units when units <= resident / 2
- * (so that the rounded per-row split counts fit one round).
+ * positions, else 1.  In the several-KV-head mode with query_tokens > 1 or
+ * 17-32 slots per KV head: ctas_per_cu defaults to 1 (except for 17-32
+ * slots over a one-byte cache), and in the live-balanced mode target =
+ * resident - units when units <= resident / 2 (so that the rounded per-row
+ * split counts fit one round); with 17-32 slots min_chunk follows the
+ * quarter rule alone, on the KV bytes the positions would take in FP16.
  * Returns PKV_EINVAL / PKV_EUNSUPPORTED as paged_decode_attention would, or
  * PKV_EHIP if the device query fails.  Does not touch device memory.
  */

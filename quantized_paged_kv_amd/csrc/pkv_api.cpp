@@ -513,21 +513,29 @@ pkv_status split_geometry(const pkv_problem* problem, const pkv_geometry_opts* o
   // sum cannot reach 2^31)
   const bool balanced = balance_fits(p) &&
                         (o.balance == 1 || (o.balance == 0 && p.num_rows >= kMinBalancedRows));
-  // Two head blocks per wave (17-32 head slots per KV head): one CTA per CU
-  // (its four waves already carry twice the scores and accumulators), all
-  // CTAs resident in one round (see target below) and the quarter-partial
-  // chunk floor -- measured on MI355X with C3's lengths: 8 tokens per row
-  // 92.5 -> 79.2 us, 32 query heads per KV head 53.8 -> 46.4 us, 20 query
-  // heads 50.2 -> 41.7 us against one KV head per CTA; two CTAs per CU, a
-  // partial second round or the eighth-partial floor left tails.
+  // Several KV heads per CTA with several query tokens per row, or with two
+  // head blocks per wave (17-32 head slots per KV head): all CTAs resident
+  // in one round (see target below), one CTA per CU (FP16 caches, and any
+  // cache with one head block), and for two head blocks the quarter-partial
+  // chunk floor on FP16-sized KV bytes.  Measured on MI355X with C3's
+  // lengths against the plain four-KV-head geometry (two CTAs per CU): 2, 3
+  // and 4 tokens per row 63.8 -> 61.3, 66.8 -> 63.4, 68.7 -> 64.5 us, INT8
+  // with 4 tokens 48.6 -> 45.9 us; against one KV head per CTA: 8 tokens
+  // 92.5 -> 79.2 us, 32 query heads per KV head 53.8 -> 46.4 us, 20 heads
+  // 50.2 -> 41.7 us (two CTAs per CU, a partial second round or the
+  // eighth-partial floor left tails; with one token per row C3 itself gains
+  // nothing from it).  With two head blocks and one-byte codes two CTAs per
+  // CU measured faster (C3 with 8 tokens, INT8: 56.2 against 67.1 us).
   const bool two_blocks = var.vb == 2;
+  const bool one_round = var.kvp > 0 && (two_blocks || var.mt);
+  const bool one_per_cu = one_round && (!two_blocks || p.cache_dtype == PKV_F16);
   int cus = o.num_cus, occ = o.ctas_per_cu;
   if (cus == 0 || occ == 0) {
     int qc = 0, qo = 0;
     st = device_numbers(var, &qc, occ == 0 ? &qo : nullptr);
     if (st != PKV_OK) return st;
     if (cus == 0) cus = qc;
-    if (occ == 0) occ = two_blocks ? 1 : qo;
+    if (occ == 0) occ = one_per_cu ? 1 : qo;
   }
   // Live-balanced mode: about two rounds of CTAs per resident slot let the
   // dispatcher even out what per-row rounding leaves (measured on MI355X),
@@ -547,18 +555,19 @@ pkv_status split_geometry(const pkv_problem* problem, const pkv_geometry_opts* o
   // every CU a CTA; else at most a quarter while it still fills a quarter
   // of the resident CTAs; else 64 (a small step is bound by latency, and
   // more, shorter splits finish sooner).  With two head blocks per wave: at
-  // most a quarter, always.
+  // most a quarter of the bytes the positions would take in FP16, always.
   int min_chunk = o.min_chunk;
   if (min_chunk == 0) {
     min_chunk = 64;
-    auto floor_for = [&](int64_t frac) {
+    auto floor_for = [&](int64_t frac, int64_t rb) {
       int64_t c = 16;
-      while (c < ceil_div(frac * partial_bytes, row_bytes)) c *= 2;
+      while (c < ceil_div(frac * partial_bytes, rb)) c *= 2;
       return std::min<int64_t>(c, 1 << 20);
     };
-    const int64_t c8 = floor_for(8), c4 = floor_for(4);
+    const int64_t c8 = floor_for(8, row_bytes), c4 = floor_for(4, row_bytes);
     if (two_blocks)
-      min_chunk = (int)std::max<int64_t>(min_chunk, c4);
+      min_chunk = (int)std::max<int64_t>(
+          min_chunk, floor_for(4, row_bytes * (p.cache_dtype == PKV_F16 ? 1 : 2)));
     else if (c8 > min_chunk && units * ceil_div(cap, c8) >= (int64_t)cus)
       min_chunk = (int)c8;
     else if (c4 > min_chunk && units * ceil_div(cap, c4) * 4 >= (int64_t)cus * occ)
@@ -571,8 +580,8 @@ pkv_status split_geometry(const pkv_problem* problem, const pkv_geometry_opts* o
                               : (balanced && cheap_partials && kv_per_cta == 1 ? 2 : 1);
   int64_t target = (int64_t)waves * cus * occ;
   // (per-row rounding adds at most one CTA per unit to the live-balanced
-  // count: with two head blocks, leave that room in the round)
-  if (two_blocks && balanced && 2 * units <= target) target -= units;
+  // count: in the one-round cases above, leave that room in the round)
+  if (one_round && balanced && 2 * units <= target) target -= units;
   int S;
   if (o.splits_override > 0) {
     S = o.splits_override;

@@ -364,6 +364,12 @@ def test_query_tokens_geometry_and_limits():
     p = pkv.make_problem(16, 32, 8, 128, 128, 16, 512, 5000, query_tokens=4)
     g = pkv.split_geometry(p, num_cus=256, ctas_per_cu=2)
     assert g.head_blocks == 1 and g.kv_heads_per_cta == 4  # 4 tokens x 4 heads = 16
+    # several tokens per row: every CTA of the live-balanced count fits one
+    # round (room for one rounding CTA per unit)
+    assert g.target_ctas == 256 * 2 - 16 * 2 and g.grid_x <= 256 * 2
+    g1 = pkv.split_geometry(pkv.make_problem(16, 32, 8, 128, 128, 16, 512, 5000), num_cus=256,
+                            ctas_per_cu=2)
+    assert g1.target_ctas == 256 * 2  # one token: the plain target
     assert g.workspace_bytes == 16 * 4 * 32 * g.num_splits * (128 + 2) * 4
     p8 = pkv.make_problem(16, 32, 8, 128, 128, 16, 512, 5000, query_tokens=8)
     g8 = pkv.split_geometry(p8, num_cus=256, ctas_per_cu=2)
