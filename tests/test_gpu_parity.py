@@ -27,7 +27,7 @@ def named(name):
 # the five workloads at full size, default geometry (the bench configuration)
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("name", ["C1", "C2", "C3", "C4", "C5", "C2b8"])
+@pytest.mark.parametrize("name", ["C1", "C2", "C3", "C4", "C5", "C2b8", "C4r1"])
 def test_workload_parity(name):
     inp, (ref, ref_lse) = named(name)
     announce(f"{name} default geometry")

@@ -398,16 +398,17 @@ def c3_tokens(T: int, seed: int = 3) -> Inputs:
                             f"U[512,8192], 32q/8kv, head 128, block 16, head sink")
 
 
-def c4(seed: int = 4) -> Inputs:
+def c4(seed: int = 4, rows: int = 8) -> Inputs:
     rng = np.random.default_rng(seed + 1000)
     ctx, k = 32768, 2048
-    cand = sorted_subsets(rng, 8, ctx, k)
-    p = Problem(rows=8, heads=24, kv_heads=2, head_size=256, v_head_size=256, block_size=16,
+    cand = sorted_subsets(rng, rows, ctx, k)
+    p = Problem(rows=rows, heads=24, kv_heads=2, head_size=256, v_head_size=256, block_size=16,
                 max_blocks_per_row=ctx // 16, num_pool_blocks=0, max_candidates=k,
                 cache_dtype="i8", k_quant="channel", v_quant="channel")
     return make_inputs(p, seed, ctx, softmax_scale=0.0625, q_std=1.4, candidates=cand,
                        code_std=40.0, shared_table=True,
-                       name="C4 INT8 per-channel dynamic-sparse: 8 rows, 24q/2kv, head 256, context 32768, 2048 candidates")
+                       name=f"C4 INT8 per-channel dynamic-sparse: {rows} row{'s' if rows > 1 else ''}, 24q/2kv, "
+                            "head 256, context 32768, 2048 candidates")
 
 
 def c5(seed: int = 5) -> Inputs:
@@ -455,6 +456,7 @@ WORKLOADS = {"C1": c1, "C2": c2, "C3": c3, "C4": c4, "C5": c5,
              **{f"X{c}b{b}{d}": (lambda seed=7, c=c, b=b, d=d: paged_quantized(c, b, d, seed))
                 for c, b in ((1024, 32), (4096, 8), (4096, 32), (16384, 8), (16384, 32))
                 for d in ("i8", "fp8")},
+             "C4r1": lambda seed=4: c4(seed, rows=1),
              "C3t4": lambda seed=3: c3_tokens(4, seed),
              "C3t4rows": lambda seed=3: expand_query_tokens(c3_tokens(4, seed)),
              "C3t8": lambda seed=3: c3_tokens(8, seed),
