@@ -185,10 +185,11 @@ typedef struct {
  *         query_tokens * group, the (token, head) slots of a KV head);
  *         kv_heads_per_cta is 4 when the problem allows it (dense rows, SEPARATE
  *         layout, a multiple of four KV heads, head size <= 128, slots <= 16 --
- *         or slots <= 32 with an FP16 cache: the cache keeps the KV heads of a
- *         token side by side, and a CTA whose four waves read four
- *         neighbouring heads of the same records streams faster than four CTAs
- *         reading one head each) and opts do not ask for 1;
+ *         or slots <= 32 with an FP16 cache or query_tokens > 1: the cache
+ *         keeps the KV heads of a token side by side, and a CTA whose four
+ *         waves read four neighbouring heads of the same records streams
+ *         faster than four CTAs reading one head each) and opts do not ask
+ *         for 1;
  * cap   = max_blocks_per_row * block_size (dense; with a sliding window W
  *         at most W + 15, the positions from the window start rounded down
  *         to a multiple of 16) or max_candidates (gathered);

@@ -495,12 +495,13 @@ pkv_status split_geometry(const pkv_problem* problem, const pkv_geometry_opts* o
                 o.kv_heads_per_cta, o.kv_heads_per_cta);
   // (automatic for head sizes up to 128: measured faster there; larger
   // heads need more registers per wave than two waves per SIMD allow.  With
-  // 17-32 head slots per KV head only for FP16 caches: with one-byte codes
-  // the KV bytes per position halve while a split's partial does not, and
-  // one KV head per CTA with fewer splits measured faster -- C3's lengths,
-  // INT8, 8 tokens per row: 59.3 us against 63.3 at best)
+  // 17-32 head slots per KV head: for FP16 caches, and for one-byte codes
+  // with several query tokens per row -- C3's lengths, 8 tokens: INT8 56.2
+  // against 59.7 us, FP8 54.5 against 58.1 -- but not for one-byte codes
+  // with one token and 20 or 32 query heads per KV head, where one KV head
+  // per CTA stayed faster: 36.3 against 37.0 us, 38.5 against 39.9)
   const bool auto_kvp = kvp_allowed(p, pkv::kKvHeadsPerCta) && p.head_size <= 128 &&
-                        (vgroup_of(p) <= 16 || p.cache_dtype == PKV_F16);
+                        (vgroup_of(p) <= 16 || p.cache_dtype == PKV_F16 || qtok_of(p) > 1);
   const int kv_per_cta = o.kv_heads_per_cta ? o.kv_heads_per_cta : (auto_kvp ? pkv::kKvHeadsPerCta : 1);
   const pkv::Variant var = variant_for(p, kv_per_cta);
   const int64_t units = std::max<int64_t>(1, (int64_t)p.num_rows * units_row_of(p, kv_per_cta));
@@ -525,7 +526,8 @@ pkv_status split_geometry(const pkv_problem* problem, const pkv_geometry_opts* o
   // 50.2 -> 41.7 us (two CTAs per CU, a partial second round or the
   // eighth-partial floor left tails; with one token per row C3 itself gains
   // nothing from it).  With two head blocks and one-byte codes two CTAs per
-  // CU measured faster (C3 with 8 tokens, INT8: 56.2 against 67.1 us).
+  // CU measured faster (C3 with 8 tokens, INT8: 56.2 against 67.1 us; FP8,
+  // whose kernel fits three per CU: 54.5 against 61.3 us at three).
   const bool two_blocks = var.vb == 2;
   const bool one_round = var.kvp > 0 && (two_blocks || var.mt);
   const bool one_per_cu = one_round && (!two_blocks || p.cache_dtype == PKV_F16);
@@ -535,7 +537,7 @@ pkv_status split_geometry(const pkv_problem* problem, const pkv_geometry_opts* o
     st = device_numbers(var, &qc, occ == 0 ? &qo : nullptr);
     if (st != PKV_OK) return st;
     if (cus == 0) cus = qc;
-    if (occ == 0) occ = one_per_cu ? 1 : qo;
+    if (occ == 0) occ = one_per_cu ? 1 : (two_blocks ? std::min(qo, 2) : qo);
   }
   // Live-balanced mode: about two rounds of CTAs per resident slot let the
   // dispatcher even out what per-row rounding leaves (measured on MI355X),

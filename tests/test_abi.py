@@ -383,11 +383,15 @@ def test_query_tokens_geometry_and_limits():
     # quarter of the KV bytes it covers (4 KV heads x 512 bytes a position)
     assert g8.target_ctas == 256 * 2 - 16 * 2 and g8.grid_x <= 256 * 2
     assert g8.min_chunk == 256
-    # automatic only for FP16 caches: one-byte codes keep one KV head per CTA
+    # automatic for one-byte caches only with several tokens per row: one
+    # token with 32 query heads per KV head keeps one KV head per CTA
     p8i = pkv.make_problem(16, 32, 8, 128, 128, 16, 512, 5000, query_tokens=8, cache_dtype="i8",
                            k_quant="tensor", v_quant="tensor")
-    assert pkv.split_geometry(p8i, num_cus=256, ctas_per_cu=2).kv_heads_per_cta == 1
-    assert pkv.split_geometry(p8i, num_cus=256, ctas_per_cu=2, kv_heads_per_cta=4).kv_heads_per_cta == 4
+    assert pkv.split_geometry(p8i, num_cus=256, ctas_per_cu=2).kv_heads_per_cta == 4
+    p32i = pkv.make_problem(16, 128, 4, 128, 128, 16, 512, 5000, cache_dtype="i8",
+                            k_quant="tensor", v_quant="tensor")
+    assert pkv.split_geometry(p32i, num_cus=256, ctas_per_cu=2).kv_heads_per_cta == 1
+    assert pkv.split_geometry(p32i, num_cus=256, ctas_per_cu=2, kv_heads_per_cta=4).kv_heads_per_cta == 4
     g81 = pkv.split_geometry(p8, num_cus=256, ctas_per_cu=2, kv_heads_per_cta=1)
     assert g81.head_blocks == 2 and g81.kv_heads_per_cta == 1
     assert g81.grid_x == min(16 * 16 * g81.num_splits, g81.target_ctas + 16 * 16)
