@@ -448,3 +448,74 @@ def test_binding_rejects_tensors_smaller_than_the_problem():
         pkv._check_extents(p, lse_out=DeviceStub(4 * 8, 4))
     with pytest.raises(ValueError, match="device"):
         pkv._check_extents(p, query=torch.empty((12, 8, 64), dtype=torch.float16))
+
+
+def _ceil(a, b):
+    return -(-a // b)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_geometry_invariants_on_random_dense_problems(seed):
+    """Random dense problems (head sizes, groups, query tokens, quantisation,
+    row counts on both sides of the live-balanced range, caller CU counts and
+    occupancies, automatic or explicit KV heads per CTA): the geometry stays
+    within its documented bounds, and for random live lengths the
+    live-balanced split counts n_r = clamp(ceil(npos_r / c), 1, S) never ask
+    for more work items than the grid holds, so every item has a CTA."""
+    import numpy as np
+
+    rng = np.random.default_rng(seed)
+    checked = 0
+    for _ in range(300):
+        D = int(rng.choice([64, 128, 256]))
+        kvh = int(rng.choice([1, 2, 4, 8, 12, 16]))
+        group = int(rng.choice([1, 2, 4, 5, 8, 12, 16, 20, 32]))
+        T = int(rng.choice([1, 1, 1, 2, 3, 4, 8]))
+        if T * group > 64:
+            continue
+        rows = int(rng.choice([1, 5, 16, 33, 64, 200, 1024, 1500]))
+        B = int(rng.choice([16, 32, 64]))
+        mbpr = int(rng.integers(1, 300))
+        dtype = str(rng.choice(["f16", "i8", "fp8"]))
+        quant = "none" if dtype == "f16" else str(rng.choice(["tensor", "channel"]))
+        p = pkv.make_problem(rows, kvh * group, kvh, D, D, B, mbpr, 5000, cache_dtype=dtype,
+                             k_quant=quant, v_quant=quant, query_tokens=T)
+        cus = int(rng.choice([64, 256, 304]))
+        occ = int(rng.integers(1, 9))
+        kpc = int(rng.choice([0, 0, 1, 4, 8]))
+        try:
+            g = pkv.split_geometry(p, num_cus=cus, ctas_per_cu=occ, kv_heads_per_cta=kpc)
+        except pkv.PkvError as e:
+            # only an explicit several-heads request the problem cannot take
+            assert kpc in (4, 8) and e.status == 2, (str(e), kpc)
+            continue
+        cap = mbpr * B
+        slots = T * group
+        assert 1 <= g.num_splits <= 64 and g.num_splits <= _ceil(cap, 16)
+        assert g.min_chunk >= 16 and g.min_chunk % 16 == 0
+        assert g.head_blocks == _ceil(slots, 16)
+        k = g.kv_heads_per_cta
+        assert k in (1, 4, 8) and (kpc == 0 or k == kpc)
+        if k > 1:
+            assert kvh % k == 0 and (slots <= 16 or (k == 4 and slots <= 32 and D <= 128))
+            assert g.threads == 64 * k
+            units_row = kvh // k
+        else:
+            units_row = kvh * g.head_blocks
+        units = rows * units_row
+        S = g.num_splits
+        assert g.workspace_bytes == rows * T * kvh * group * S * (D + 2) * 4
+        if g.target_ctas > 0:
+            assert g.grid_x == min(units * S, g.target_ctas + units)
+            for _ in range(3):
+                npos = rng.integers(0, cap + 1, size=rows)
+                if rng.random() < 0.3:
+                    npos[:] = cap
+                work = int(npos.sum()) * units_row
+                c = max(g.min_chunk, _ceil(_ceil(work, g.target_ctas), 16) * 16)
+                n = np.clip(-(-npos // c), 1, S)
+                assert int(n.sum()) * units_row <= g.grid_x
+        else:
+            assert g.grid_x == units * S
+        checked += 1
+    assert checked > 100
