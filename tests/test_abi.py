@@ -519,3 +519,31 @@ def test_geometry_invariants_on_random_dense_problems(seed):
             assert g.grid_x == units * S
         checked += 1
     assert checked > 100
+
+
+def test_plain_c_consumer_compiles_links_and_agrees(tmp_path):
+    """include/pkv.h is a C header: a C11 program (tests/c_consumer.c) built
+    with gcc -std=c11 -pedantic -Werror links libpkv.so, and the geometry it
+    prints equals the binding's for the same problem; a rejected problem
+    reports its status, name and message through the C entry points."""
+    import shutil
+    import subprocess
+
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("no C compiler")
+    libdir = os.path.dirname(pkv.LIB_PATH)
+    exe = str(tmp_path / "c_consumer")
+    subprocess.run([gcc, "-std=c11", "-Wall", "-Wextra", "-Werror", "-pedantic",
+                    "-I", os.path.join(ROOT, "include"), os.path.join(ROOT, "tests", "c_consumer.c"),
+                    "-L", libdir, "-lpkv", f"-Wl,-rpath,{libdir}", "-o", exe], check=True)
+    out = subprocess.run([exe], check=True, capture_output=True, text=True).stdout
+    got = dict(line.split("=", 1) for line in out.strip().splitlines())
+    g = pkv.split_geometry(pkv.make_problem(16, 32, 8, 128, 128, 16, 512, 5000), num_cus=256,
+                           ctas_per_cu=2)
+    for key in ("num_splits", "min_chunk", "threads", "head_blocks", "grid_x", "target_ctas",
+                "kv_heads_per_cta", "workspace_bytes"):
+        assert int(got[key]) == int(getattr(g, key)), key
+    assert int(got["status"]) == 0 and int(got["bad_status"]) == 1
+    assert got["bad_name"].startswith("PKV_EINVAL")
+    assert "num_heads (30) is not a multiple of num_kv_heads (8)" in got["bad_message"]
