@@ -201,6 +201,8 @@ typedef struct {
  *   unit of work is a 64-candidate tile; tiles-per-split is the smallest
  *   power of two for which ceil(tiles / tps) * units <= waves * resident;
  *   S = min(ceil(tiles / tps), max_splits).
+ * With the automatic split count and min_chunk, rows of at most 256
+ * positions (cap <= 256) take S = 1: one launch with the direct output.
  * A positive splits_override replaces the automatic count (then clipped to
  * [1, max_splits] and to ceil(cap / 16)).
  * On the device (graph safe, from live data): with target_ctas > 0 every CTA

@@ -30,6 +30,8 @@ using pkv::kMaxBalancedRows;
 // Fewer rows than this: the static decomposition (its first block reads do
 // not wait for the live lengths, which matters more than balance there).
 constexpr int kMinBalancedRows = 16;
+// Rows of at most this many positions take one split (see split_geometry).
+constexpr int64_t kOneSplitCap = 256;
 
 bool aligned(const void* p, size_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
 
@@ -601,6 +603,13 @@ pkv_status split_geometry(const pkv_problem* problem, const pkv_geometry_opts* o
       S = (int)std::min<int64_t>(ceil_div(want, units), ceil_div(cap, min_chunk));
     }
   }
+  // Short rows take one split (with the automatic split count and chunk
+  // floor): at most 256 positions per row is four 16-token tiles per wave of
+  // a CTA, and one launch with the direct output beats the split kernel plus
+  // the combine's second launch (measured on MI355X with one row, 4q/1kv,
+  // head 64: 128 positions 4.5 against 5.7 us at 2 splits, 256 positions
+  // 5.3 against 6.1 at 4; at 512 positions 8 splits win, 6.6 against 7.1).
+  if (o.splits_override == 0 && o.min_chunk == 0 && cap <= kOneSplitCap) S = 1;
   S = std::max(1, std::min(S, max_splits));
   S = std::max(1, std::min<int>(S, ceil_div(cap, 16)));
 

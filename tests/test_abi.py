@@ -547,3 +547,21 @@ def test_plain_c_consumer_compiles_links_and_agrees(tmp_path):
     assert int(got["status"]) == 0 and int(got["bad_status"]) == 1
     assert got["bad_name"].startswith("PKV_EINVAL")
     assert "num_heads (30) is not a multiple of num_kv_heads (8)" in got["bad_message"]
+
+
+def test_short_rows_take_one_split():
+    """Rows of at most 256 positions take one split with the automatic split
+    count and chunk floor (one launch, direct output); longer rows, or an
+    explicit min_chunk or split count, keep the split rule."""
+    def geo(mbpr, **kw):
+        p = pkv.make_problem(1, 4, 1, 64, 64, 16, mbpr, 64)
+        return pkv.split_geometry(p, num_cus=256, ctas_per_cu=2, **kw)
+
+    assert geo(16).num_splits == 1      # 256 positions
+    assert geo(8).num_splits == 1       # 128
+    assert geo(32).num_splits > 1       # 512
+    assert geo(16, min_chunk=64).num_splits == 4
+    assert geo(16, splits_override=4).num_splits == 4
+    # a sliding window bounds a row's positions too (W + 15)
+    pw = pkv.make_problem(1, 4, 1, 64, 64, 16, 64, 64, sliding_window=200)
+    assert pkv.split_geometry(pw, num_cus=256, ctas_per_cu=2).num_splits == 1
