@@ -514,8 +514,8 @@ pkv_status split_geometry(const pkv_problem* problem, const pkv_geometry_opts* o
   if (o.balance < 0 || o.balance > 2) return fail(PKV_EINVAL, "balance must be 0, 1 or 2");
   // (its CTAs sum the live positions of all rows in 32 bits: only when that
   // sum cannot reach 2^31)
-  const bool balanced = balance_fits(p) &&
-                        (o.balance == 1 || (o.balance == 0 && p.num_rows >= kMinBalancedRows));
+  bool balanced = balance_fits(p) &&
+                  (o.balance == 1 || (o.balance == 0 && p.num_rows >= kMinBalancedRows));
   // Several KV heads per CTA with several query tokens per row, or with two
   // head blocks per wave (17-32 head slots per KV head): all CTAs resident
   // in one round (see target below), one CTA per CU (FP16 caches, and any
@@ -577,6 +577,16 @@ pkv_status split_geometry(const pkv_problem* problem, const pkv_geometry_opts* o
     else if (c4 > min_chunk && units * ceil_div(cap, c4) * 4 >= (int64_t)cus * occ)
       min_chunk = (int)c4;
   }
+  // The live-balanced decomposition cannot cut the rows finer than the
+  // static one when even full rows would get the chunk floor (rows x cap x
+  // units per row <= resident CTAs x min_chunk: both then cut every row into
+  // the same min_chunk pieces), and it reads all row lengths before the
+  // first block-id read; so automatic mode takes the static one there
+  // (measured on MI355X, latent C5: 24.4 against 25.3 us; with lengths
+  // U[1024, 4096] 23.9 against 24.1).
+  if (balanced && o.balance == 0 &&
+      (int64_t)p.num_rows * cap * units_row_of(p, kv_per_cta) <= (int64_t)cus * occ * min_chunk)
+    balanced = false;
   const bool cheap_partials = 2 * partial_bytes < row_bytes * min_chunk;
   // (four KV heads per CTA: one round; their CTAs already carry four
   // units' partials, and a second round measured slower)

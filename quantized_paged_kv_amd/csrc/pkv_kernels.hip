@@ -2780,16 +2780,18 @@ static hipError_t launch_combine_t(const CombineArgs& a, hipStream_t stream) {
   // measured on MI355X: a wave per pair wins up to 8 splits, up to 16 once
   // there are enough pairs to fill the chip with its small CTAs, and for any
   // split count from 1024 pairs (C3 with 8 tokens per row: 4096 pairs, 28
-  // splits, step 79.3 -> 70.5 us); with fewer pairs and more splits one CTA per
-  // pair pulls its partials in fewer dependent rounds (C2: 64 splits, 6.6
-  // against 8.5 us or more)
+  // splits, step 79.3 -> 70.5 us) with at least 128 channels; with fewer
+  // pairs and more splits one CTA per pair pulls its partials in fewer
+  // dependent rounds (C2: 64 splits, 6.6 against 8.5 us or more), and at 64
+  // channels (one 4-byte load per lane and split) with its 16-byte loads (the
+  // 16384 x 32 INT8 page shape: 2048 pairs of 64 full splits, 0.6 us ahead)
   constexpr int PARTS = VD > 256 ? 2 : 1;  // waves per pair
   const int ctas = (pairs * PARTS + 3) / 4;
   if (a.num_splits <= 8)
     hipLaunchKernelGGL((combine_small_kernel<VD, F32, 8, PARTS>), dim3(ctas), dim3(256), 0, stream, a);
   else if (a.num_splits <= 16 && VD <= 256 && pairs >= 512)
     hipLaunchKernelGGL((combine_wave_kernel<VD, F32, PARTS, 16>), dim3(ctas), dim3(256), 0, stream, a);
-  else if (pairs >= 1024)
+  else if (pairs >= 1024 && VD >= 128)
     hipLaunchKernelGGL((combine_wave_kernel<VD, F32, PARTS, 8>), dim3(ctas), dim3(256), 0, stream, a);
   else
     hipLaunchKernelGGL((combine_kernel<VD, F32>), dim3(pairs), dim3(combine_threads<VD>()), 0, stream, a);

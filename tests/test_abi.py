@@ -565,3 +565,18 @@ def test_short_rows_take_one_split():
     # a sliding window bounds a row's positions too (W + 15)
     pw = pkv.make_problem(1, 4, 1, 64, 64, 16, 64, 64, sliding_window=200)
     assert pkv.split_geometry(pw, num_cus=256, ctas_per_cu=2).num_splits == 1
+
+
+def test_static_decomposition_when_the_chunk_floor_binds():
+    """Automatic mode takes the static decomposition when even full rows
+    would get the chunk floor (rows x cap x units per row <= resident CTAs x
+    min_chunk): the latent C5 shape (32 rows x 4096, chunk floor 512 for its
+    16 x 512-channel partials); C3's continuous-batching shape stays
+    live-balanced; balance=1 still forces it."""
+    lat = pkv.make_problem(32, 16, 1, 576, 512, 64, 64, 5000, cache_dtype="fp8", k_quant="tensor",
+                           v_quant="tensor", layout="latent")
+    g = pkv.split_geometry(lat, num_cus=256, ctas_per_cu=2)
+    assert g.target_ctas == 0 and g.min_chunk == 512 and g.num_splits == 8
+    assert pkv.split_geometry(lat, num_cus=256, ctas_per_cu=2, balance=1).target_ctas > 0
+    c3 = pkv.make_problem(16, 32, 8, 128, 128, 16, 512, 5000)
+    assert pkv.split_geometry(c3, num_cus=256, ctas_per_cu=2).target_ctas > 0

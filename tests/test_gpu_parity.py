@@ -346,13 +346,15 @@ def _replay_lens(rows, cap, seed):
 @pytest.mark.parametrize("kpc", [0, 8])
 def test_graph_replay_continuous_batching_shape(kpc):
     """C3's shape at a smaller capacity: 16 rows (the live-balanced
-    decomposition, every CTA reading all lengths), 32 query / 8 KV heads,
+    decomposition, asked for, every CTA reading all lengths), 32 query / 8 KV heads,
     head 128, FP16 with a head sink: several KV heads per CTA."""
     cap = 512
     p = Problem(rows=16, heads=32, kv_heads=8, head_size=128, v_head_size=128, block_size=16,
                 max_blocks_per_row=cap // 16, num_pool_blocks=0, cache_dtype="f16")
     inp = workloads.make_inputs(p, 31, cap, with_sink=True, softmax_scale=1 / np.sqrt(128))
-    geo = {"kv_heads_per_cta": kpc} if kpc else {}
+    # (balance asked for: at this capacity the automatic geometry would take
+    # the static decomposition, the chunk floor cutting full rows the same way)
+    geo = {"kv_heads_per_cta": kpc, "balance": 1} if kpc else {"balance": 1}
     g = _replay_with_lengths(inp, _replay_lens(16, cap, 31), f"C3 shape kpc={kpc}", **geo)
     assert g.target_ctas > 0 and g.kv_heads_per_cta == (kpc or 4) and g.num_splits > 1
 
@@ -385,7 +387,8 @@ def test_combine_many_live_balanced_splits(cache, heads, kvh, D, VD, lay, out_dt
     """The combine with more splits than it reads speculatively (rows of up
     to 64 live-balanced splits; 512-2048 pairs: the CTA-per-pair combine,
     whose slots past 16 are read only when their weight is nonzero, and from
-    1024 pairs the wave-per-pair one), for every value-head size, against
+    1024 pairs at 128 or more channels the wave-per-pair one), for every
+    value-head size, against
     the oracle; paged_decode_attention equals partials + split_combine."""
     cap = 1024
     rows = 32
@@ -452,8 +455,9 @@ def test_graph_replay_multitoken_shape(T):
                 max_blocks_per_row=cap // 16, num_pool_blocks=0, cache_dtype="f16",
                 query_tokens=T)
     inp = workloads.make_inputs(p, 33, cap, with_sink=True, softmax_scale=1 / np.sqrt(128))
-    g = _replay_with_lengths(inp, _replay_lens(16, cap, 33), f"C3 shape, {T} tokens per row")
-    assert g.target_ctas > 0 and g.head_blocks == T // 4
+    g = _replay_with_lengths(inp, _replay_lens(16, cap, 33), f"C3 shape, {T} tokens per row",
+                             balance=1, min_chunk=16)
+    assert g.target_ctas > 0 and g.head_blocks == T // 4 and g.num_splits > 1
 
 
 def test_graph_replay_latent_shape():
@@ -466,8 +470,12 @@ def test_graph_replay_latent_shape():
                 max_blocks_per_row=cap // 64, num_pool_blocks=0, cache_dtype="fp8",
                 k_quant="tensor", v_quant="tensor", layout="latent")
     inp = workloads.make_inputs(p, 32, cap, with_sink=True, softmax_scale=1 / 24)
-    g = _replay_with_lengths(inp, _replay_lens(16, cap, 32), "C5 shape")
+    # (asked for: the automatic geometry takes the static decomposition here,
+    # since the chunk floor would cut even full rows the same way)
+    g = _replay_with_lengths(inp, _replay_lens(16, cap, 32), "C5 shape", balance=1)
     assert g.target_ctas > 0 and g.num_splits > 1
+    gs = _replay_with_lengths(inp, _replay_lens(16, cap, 32), "C5 shape, automatic geometry")
+    assert gs.target_ctas == 0 and gs.num_splits > 1
 
 
 # ---------------------------------------------------------------------------
