@@ -225,7 +225,8 @@ typedef struct {
  * Defaults: max_splits 64.  min_chunk: 64, raised to the smallest power of
  * two c for which a split's partial P = group * (v_head_size + 2) * 4 bytes
  * is at most an eighth of the KV bytes of c positions, if the grid then
- * still gives every CU a CTA (units * ceil(cap / c) >= num_cus); else to
+ * still gives every CU a CTA (units * ceil(cap / c) >= num_cus; two CTAs,
+ * >= 2 * num_cus, with several KV heads per CTA); else to
  * the smallest c with P at most a quarter of them, if the grid then still
  * holds a quarter of the resident CTAs (units * ceil(cap / c) * 4 >=
  * resident); else kept at 64 -- a latency-bound step gains from more,

@@ -556,9 +556,11 @@ pkv_status split_geometry(const pkv_problem* problem, const pkv_geometry_opts* o
   // Automatic chunk floor: 64 positions, raised to the power of two that
   // keeps a split's partial (written once, read back once by the combine) at
   // most an eighth of the KV bytes it covers while the grid still gives
-  // every CU a CTA; else at most a quarter while it still fills a quarter
-  // of the resident CTAs; else 64 (a small step is bound by latency, and
-  // more, shorter splits finish sooner).  With two head blocks per wave: at
+  // every CU a CTA (two CTAs with several KV heads per CTA: the PagedAttention
+  // page's 1024 x 32 and 4096 x 8 INT8 shapes 18.5 -> 15.9 and 18.8 -> 16.3
+  // us with the quarter floor below instead); else at most a quarter while it
+  // still fills a quarter of the resident CTAs; else 64 (a small step is
+  // bound by latency, and more, shorter splits finish sooner).  With two head blocks per wave: at
   // most a quarter of the bytes the positions would take in FP16, always.
   int min_chunk = o.min_chunk;
   if (min_chunk == 0) {
@@ -572,7 +574,7 @@ pkv_status split_geometry(const pkv_problem* problem, const pkv_geometry_opts* o
     if (two_blocks)
       min_chunk = (int)std::max<int64_t>(
           min_chunk, floor_for(4, row_bytes * (p.cache_dtype == PKV_F16 ? 1 : 2)));
-    else if (c8 > min_chunk && units * ceil_div(cap, c8) >= (int64_t)cus)
+    else if (c8 > min_chunk && units * ceil_div(cap, c8) >= (int64_t)cus * (kv_per_cta > 1 ? 2 : 1))
       min_chunk = (int)c8;
     else if (c4 > min_chunk && units * ceil_div(cap, c4) * 4 >= (int64_t)cus * occ)
       min_chunk = (int)c4;
