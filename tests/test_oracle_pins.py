@@ -784,3 +784,55 @@ def test_writer_fp16_double_rounding_is_the_stated_reading():
         if found >= 3:
             break
     assert found >= 3
+
+
+# ---------------------------------------------------------------------------
+# several query tokens per row
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("T", [1, 3, 8])
+def test_multitoken_rows_are_causal_attention(T):
+    """Several query tokens per row (the DSA page's decode tests take 1, 3
+    and 8 query rows of one sequence): token j of a row of length len sees
+    the positions [0, len - T + 1 + j) of that row (none when that is not
+    positive), through the row's one block table.  Brute force over the
+    definition, independent of the expansion into separate rows that the
+    GPU tests compare against."""
+    p = Problem(rows=3, heads=4, kv_heads=2, head_size=8, v_head_size=8, block_size=4,
+                max_blocks_per_row=3, num_pool_blocks=0, cache_dtype="i8", k_quant="tensor",
+                v_quant="channel", query_tokens=T)
+    lens = [12, 5, 2]  # full capacity, a row shorter than 8 tokens, one shorter than 3
+    inp = workloads.make_inputs(p, 60 + T, lens, with_sink=True, softmax_scale=0.37)
+    o, l = oracle.paged_decode(workloads.expand_query_tokens(inp), threads=2)
+    K = _decode_cache(inp.key_cache, p.cache_dtype)
+    V = _decode_cache(inp.value_cache, p.cache_dtype)
+    q = inp.query.astype(np.float64)
+    group = p.heads // p.kv_heads
+    cap = p.max_blocks_per_row * p.block_size
+    assert o.shape == (p.rows * T, p.heads, p.v_head_size)
+    for r in range(p.rows):
+        for j in range(T):
+            n = max(0, min(lens[r], cap) - (T - 1 - j))
+            qi = r * T + j
+            for h in range(p.heads):
+                g = h // group
+                ks = _scale(inp.k_scale, p.k_quant, g, p.head_size)
+                vs = _scale(inp.v_scale, p.v_quant, g, p.v_head_size)
+                if n == 0:
+                    assert math.isinf(l[qi, h]) and l[qi, h] < 0 and np.all(o[qi, h] == 0)
+                    continue
+                xs, vrows = [], []
+                for t in range(n):
+                    blk = int(inp.block_table[r, t // p.block_size])
+                    k = K[blk, t % p.block_size, g, :] * ks
+                    xs.append(inp.softmax_scale * math.fsum(q[qi, h, d] * k[d] for d in range(p.head_size)))
+                    vrows.append(V[blk, t % p.block_size, g, :] * vs)
+                m = max(xs)
+                w = [math.exp(x - m) for x in xs]
+                L = math.fsum(w)
+                lse = m + math.log(L)
+                sink = 1.0 / (1.0 + math.exp(float(inp.head_sink[h]) - lse))
+                exp_o = [math.fsum(w[i] * vrows[i][c] for i in range(n)) / L * sink
+                         for c in range(p.v_head_size)]
+                assert abs(l[qi, h] - lse) <= 1e-12 * max(1.0, abs(lse))
+                np.testing.assert_allclose(o[qi, h], exp_o, rtol=1e-12, atol=1e-14)
