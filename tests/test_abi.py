@@ -521,6 +521,77 @@ def test_geometry_invariants_on_random_dense_problems(seed):
     assert checked > 100
 
 
+
+@pytest.mark.parametrize("seed", range(4))
+def test_geometry_invariants_on_random_gathered_and_latent_problems(seed):
+    """Random gathered (candidate-list) and latent problems: one KV head per
+    CTA, the grid and workspace formulas, the split-count bounds, the
+    64-candidate tile rule of gathered rows (S is ceil(tiles / tps) for a
+    power of two tps unless a bound clips it), one split for rows of at most
+    256 positions, and the live-balanced items always fit the grid."""
+    import numpy as np
+
+    rng = np.random.default_rng(500 + seed)
+    checked = 0
+    for _ in range(300):
+        latent = rng.random() < 0.5
+        gathered = (not latent) or rng.random() < 0.5
+        if latent:
+            D, VD, kvh = 576, 512, 1
+            group = int(rng.choice([4, 8, 16, 32, 64]))
+            dtype = str(rng.choice(["f16", "fp8"]))
+            kq, vq = ("none", "none") if dtype == "f16" else ("tensor", "none")
+        else:
+            D = int(rng.choice([64, 128, 256]))
+            VD = D
+            kvh = int(rng.choice([1, 2, 4, 8]))
+            group = int(rng.choice([1, 2, 4, 8, 12, 16, 24, 32]))
+            dtype = str(rng.choice(["f16", "i8", "fp8"]))
+            kq = vq = "none" if dtype == "f16" else str(rng.choice(["tensor", "channel"]))
+        rows = int(rng.choice([1, 5, 16, 33, 64, 200, 1024, 1500]))
+        B = int(rng.choice([16, 32, 64]))
+        mbpr = int(rng.integers(1, 300))
+        nc = int(rng.choice([1, 17, 64, 200, 256, 257, 2048, 5000])) if gathered else 0
+        p = pkv.make_problem(rows, kvh * group, kvh, D, VD, B, mbpr, 5000, max_candidates=nc,
+                             cache_dtype=dtype, k_quant=kq, v_quant=vq,
+                             layout="latent" if latent else "separate")
+        cus = int(rng.choice([64, 256, 304]))
+        occ = int(rng.integers(1, 5))
+        override = int(rng.integers(1, 80)) if rng.random() < 0.3 else 0
+        g = pkv.split_geometry(p, num_cus=cus, ctas_per_cu=occ, splits_override=override,
+                               min_chunk=16 if override else 0)
+        cap = nc if gathered else mbpr * B
+        S = g.num_splits
+        assert g.kv_heads_per_cta == 1
+        assert 1 <= S <= 64 and S <= _ceil(cap, 16)
+        assert g.head_blocks == _ceil(group, 16)
+        assert g.threads == 256
+        units_row = kvh * g.head_blocks
+        units = rows * units_row
+        assert g.workspace_bytes == rows * kvh * group * S * (VD + 2) * 4
+        if override:
+            assert S == min(override, 64, _ceil(cap, 16))
+        elif cap <= 256:
+            assert S == 1
+        elif gathered:
+            tiles = _ceil(nc, 64)
+            clipped = S == min(64, _ceil(cap, 16))
+            assert clipped or any(_ceil(tiles, 1 << k) == S for k in range(0, 20)), (tiles, S)
+        if g.target_ctas > 0:
+            assert g.grid_x == min(units * S, g.target_ctas + units)
+            for _ in range(3):
+                npos = rng.integers(0, cap + 1, size=rows)
+                if rng.random() < 0.3:
+                    npos[:] = cap
+                work = int(npos.sum()) * units_row
+                c = max(g.min_chunk, _ceil(_ceil(work, g.target_ctas), 16) * 16)
+                n = np.clip(-(-npos // c), 1, S)
+                assert int(n.sum()) * units_row <= g.grid_x
+        else:
+            assert g.grid_x == units * S
+        checked += 1
+    assert checked == 300
+
 def test_plain_c_consumer_compiles_links_and_agrees(tmp_path):
     """include/pkv.h is a C header: a C11 program (tests/c_consumer.c) built
     with gcc -std=c11 -pedantic -Werror links libpkv.so, and the geometry it
