@@ -478,6 +478,90 @@ def test_graph_replay_latent_shape():
     assert gs.target_ctas == 0 and gs.num_splits > 1
 
 
+
+@pytest.mark.parametrize("balance,latent", [(1, False), (2, False), (1, True)])
+def test_graph_replay_gathered_rows(balance, latent):
+    """Gathered rows under graph replay: between replays the candidate lists,
+    their live counts and the row lengths change (random lists with invalid
+    entries, empty lists, full sorted lists, lengths cutting lists short).
+    Each replay is bitwise the eager call's and meets the oracle, in the
+    live-balanced decomposition (every CTA sums the live candidate counts)
+    and the static one, on the per-head and the latent kernels."""
+    import torch
+
+    import quantized_paged_kv_amd as pkv
+    from workloads.device import to_device
+
+    rows, cap, nc = 16, 1024, 300
+    if latent:
+        p = Problem(rows=rows, heads=16, kv_heads=1, head_size=576, v_head_size=512,
+                    block_size=64, max_blocks_per_row=cap // 64, num_pool_blocks=0,
+                    max_candidates=nc, cache_dtype="f16", layout="latent")
+    else:
+        p = Problem(rows=rows, heads=24, kv_heads=2, head_size=256, v_head_size=256,
+                    block_size=16, max_blocks_per_row=cap // 16, num_pool_blocks=0,
+                    max_candidates=nc, cache_dtype="i8", k_quant="channel", v_quant="channel")
+    rng = np.random.default_rng(77)
+    cand0 = rng.integers(-3, cap + 3, size=(rows, nc)).astype(np.int32)
+    inp = workloads.make_inputs(p, 77, cap, with_sink=True, candidates=cand0,
+                                num_candidates=np.full(rows, nc),
+                                softmax_scale=1.0 / np.sqrt(p.head_size))
+    d = to_device(inp, "cuda")
+    prob = pkv.make_problem(**d.problem_kwargs)
+    g = pkv.split_geometry(prob, balance=balance)
+    assert (g.target_ctas > 0) == (balance == 1)
+    ws = pkv.workspace_for(g)
+    out = torch.zeros((rows, p.heads, p.v_head_size), dtype=torch.float16, device="cuda")
+    lse = torch.zeros((rows, p.heads), dtype=torch.float32, device="cuda")
+
+    def step():
+        pkv.paged_decode_attention(prob, g, d.query, d.key_cache, d.value_cache, d.block_table,
+                                   d.seq_lens, d.candidates, d.num_candidates, d.k_scale,
+                                   d.v_scale, d.softmax_scale, d.head_sink, out, lse, ws)
+
+    what = f"gathered replay balance={balance} latent={latent}"
+    announce(f"{what}: graph capture (S={g.num_splits}, target_ctas={g.target_ctas})")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    sorted_full = np.sort(np.stack([rng.permutation(cap)[:nc] for _ in range(rows)]), axis=1)
+    steps = [
+        (rng.integers(-3, cap + 3, size=(rows, nc)), rng.integers(0, nc + 1, size=rows),
+         np.full(rows, cap)),
+        (cand0, np.zeros(rows, dtype=np.int64), np.full(rows, cap)),
+        (sorted_full, np.full(rows, nc), np.full(rows, cap)),
+        (sorted_full, np.full(rows, nc), rng.integers(0, cap + 1, size=rows)),
+        (sorted_full, np.where(np.arange(rows) % 2 == 0, 0, nc), np.full(rows, cap)),
+    ]
+    for i, (cand, ncand, lens) in enumerate(steps):
+        d.candidates.copy_(torch.from_numpy(np.ascontiguousarray(cand, dtype=np.int32)))
+        d.num_candidates.copy_(torch.from_numpy(np.asarray(ncand, dtype=np.int32)))
+        d.seq_lens.copy_(torch.from_numpy(np.asarray(lens, dtype=np.int32)))
+        announce(f"{what}: replay {i}")
+        graph.replay()
+        torch.cuda.synchronize()
+        o_graph, l_graph = out.clone(), lse.clone()
+        for _ in range(3):
+            graph.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(o_graph, out) and torch.equal(l_graph, lse)
+        step()
+        torch.cuda.synchronize()
+        assert torch.equal(o_graph, out) and torch.equal(l_graph, lse)
+        ref_inp = Inputs(**{**inp.__dict__, "candidates": np.asarray(cand, dtype=np.int32),
+                            "num_candidates": np.asarray(ncand, dtype=np.int32),
+                            "seq_lens": np.asarray(lens, dtype=np.int32)})
+        ref, ref_lse = oracle.paged_decode(ref_inp)
+        assert_close_to_oracle(o_graph.double().cpu().numpy(), l_graph.double().cpu().numpy(),
+                               ref, ref_lse, what=f"{what} replay {i}")
+
+
 # ---------------------------------------------------------------------------
 # the pages' worked examples (FP32 output)
 # ---------------------------------------------------------------------------
