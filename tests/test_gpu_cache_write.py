@@ -194,3 +194,91 @@ def test_append_then_decode_matches_oracle(cache, quant):
     assert np.array_equal(_bytes(d.value_cache), ref_v.view(np.uint8).reshape(-1))
     assert_close_to_oracle(out.double().cpu().numpy(), lse.double().cpu().numpy(), ref, ref_lse,
                            what="append+decode")
+
+
+@pytest.mark.parametrize("cache,quant", [("i8", "channel"), ("fp8", "tensor")])
+def test_graph_replay_write_then_decode(cache, quant):
+    """A serving loop's step captured once in a HIP graph -- the writer puts
+    each row's newest token at its slot, then the decode attends over the
+    updated cache -- and replayed for four consecutive steps with new tokens,
+    new slots and lengths grown by one.  After every replay the caches are
+    bit-exact the oracle writer's (applied step after step) and the output
+    meets the oracle's decode of them at the usual tolerance.
+
+    The new rows are drawn at a tenth of unit deviation (their tenfold
+    outliers at unit deviation), so the cache stays the unit-variance data
+    the tolerance is stated for: rows at the default deviation saturate at
+    the cache's top code, and keys of that size scale up the logit shift
+    that folding the key scale into the FP16 query allows (2^-11 of
+    scale * sum_d |Q'_d K_d|), which a row of two to five tokens passes on
+    to its output almost undamped."""
+    import dataclasses
+
+    import torch
+
+    import oracle
+    import quantized_paged_kv_amd as pkv
+    from tests.gpu_util import assert_close_to_oracle
+    from workloads.device import problem_kwargs, to_device
+
+    p = Problem(rows=6, heads=16, kv_heads=2, head_size=128, v_head_size=128, block_size=16,
+                max_blocks_per_row=64, num_pool_blocks=1, cache_dtype=cache, k_quant=quant,
+                v_quant=quant)
+    # the next four positions of every row stay in the last block the row
+    # already owns, so the new tokens' slots are the row's own
+    lens = np.array([1, 17, 300, 507, 33, 1000])
+    inp = workloads.make_inputs(p, seed=23, seq_lens=lens)
+    p = inp.problem
+    B, KVH, D = p.block_size, p.kv_heads, p.head_size
+    d = to_device(inp, "cuda")
+    prob = pkv.make_problem(**problem_kwargs(p))
+    g = pkv.split_geometry(prob)
+    ws = pkv.workspace_for(g)
+    out = torch.empty((p.rows, p.heads, p.v_head_size), dtype=torch.float16, device="cuda")
+    lse = torch.empty((p.rows, p.heads), dtype=torch.float32, device="cuda")
+    dkey = torch.zeros((p.rows, KVH, D), dtype=torch.float16, device="cuda")
+    dval = torch.zeros((p.rows, KVH, D), dtype=torch.float16, device="cuda")
+    dslots = torch.full((p.rows,), -1, dtype=torch.int64, device="cuda")
+
+    def step():
+        pkv.reshape_and_cache(prob, dkey, dval, dslots, d.k_scale, d.v_scale, d.key_cache,
+                              d.value_cache)
+        pkv.paged_decode_attention(prob, g, d.query, d.key_cache, d.value_cache, d.block_table,
+                                   d.seq_lens, d.candidates, d.num_candidates, d.k_scale,
+                                   d.v_scale, d.softmax_scale, d.head_sink, out, lse, ws)
+
+    announce(f"graph write+decode {cache} {quant}: capture")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()  # warm-up: every slot is -1, so the writer skips all rows
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    ref_k, ref_v = inp.key_cache.copy(), inp.value_cache.copy()
+    cur = lens.copy()
+    for it in range(4):
+        cur = cur + 1  # the new token's position is cur - 1
+        pos = cur - 1
+        slots = np.array([int(inp.block_table[r, pos[r] // B]) * B + pos[r] % B
+                          for r in range(p.rows)], dtype=np.int64)
+        assert np.all(pos // B < -(-lens // B)) and len(set(slots.tolist())) == p.rows
+        nt = workloads.new_tokens(p, p.rows, seed=30 + it, x_std=0.1, slots=slots)
+        dkey.copy_(_dev(nt.key))
+        dval.copy_(_dev(nt.value))
+        dslots.copy_(_dev(slots))
+        d.seq_lens.copy_(_dev(cur.astype(np.int32)))
+        announce(f"graph write+decode {cache} {quant}: replay {it}")
+        graph.replay()
+        torch.cuda.synchronize()
+        ref_k, ref_v = cache_write.reshape_and_cache(p, nt.key, nt.value, slots, inp.k_scale,
+                                                     inp.v_scale, ref_k, ref_v)
+        assert np.array_equal(_bytes(d.key_cache), ref_k.view(np.uint8).reshape(-1))
+        assert np.array_equal(_bytes(d.value_cache), ref_v.view(np.uint8).reshape(-1))
+        ref_inp = dataclasses.replace(inp, key_cache=ref_k, value_cache=ref_v,
+                                      seq_lens=cur.astype(np.int32))
+        ref, ref_lse = oracle.paged_decode(ref_inp)
+        assert_close_to_oracle(out.double().cpu().numpy(), lse.double().cpu().numpy(), ref,
+                               ref_lse, what=f"write+decode replay {it}")
