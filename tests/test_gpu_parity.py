@@ -163,6 +163,51 @@ def test_edge_lengths(lens):
             assert np.all(got[0] == 0) and np.all(np.isneginf(lse[0]))
 
 
+
+@pytest.mark.parametrize("kind", ["kvp", "per_head", "gathered", "latent", "multitoken"])
+@pytest.mark.parametrize("balance", [1, 2])
+def test_out_of_range_lengths_are_clamped(kind, balance):
+    """Row lengths (and candidate counts) anywhere in int32 -- negative, zero,
+    past the capacity, INT32_MIN and INT32_MAX -- act as their clamp to
+    [0, capacity] ([0, max_candidates]), in both decompositions, as the
+    oracle reads them."""
+    import dataclasses
+
+    cap, rows, nc = 256, 8, 40
+    kw = dict(rows=rows, max_blocks_per_row=cap // 16, block_size=16, num_pool_blocks=0)
+    if kind == "latent":
+        p = Problem(heads=16, kv_heads=1, head_size=576, v_head_size=512, cache_dtype="fp8",
+                    k_quant="tensor", v_quant="tensor", layout="latent",
+                    **dict(kw, block_size=64, max_blocks_per_row=cap // 64))
+    elif kind == "kvp":
+        p = Problem(heads=32, kv_heads=8, head_size=128, v_head_size=128, cache_dtype="f16", **kw)
+    elif kind == "multitoken":
+        p = Problem(heads=32, kv_heads=8, head_size=64, v_head_size=64, cache_dtype="i8",
+                    k_quant="tensor", v_quant="tensor", query_tokens=3, **kw)
+    else:
+        p = Problem(heads=12, kv_heads=2, head_size=256, v_head_size=256, cache_dtype="i8",
+                    k_quant="channel", v_quant="channel",
+                    max_candidates=nc if kind == "gathered" else 0, **kw)
+    rng = np.random.default_rng(91)
+    cand = ncand = None
+    if kind == "gathered":
+        cand = rng.integers(-2, cap + 2, size=(rows, nc)).astype(np.int32)
+        ncand = np.full(rows, nc)
+    inp = workloads.make_inputs(p, 91, cap, with_sink=True, candidates=cand,
+                                num_candidates=ncand, softmax_scale=1.0 / np.sqrt(p.head_size))
+    i32 = np.iinfo(np.int32)
+    lens = np.array([-5, i32.max, i32.min, 3, cap, cap + 1, 0, 17], dtype=np.int32)
+    inp = dataclasses.replace(inp, seq_lens=lens)
+    if kind == "gathered":
+        inp = dataclasses.replace(inp, num_candidates=np.array(
+            [-1, i32.max, nc, i32.min, 5, 0, nc + 7, 3], dtype=np.int32))
+    ref_inp = workloads.expand_query_tokens(inp) if p.query_tokens > 1 else inp
+    ref, ref_lse = oracle.paged_decode(ref_inp)
+    announce(f"out-of-range lengths: {kind} balance={balance}")
+    got, lse, g = run_gpu(inp, balance=balance)
+    assert (g.target_ctas > 0) == (balance == 1)
+    assert_close_to_oracle(got, lse, ref, ref_lse, what=f"clamped lengths {kind} balance={balance}")
+
 def test_repeat_is_bitwise_identical():
     inp, _ = named("C3")
     announce("C3 repeat")
