@@ -49,13 +49,15 @@
  * and 8 query rows of one sequence).  A row is then one sequence with T new
  * query tokens that share its block-table row; seq_lens[r] counts all T of
  * them, and token j (0 <= j < T) attends causally:
- *   len_j  = max(0, len - (T - 1 - j)),  T_j = [0, len_j)
+ *   len_j  = max(0, len - (T - 1 - j)),  T_j = [lo_j, len_j),
+ *   lo_j   = max(0, len_j - sliding_window) when sliding_window > 0, else 0
  * query is [num_rows, T, num_heads, head_size], out [num_rows, T, num_heads,
  * v_head_size], lse [num_rows, T, num_heads]; the result for token j is the
- * definition above with len_j.  Every KV tile a CTA reads serves all T tokens
- * of its query heads (the (token, head) pairs of a KV head fill the 16-wide
- * MFMA tile: T * group <= 16 reads each tile once).  Dense rows, the
- * SEPARATE layout, no sliding window, 1 <= T <= 16.
+ * definition above with len_j (each token's window ends at its own
+ * position).  Every KV tile a CTA reads serves all T tokens of its query
+ * heads (the (token, head) pairs of a KV head fill the 16-wide MFMA tile:
+ * T * group <= 16 reads each tile once).  Dense rows, the SEPARATE layout,
+ * 1 <= T <= 16.
  *
  * Memory layouts (all row-major, device memory unless stated):
  *   query        [num_rows, num_heads, head_size]              float16
@@ -191,8 +193,9 @@ typedef struct {
  *         faster than four CTAs reading one head each) and opts do not ask
  *         for 1;
  * cap   = max_blocks_per_row * block_size (dense; with a sliding window W
- *         at most W + 15, the positions from the window start rounded down
- *         to a multiple of 16) or max_candidates (gathered);
+ *         at most W + T - 1 + 15, the positions from the first token's
+ *         window start rounded down to a multiple of 16) or max_candidates
+ *         (gathered);
  *         resident = num_cus * ctas_per_cu.
  * Dense rows (onnx-genai PR #1350 "Summary"; target = waves * resident):
  *   S = min(ceil(target / units), ceil(cap / min_chunk), max_splits)

@@ -81,12 +81,15 @@ int64_t units_row_of(const pkv_problem& p, int kv_per_cta) {
 
 // Most positions one row can have: the candidate-list capacity (gathered
 // rows), else the block-table capacity -- with a sliding window of W
-// tokens at most W + 15, since a row's range starts at the window start
-// rounded down to a multiple of 16 (so tiles never straddle a block).
+// tokens at most W + T - 1 + 15 (T query tokens per row: the first token's
+// window start to the last token), since a row's range starts at the window
+// start rounded down to a multiple of 16 (so tiles never straddle a block).
 int64_t positions_cap(const pkv_problem& p) {
   if (p.max_candidates > 0) return p.max_candidates;
   const int64_t cap = (int64_t)p.max_blocks_per_row * p.block_size;
-  return p.sliding_window > 0 ? std::min<int64_t>(cap, (int64_t)p.sliding_window + 15) : cap;
+  return p.sliding_window > 0
+             ? std::min<int64_t>(cap, (int64_t)p.sliding_window + (qtok_of(p) - 1) + 15)
+             : cap;
 }
 
 // Static checks of the problem description.
@@ -128,9 +131,9 @@ pkv_status check_problem(const pkv_problem* p) {
   if (p->query_tokens > 1) {
     if (p->query_tokens > 16)
       return fail(PKV_EUNSUPPORTED, "query_tokens %d exceeds 16", p->query_tokens);
-    if (p->max_candidates > 0 || p->layout != PKV_SEPARATE || p->sliding_window > 0)
-      return fail(PKV_EUNSUPPORTED, "several query tokens per row need dense rows, the SEPARATE "
-                                    "layout and no sliding window");
+    if (p->max_candidates > 0 || p->layout != PKV_SEPARATE)
+      return fail(PKV_EUNSUPPORTED,
+                  "several query tokens per row need dense rows and the SEPARATE layout");
   }
   if ((int64_t)p->num_rows * qtok_of(*p) * p->num_heads > INT32_MAX)
     return fail(PKV_EUNSUPPORTED, "num_rows * query_tokens * num_heads is too large");

@@ -332,11 +332,15 @@ struct Work {
 // sliding window or soft cap (none of the code below is compiled in), and
 // EXT = true for the rest.
 
-// First token of a row's sliding window (0 without one).
+// First token of a row's sliding window (0 without one).  With T query
+// tokens per row, token j's window ends at len - (T - 1 - j), so the row's
+// range starts at the first token's window start (each later token's own
+// start is masked per head slot).
 template <bool EXT>
 __device__ __forceinline__ int window_lo(const SplitArgs& a, int len) {
   if constexpr (!EXT) return 0;
-  return (a.window > 0 && len > a.window) ? len - a.window : 0;
+  const int first = len - (a.qtok - 1);  // positions the row's first token attends
+  return (a.window > 0 && first > a.window) ? first - a.window : 0;
 }
 
 // Logit soft cap x -> c tanh(x / c) (identity without one).
@@ -813,8 +817,10 @@ __device__ __forceinline__ void exact_partial(const SplitArgs& a, const Work& wk
   for (int hh = 0; hh < wk.nh; ++hh) {
     const HeadSlot hs = head_slot<MT>(a, wk, hh);
     const int h = hs.h;
-    // (several tokens per row: token j sees len - T + 1 + j positions)
+    // (several tokens per row: token j sees len - T + 1 + j positions, and
+    // with a sliding window the last `window` of them)
     const int tlen = MT ? wk.len - (a.qtok - 1 - hs.tok) : wk.len;
+    const int tlo = (MT && a.window > 0 && tlen > a.window) ? tlen - a.window : wk.lo;
     float qf[KD];
 #pragma unroll
     for (int k = 0; k < KD; ++k) {
@@ -832,7 +838,7 @@ __device__ __forceinline__ void exact_partial(const SplitArgs& a, const Work& wk
     for (int pos = p0 + wave; pos < p1; pos += W) {
       int t = wk.base + pos;
       if constexpr (GATHER) t = a.candidates[(size_t)wk.r * a.max_candidates + pos];
-      if (t < wk.lo || t >= tlen) continue;
+      if (t < tlo || t >= tlen) continue;
       const int blk = bt_row[t >> a.log2_block];
       if (blk < 0 || blk >= a.num_pool_blocks) continue;
       const size_t slot = ((size_t)blk << a.log2_block) + (t & (a.block_size - 1));
@@ -1129,8 +1135,15 @@ split_kernel(const SplitArgs a) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       bool valid = (T.vmask >> q) & 1u;
-      if constexpr (MT) valid = valid && p0 + 16 * tt + 4 * lj + q < lim;
-      else (void)tt;
+      if constexpr (MT) {
+        const int pos = p0 + 16 * tt + 4 * lj + q;
+        valid = valid && pos < lim;
+        // the slot's own window start (the row's range starts at the first
+        // token's)
+        if constexpr (EXT) valid = valid && (a.window == 0 || pos >= lim - a.window);
+      } else {
+        (void)tt;
+      }
       sc[q] = valid ? sc[q] : kNegInf;
       smin = fminf(smin, valid ? sc[q] : __builtin_inff());
     }
@@ -1560,8 +1573,13 @@ split_kvp_kernel(const SplitArgs a) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         bool valid = (T.vmask >> q) & 1u;
-        if constexpr (MT) valid = valid && p0 + 16 * tt + 4 * lj + q < lim[vb];
-        else (void)tt;
+        if constexpr (MT) {
+          const int pos = p0 + 16 * tt + 4 * lj + q;
+          valid = valid && pos < lim[vb];
+          if constexpr (EXT) valid = valid && (a.window == 0 || pos >= lim[vb] - a.window);
+        } else {
+          (void)tt;
+        }
         x[q] = valid ? x[q] : kNegInf;
         smin[vb] = fminf(smin[vb], valid ? x[q] : __builtin_inff());
       }

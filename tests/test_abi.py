@@ -407,7 +407,7 @@ def test_query_tokens_geometry_and_limits():
                               num_cus=256, ctas_per_cu=2).kv_heads_per_cta == 1
     for kw, st in ((dict(max_candidates=64), 2), (dict(layout="latent", cache_dtype="fp8",
                                                         k_quant="tensor"), 2),
-                   (dict(sliding_window=32), 2), (dict(query_tokens=17), 2),
+                   (dict(query_tokens=17), 2),
                    (dict(query_tokens=-1), 1)):
         args = {"query_tokens": 3, **kw}
         hs, vhs = (576, 512) if kw.get("layout") == "latent" else (128, 128)

@@ -104,3 +104,45 @@ def test_multitoken_with_softcap(T, kpc):
         announce(f"multi-token softcap T={T} S={S} kv_heads_per_cta={kpc}")
         got, lse, _ = run_gpu(inp, splits_override=S, min_chunk=16, kv_heads_per_cta=kpc)
         assert_close_to_oracle(got, lse, ref, ref_lse, what=f"softcap T={T} S={S}")
+
+
+@pytest.mark.parametrize("T,W", [(3, 1), (3, 17), (8, 5), (8, 40), (4, 100)])
+@pytest.mark.parametrize("kpc,balance", [(1, 2), (4, 1), (4, 2)])
+def test_multitoken_with_sliding_window(T, W, kpc, balance):
+    """A sliding window with several tokens per row: token j attends the last
+    W of its own len - T + 1 + j positions, so the tokens' windows start at
+    different positions; the row's range starts at the first token's window
+    start and each (token, head) slot masks the positions before its own.
+    Windows shorter than T, inside one tile and across several tiles, with
+    one or four KV heads per CTA, both decompositions and split counts."""
+    from dataclasses import replace
+    inp = _mt("f16" if W % 2 else "i8", 128, 32, 8, T, seed=71 + W)
+    inp = workloads.Inputs(**{**inp.__dict__, "problem": replace(inp.problem, sliding_window=W)})
+    ref, ref_lse = oracle.paged_decode(workloads.expand_query_tokens(inp))
+    full, _ = oracle.paged_decode(workloads.expand_query_tokens(
+        workloads.Inputs(**{**inp.__dict__, "problem": replace(inp.problem, sliding_window=0)})))
+    assert np.abs(ref - full).max() > 1e-2  # the window changes the result
+    for geo in (dict(balance=balance), dict(splits_override=3, min_chunk=16, balance=balance)):
+        announce(f"multi-token window T={T} W={W} kv_heads_per_cta={kpc} {geo}")
+        got, lse, g = run_gpu(inp, kv_heads_per_cta=kpc, **geo)
+        assert (g.target_ctas > 0) == (balance == 1)
+        assert_close_to_oracle(got, lse, ref, ref_lse, what=f"window T={T} W={W} kpc={kpc} {geo}")
+
+
+@pytest.mark.parametrize("T,W", [(3, 20), (8, 40)])
+def test_multitoken_with_sliding_window_fp32_path(T, W):
+    """The FP32 path (large queries) with several tokens per row and a
+    window: each (token, head) pair keeps its own window."""
+    from dataclasses import replace
+    inp = _mt("i8", 128, 32, 8, T, seed=13)
+    inp = workloads.Inputs(**{**inp.__dict__, "problem": replace(inp.problem, sliding_window=W)})
+    inp.query[...] = (inp.query.astype(np.float32) * 200.0).astype(np.float16)
+    ref, ref_lse = oracle.paged_decode(workloads.expand_query_tokens(inp))
+    for kpc in (1, 4):
+        announce(f"multi-token window FP32 path T={T} W={W} kv_heads_per_cta={kpc}")
+        got, lse, _ = run_gpu(inp, splits_override=2, min_chunk=16, out_dtype="f32",
+                              kv_heads_per_cta=kpc)
+        scale = np.abs(ref).max()
+        assert np.abs(got - ref).max() <= 1e-4 * scale
+        fin = np.isfinite(ref_lse)
+        np.testing.assert_allclose(lse[fin], ref_lse[fin], rtol=1e-5, atol=1e-4)
