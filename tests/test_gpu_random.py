@@ -45,7 +45,7 @@ def _draw(rng):
     mbpr = int(rng.integers(1, 9))
     cap = mbpr * B
     rows = int(rng.integers(1, 21))
-    window = int(rng.choice([0, 0, 0, 1, 17, 40, 100])) if T == 1 else 0
+    window = int(rng.choice([0, 0, 0, 1, 17, 40, 100]))
     softcap = float(rng.choice([0.0, 0.0, 0.0, 2.0, 30.0]))
     nc = int(rng.integers(1, 100)) if gathered else 0
     p = Problem(rows=rows, heads=heads, kv_heads=kvh, head_size=D, v_head_size=VD, block_size=B,
