@@ -49,6 +49,13 @@ def run_gpu(inp, out_dtype=None, geometry=None, partials_then_combine=False, **g
 
 def assert_close_to_oracle(got, lse, ref, ref_lse, max_abs=MAX_ABS, mean_abs=MEAN_ABS, what=""):
     assert np.all(np.isfinite(got)), f"{what}: non-finite output"
+    if np.array_equal(got, got.astype(np.float16).astype(np.float64)):
+        # An FP16 output cannot come closer to the exact result than rounding
+        # it to FP16: where every output is one unit-variance value (a window
+        # of one position, one-token rows) that rounding alone averages about
+        # 2e-4, so the mean bound is at least 1.1 times its mean.
+        floor = float(np.abs(ref.astype(np.float16).astype(np.float64) - ref).mean())
+        mean_abs = max(mean_abs, 1.1 * floor)
     err = np.abs(got - ref)
     assert err.max() <= max_abs, f"{what}: max abs error {err.max():.3e} > {max_abs:.1e}"
     assert err.mean() <= mean_abs, f"{what}: mean abs error {err.mean():.3e} > {mean_abs:.1e}"
